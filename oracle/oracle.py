@@ -1,0 +1,139 @@
+"""Python face of the CPU oracle (fp64).  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check and the CPU-baseline leg of ``bench.py`` may
+import this module.  It shares no code with the GPU library: it takes numpy
+arrays (bf16 bit patterns as ``uint16`` or ``float32``) and returns float64.
+
+Pages cited (title; section):
+  [SPYRE]  "Enable compact sliding-window attention for Gemma 3 and Gemma 4
+           variants" (torch-spyre/hf-adapters pull request 496)
+  [BONSAI] "Gemma3 Local Attention Cache" (jax-ml/bonsai issue 124)
+  [SDPA]   "Add SDPA attention implementation" (Fast-LLM pull request 512)
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+CAUSAL = 0
+BLOCKWISE = 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _build.build(force=False)
+        lib = ctypes.CDLL(path)
+        P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        lib.oracle_prefill_rows.argtypes = [P, P, P, I, P, I, P, I, I, I, I, I, I, D, P, I, P, I]
+        lib.oracle_prefill_rows.restype = I
+        lib.oracle_decode_linear.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, D, P, I]
+        lib.oracle_decode_linear.restype = I
+        lib.oracle_count_allowed.argtypes = [P, I, P, I, I, I, I]
+        lib.oracle_count_allowed.restype = ctypes.c_longlong
+        lib.oracle_allowed.argtypes = [P, I, P, I, I, I, I]
+        lib.oracle_allowed.restype = I
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = I
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(a):
+    if a.dtype == np.uint16:
+        return 0
+    if a.dtype == np.float32:
+        return 1
+    raise TypeError("oracle inputs are bf16 bit patterns (uint16) or float32, got %s" % a.dtype)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def max_threads() -> int:
+    return _load().oracle_max_threads()
+
+
+def prefill(q, k, v, cu_seqlens, ids=None, window=0, mode=CAUSAL, scale=None,
+            rows=None, nthreads=0):
+    """Packed varlen SWA prefill in fp64.
+
+    q [T, Hq, D], k/v [T, Hkv, D] (uint16 bf16 bits or float32); cu_seqlens
+    int32 [ndocs+1].  ``rows`` selects packed query indices (default: all).
+    Returns float64 [len(rows), Hq, D].  ``scale`` defaults to 1/sqrt(D).
+    """
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dt = _dtype_code(q)
+    assert _dtype_code(k) == dt and _dtype_code(v) == dt
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    assert k.shape == (T, hkv, d) and v.shape == (T, hkv, d)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    ids_a = None if ids is None else np.ascontiguousarray(ids, dtype=np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    n = T if rows_a is None else rows_a.size
+    out = np.empty((n, hq, d), dtype=np.float64)
+    rc = _load().oracle_prefill_rows(
+        _ptr(q), _ptr(k), _ptr(v), dt, _ptr(cu), cu.size - 1, _ptr(ids_a),
+        int(window), int(mode), T, hq, hkv, d, float(scale), _ptr(rows_a), n,
+        _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_prefill_rows rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+def decode_linear(q, k_hist, v_hist, hist_off, first_pos, hist_len, pos, lo,
+                  window, scale=None, nthreads=0):
+    """One-token decode per sequence on linear histories, fp64.
+
+    q [B, Hq, D]; k_hist/v_hist [rows, Hkv, D]; sequence b owns rows
+    hist_off[b] .. hist_off[b]+hist_len[b]-1 holding positions first_pos[b]..
+    Returns float64 [B, Hq, D].
+    """
+    q = np.ascontiguousarray(q)
+    k_hist = np.ascontiguousarray(k_hist)
+    v_hist = np.ascontiguousarray(v_hist)
+    dt = _dtype_code(q)
+    B, hq, d = q.shape
+    hkv = k_hist.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    off = np.ascontiguousarray(hist_off, dtype=np.int64)
+    fp = np.ascontiguousarray(first_pos, dtype=np.int32)
+    hl = np.ascontiguousarray(hist_len, dtype=np.int32)
+    ps = np.ascontiguousarray(pos, dtype=np.int32)
+    lo_a = np.ascontiguousarray(lo, dtype=np.int32)
+    out = np.empty((B, hq, d), dtype=np.float64)
+    rc = _load().oracle_decode_linear(
+        _ptr(q), _ptr(k_hist), _ptr(v_hist), dt, _ptr(off), _ptr(fp), _ptr(hl),
+        _ptr(ps), _ptr(lo_a), int(window), B, hq, hkv, d, float(scale), _ptr(out),
+        int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_decode_linear rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+def count_allowed(cu_seqlens, ids=None, window=0, mode=CAUSAL, nthreads=0):
+    """Number of admitted (query, key) pairs, counted pair by pair."""
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    ids_a = None if ids is None else np.ascontiguousarray(ids, dtype=np.int32)
+    return int(_load().oracle_count_allowed(_ptr(cu), cu.size - 1, _ptr(ids_a),
+                                            int(window), int(mode), int(cu[-1]),
+                                            int(nthreads)))
+
+
+def allowed(cu_seqlens, ids, window, mode, i, j):
+    """The oracle's mask for one (query i, key j) pair, as a bool."""
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    ids_a = None if ids is None else np.ascontiguousarray(ids, dtype=np.int32)
+    return bool(_load().oracle_allowed(_ptr(cu), cu.size - 1, _ptr(ids_a), int(window),
+                                       int(mode), int(i), int(j)))
