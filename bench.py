@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of the sliding-window GQA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline (`value`): useful (unmasked) TFLOP/s of swa_prefill on 4 packed
+documents x 1024 tokens, Hq = Hkv = 32, D = 128, W = 1024, causal, bf16.  A
+step is one swa_prefill over one batch; inputs rotate over several resident
+copies so the 256 MB Infinity Cache cannot hold them.  The other prefill
+workloads and the two ring-decode workloads (append + decode per step, the
+roll every 64 steps) are measured in the same run and reported under
+"workloads".  Times come from HIP events on the stream the kernels run on.
+
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the headline
+workload on this host's cores.  `roofline.traffic` is read from the counter
+summary under profiles/ only while the kernel sources still hash to the
+value recorded there.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import swa_inputs as si  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0       # HBM3E
+HEADLINE = "prefill_4x1024_mha_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "prefill_fwd_kernel": ["prefill_kernel.h", "prefill_launch.h", "prefill_d128.hip"],
+    "decode_split_kernel": ["decode.hip"],
+}
+
+
+# ------------------------------------------------------------ work counts
+def causal_window_pairs(n: int, W: int) -> int:
+    """Pairs (i, j), j <= i, i - j < W in one document of n tokens."""
+    if W <= 0 or W >= n:
+        return n * (n + 1) // 2
+    return W * (W + 1) // 2 + (n - W) * W
+
+
+def useful_pairs(c: si.PrefillCase) -> int:
+    """Allowed (query, key) pairs per query head.  The blockwise extra is
+    every later key of the same image run (the window is one-sided)."""
+    cu = c.cu_seqlens
+    total = sum(causal_window_pairs(int(b - a), c.window) for a, b in zip(cu[:-1], cu[1:]))
+    if c.mode == si.BLOCKWISE:
+        ids = c.ids
+        for a, b in zip(cu[:-1], cu[1:]):
+            t = int(a)
+            while t < int(b):
+                e = t
+                while e + 1 < int(b) and ids[e + 1] == ids[t]:
+                    e += 1
+                if ids[t] >= 0:
+                    n = e - t + 1
+                    total += n * (n - 1) // 2
+                t = e + 1
+    return total
+
+
+def useful_flops(c: si.PrefillCase) -> int:
+    return 4 * c.d * c.hq * useful_pairs(c)  # 2D for QK^T + 2D for PV per pair
+
+
+def decode_valid_rows(pos, lo, W):
+    low = np.maximum(np.maximum(lo, pos - W + 1), 0)
+    return pos - low + 1
+
+
+def sources_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "sliding_window_gqa_swa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None if absent or taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("sources_sha256") != sources_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------ GPU timing
+def to_dev(a, torch):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def time_loop(fn, steps, warmup, torch):
+    """ms per call of fn(i) over `steps` calls, HIP events on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_prefill(name, steps, warmup, torch, api, nsets=None):
+    c = si.PREFILL_WORKLOADS[name]()
+    q, k, v = c.tensors("bf16")
+    in_bytes = (q.nbytes + k.nbytes + v.nbytes) * 2  # + out
+    if nsets is None:
+        nsets = max(1, min(6, int(np.ceil(1.1e9 / in_bytes))))
+    sets = []
+    for s in range(nsets):
+        if s == 0:
+            qq, kk, vv = q, k, v
+        else:
+            qq, kk, vv = c.tensors("bf16", seed=c.seed * 1000 + s)
+        sets.append((to_dev(qq, torch), to_dev(kk, torch), to_dev(vv, torch)))
+    cu = to_dev(c.cu_seqlens, torch)
+    ids = to_dev(c.ids, torch) if c.ids is not None else None
+    outs = [torch.empty_like(s[0]) for s in sets]
+
+    def step(i):
+        s = i % nsets
+        api.prefill(sets[s][0], sets[s][1], sets[s][2], cu, ids, c.window, c.mode, out=outs[s])
+
+    ms = time_loop(step, steps, warmup, torch)
+    fl = useful_flops(c)
+    return {
+        "workload": name, "T": c.T, "docs": int(c.cu_seqlens.size - 1), "hq": c.hq,
+        "hkv": c.hkv, "d": c.d, "window": c.window,
+        "mask": "blockwise" if c.mode == si.BLOCKWISE else "causal",
+        "useful_flop": fl, "ms_per_call": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+        "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "input_sets": nsets,
+    }
+
+
+def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
+    """Append + decode per step over `layers` independent ring sets (one per
+    simulated sliding layer), the roll before every step (it only moves the
+    rings that are full: every 64 steps)."""
+    c = si.DECODE_WORKLOADS[name]()
+    ks, vs = c.prompt_tail("bf16")
+    B, hq, hkv, d, R, W = c.batch, c.hq, c.hkv, c.d, c.ring_rows, c.window
+    rings = []
+    for _ in range(layers):
+        kr = torch.zeros((B, hkv, R, d), dtype=torch.bfloat16, device="cuda")
+        vr = torch.zeros_like(kr)
+        meta = torch.zeros((B, 4), dtype=torch.int32, device="cuda")
+        api.cache_compact(to_dev(ks, torch), to_dev(vs, torch), to_dev(c.cu_tail, torch), kr, vr,
+                          meta, W, to_dev(c.prompt_lens, torch), to_dev(c.left_pad, torch))
+        rings.append((kr, vr, meta))
+    steps_in = []
+    for s in range(-c.pre_appends, c.steps):
+        q, kn, vn = c.step_inputs(s, "bf16")
+        steps_in.append((to_dev(q, torch), to_dev(kn, torch), to_dev(vn, torch)))
+    ws = api.decode_workspace(steps_in[0][0], rings[0][0])
+    outs = [torch.empty_like(steps_in[0][0]) for _ in range(layers)]
+    # pre-appends (not timed): bring the single-sequence case to position 3000
+    for s in range(c.pre_appends):
+        q, kn, vn = steps_in[s]
+        for kr, vr, meta in rings:
+            api.cache_roll(kr, vr, meta, W)
+            api.cache_append(kn, vn, kr, vr, meta)
+    torch.cuda.synchronize()
+    timed = steps_in[c.pre_appends:]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for q, kn, vn in timed:
+        for li, (kr, vr, meta) in enumerate(rings):
+            api.cache_roll(kr, vr, meta, W)
+            api.cache_append(kn, vn, kr, vr, meta)
+            api.decode(q, kr, vr, meta, W, out=outs[li], workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / (len(timed) * layers)
+    # decode alone on the final state, rotating over the ring sets (cold)
+    q = timed[-1][0]
+
+    def dstep(i):
+        kr, vr, meta = rings[i % layers]
+        api.decode(q, kr, vr, meta, W, out=outs[i % layers], workspace=ws)
+
+    dec_ms = time_loop(dstep, reps * layers, warmup * layers, torch)
+    # warm: the same ring set every call
+    warm_ms = time_loop(lambda i: api.decode(q, rings[0][0], rings[0][1], rings[0][2], W,
+                                             out=outs[0], workspace=ws), reps, warmup, torch)
+    pos = c.prompt_lens.astype(np.int64) - 1 + c.pre_appends + c.steps
+    valid = decode_valid_rows(pos, c.left_pad.astype(np.int64), W)
+    es = 2
+    alg_bytes = int(valid.sum()) * hkv * d * es * 2 + 2 * B * hq * d * es + B * 16
+    scanned = B * hkv * R * d * es * 2
+    return {
+        "workload": name, "batch": B, "hq": hq, "hkv": hkv, "d": d, "window": W,
+        "ring_rows": R, "steps": len(timed), "layers_rotated": layers,
+        "us_per_step_append_decode_roll": step_us,
+        "decode_us": dec_ms * 1e3, "decode_warm_us": warm_ms * 1e3,
+        "algorithmic_bytes": alg_bytes, "full_ring_bytes": scanned,
+        "decode_gbs": alg_bytes / (dec_ms * 1e-3) / 1e9,
+        "frac_of_hbm_peak": alg_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+
+
+# ------------------------------------------------------------ CPU baseline
+def cpu_baseline(budget_s=15.0):
+    """fp64 oracle on a bounded, seeded sample of the headline workload."""
+    from oracle import oracle as orc
+    c = si.PREFILL_WORKLOADS[HEADLINE]()
+    q, k, v = c.tensors("bf16")
+    rng = si.rng_for(99)
+    order = rng.permutation(c.T).astype(np.int32)
+    threads = orc.max_threads()
+    cu = c.cu_seqlens
+    doc = np.searchsorted(cu, np.arange(c.T), side="right") - 1
+    start = cu[doc]
+    keys = np.minimum(np.arange(c.T) - start + 1, c.window)
+    done, flops, t0 = 0, 0, time.perf_counter()
+    chunk = 256
+    while done < c.T and time.perf_counter() - t0 < budget_s:
+        rows = order[done:done + chunk]
+        orc.prefill(q, k, v, cu, None, c.window, c.mode, rows=rows, nthreads=threads)
+        flops += int(keys[rows].sum()) * 4 * c.d * c.hq
+        done += rows.size
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": "%d of %d query rows (all %d heads) of %s, seeded random order, fp64, %.1f s"
+                  % (done, c.T, c.hq, HEADLINE, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this implementation has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from sliding_window_gqa_swa_amd import api
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+
+    head = bench_prefill(HEADLINE, args.steps, args.warmup, torch, api)
+    print("headline %s: %.3f ms, %.1f TFLOP/s" % (HEADLINE, head["ms_per_call"], head["tflops"]),
+          file=sys.stderr, flush=True)
+    workloads = {HEADLINE: head}
+    if not args.only_headline:
+        for name in ("prefill_16k_gqa_d512", "prefill_vlm_4096_d256"):
+            workloads[name] = bench_prefill(name, max(5, args.steps // 5), 3, torch, api)
+            print("%s: %.3f ms, %.1f TFLOP/s" % (name, workloads[name]["ms_per_call"],
+                                                 workloads[name]["tflops"]), file=sys.stderr,
+                  flush=True)
+        for name in ("decode_b64_d256", "decode_single_d256"):
+            workloads[name] = bench_decode(name, torch, api)
+            print("%s: %.2f us/step, decode %.2f us, %.0f GB/s" % (
+                name, workloads[name]["us_per_step_append_decode_roll"],
+                workloads[name]["decode_us"], workloads[name]["decode_gbs"]), file=sys.stderr,
+                flush=True)
+
+    traffic = read_traffic("prefill_fwd_kernel", HEADLINE)
+    roof = {
+        "bound": "mfma", "kernel": "prefill_fwd_kernel<128, bf16>",
+        "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": head["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()
+        print("cpu baseline: %.4f TFLOP/s on %d threads" % (cpu["value"], cpu["cores"]),
+              file=sys.stderr, flush=True)
+    line = {
+        "metric": "SWA prefill useful TFLOP/s (4x1024-token packed causal prefill, MHA 32 heads, D=128, W=1024)",
+        "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_call"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) rounded to bf16",
+        "config": {"workload": HEADLINE, "docs": 4, "tokens_per_doc": 1024, "total_tokens": 4096,
+                   "hq": 32, "hkv": 32, "head_dim": 128, "window": 1024, "mask": "causal",
+                   "useful_flop_per_step": head["useful_flop"], "input_sets": head["input_sets"]},
+        "roofline": roof, "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "workloads": workloads,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,127 @@
+"""Python face of libswa: the C entry points under the same names, taking
+``torch.Tensor`` arguments.
+
+Argument marshalling only -- every step of attention and of the ring cache
+runs in the HIP kernels behind the C ABI.  torch supplies device memory and
+the current stream; nothing here computes on the host.  Tensors must be
+contiguous, on a ROCm device, and of the element type the call names
+(bfloat16 or float32; int32 for lengths, ids and ring_meta).
+"""
+import torch
+
+from . import _lib
+from ._lib import SWA_BF16, SWA_BLOCKWISE, SWA_CAUSAL, SWA_F32, SWA_META_ERR  # noqa: F401
+
+CAUSAL = SWA_CAUSAL
+BLOCKWISE = SWA_BLOCKWISE
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SWA_BF16
+    if t.dtype == torch.float32:
+        return SWA_F32
+    raise TypeError("expected bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    """Device pointer of a contiguous GPU tensor (0 for None)."""
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (libswa has no CPU path)" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def prefill(q, k, v, cu_seqlens, doc_or_block_ids=None, window=0, causal_mode=CAUSAL,
+            out=None, scale=0.0):
+    """Packed varlen sliding-window GQA prefill; see swa_prefill in swa.h.
+
+    q [T, Hq, D], k/v [T, Hkv, D] (bf16 or fp32), cu_seqlens int32 [ndocs+1],
+    doc_or_block_ids int32 [T] (BLOCKWISE only).  Returns out [T, Hq, D]."""
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (T, hkv, d) or v.shape != (T, hkv, d):
+        raise ValueError("k and v must be [T, Hkv, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s dtype differs from q" % name)
+    rc = _lib.lib().swa_prefill(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+        _dev(doc_or_block_ids, "doc_or_block_ids", torch.int32), int(window), int(causal_mode),
+        _dev(out, "out"), T, cu_seqlens.numel() - 1, hq, hkv, d, dt, float(scale), _stream(q))
+    _lib.check("swa_prefill", rc)
+    return out
+
+
+def decode_workspace_bytes(batch, hq, hkv, d, ring_rows) -> int:
+    return int(_lib.lib().swa_decode_workspace_bytes(batch, hq, hkv, d, ring_rows))
+
+
+def decode_workspace(q, k_ring) -> torch.Tensor:
+    """A workspace tensor of the size swa_decode needs for these shapes."""
+    B, hq, d = q.shape
+    nbytes = decode_workspace_bytes(B, hq, k_ring.shape[1], d, k_ring.shape[2])
+    return torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+
+
+def decode(q, k_ring, v_ring, ring_meta, window, out=None, workspace=None, scale=0.0):
+    """One-token decode against compact rings; see swa_decode in swa.h.
+
+    q [B, Hq, D]; k_ring/v_ring [B, Hkv, R, D]; ring_meta int32 [B, 4]."""
+    B, hq, d = q.shape
+    _, hkv, R, _ = k_ring.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = decode_workspace(q, k_ring)
+    rc = _lib.lib().swa_decode(
+        _dev(q, "q"), _dev(k_ring, "k_ring"), _dev(v_ring, "v_ring"),
+        _dev(ring_meta, "ring_meta", torch.int32), int(window), _dev(out, "out"), B, R, hq, hkv, d,
+        _dtype_code(q), float(scale), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(q))
+    _lib.check("swa_decode", rc)
+    return out
+
+
+def cache_append(k_new, v_new, k_ring, v_ring, ring_meta):
+    """Write one token per sequence at position pos + 1; see swa_cache_append."""
+    B, hkv, R, d = k_ring.shape
+    rc = _lib.lib().swa_cache_append(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_ring, "k_ring"), _dev(v_ring, "v_ring"),
+        _dev(ring_meta, "ring_meta", torch.int32), B, R, hkv, d, _dtype_code(k_ring),
+        _stream(k_ring))
+    _lib.check("swa_cache_append", rc)
+
+
+def cache_compact(k_src, v_src, cu_seqlens, k_ring, v_ring, ring_meta, window,
+                  prompt_lens=None, left_pad=None):
+    """Build rings from packed prompt rows; see swa_cache_compact."""
+    B, hkv, R, d = k_ring.shape
+    rc = _lib.lib().swa_cache_compact(
+        _dev(k_src, "k_src"), _dev(v_src, "v_src"), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+        _dev(prompt_lens, "prompt_lens", torch.int32), _dev(left_pad, "left_pad", torch.int32),
+        k_src.shape[0], _dev(k_ring, "k_ring"), _dev(v_ring, "v_ring"),
+        _dev(ring_meta, "ring_meta", torch.int32), int(window), B, R, hkv, d,
+        _dtype_code(k_ring), _stream(k_ring))
+    _lib.check("swa_cache_compact", rc)
+
+
+def cache_roll(k_ring, v_ring, ring_meta, window):
+    """Roll every full ring by ring_rows - window rows; see swa_cache_roll."""
+    B, hkv, R, d = k_ring.shape
+    rc = _lib.lib().swa_cache_roll(
+        _dev(k_ring, "k_ring"), _dev(v_ring, "v_ring"), _dev(ring_meta, "ring_meta", torch.int32),
+        int(window), B, R, hkv, d, _dtype_code(k_ring), _stream(k_ring))
+    _lib.check("swa_cache_roll", rc)

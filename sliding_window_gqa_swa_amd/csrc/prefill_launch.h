@@ -1,0 +1,39 @@
+// prefill_launch.h -- host launcher template for prefill_fwd_kernel.
+#pragma once
+
+#include "prefill_kernel.h"
+#include "swa_internal.h"
+
+namespace swa {
+
+template <int D, typename T, int MB, int BN, int NW, int GH>
+int launch_prefill_cfg(const void* q, const void* k, const void* v,
+                       const int32_t* cu, const int32_t* ids, int window,
+                       int mode, void* out, int total_tokens, int num_docs,
+                       int hq, int hkv, float scale, hipStream_t stream) {
+  using G = PfGeom<D, T, MB, BN, NW, GH>;
+  const int ntiles = (total_tokens + G::BM - 1) / G::BM;
+  const int g = hq / hkv;
+  dim3 grid(ntiles, hkv * (g / GH));
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, T, MB, BN, NW, GH>), grid, dim3(G::NT), 0,
+                     stream, (const T*)q, (const T*)k, (const T*)v, cu, num_docs, ids,
+                     window, mode, (T*)out, total_tokens, hq, hkv,
+                     scale * kPrefillLog2e, ntiles);
+  return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
+}
+
+// One translation unit per head dimension keeps compile times parallel.
+int launch_prefill_d64(const void* q, const void* k, const void* v, const int32_t* cu,
+                       const int32_t* ids, int window, int mode, void* out, int total_tokens,
+                       int num_docs, int hq, int hkv, int dtype, float scale, hipStream_t s);
+int launch_prefill_d128(const void* q, const void* k, const void* v, const int32_t* cu,
+                        const int32_t* ids, int window, int mode, void* out, int total_tokens,
+                        int num_docs, int hq, int hkv, int dtype, float scale, hipStream_t s);
+int launch_prefill_d256(const void* q, const void* k, const void* v, const int32_t* cu,
+                        const int32_t* ids, int window, int mode, void* out, int total_tokens,
+                        int num_docs, int hq, int hkv, int dtype, float scale, hipStream_t s);
+int launch_prefill_d512(const void* q, const void* k, const void* v, const int32_t* cu,
+                        const int32_t* ids, int window, int mode, void* out, int total_tokens,
+                        int num_docs, int hq, int hkv, int dtype, float scale, hipStream_t s);
+
+}  // namespace swa

@@ -1,0 +1,46 @@
+// swa_internal.h -- launchers behind the C ABI (host side, C++).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+// Ring cache (byte copies; row_bytes = d * element size, a multiple of 16).
+int launch_ring_append(const void* k_new, const void* v_new, void* k_ring,
+                       void* v_ring, int32_t* meta, int batch, int ring_rows,
+                       int hkv, int row_bytes, hipStream_t stream);
+int launch_ring_compact(const void* k_src, const void* v_src,
+                        const int32_t* cu, const int32_t* prompt_lens,
+                        const int32_t* left_pad, int src_rows, void* k_ring,
+                        void* v_ring, int32_t* meta, int window, int batch,
+                        int ring_rows, int hkv, int row_bytes,
+                        hipStream_t stream);
+int launch_ring_roll(void* k_ring, void* v_ring, int32_t* meta, int window,
+                     int batch, int ring_rows, int hkv, int row_bytes,
+                     hipStream_t stream);
+
+// Decode: split-K partials then a fixed-order combine.
+struct DecodePlan {
+  int heads_per_block;  // query heads of one kv group handled per block
+  int head_blocks;      // ceil(g / heads_per_block)
+  int splits;           // ring row ranges per (sequence, kv head)
+  int rows_per_split;   // multiple of 32
+  size_t workspace_bytes;
+};
+DecodePlan plan_decode(int batch, int hq, int hkv, int d, int ring_rows);
+int launch_decode(const void* q, const void* k_ring, const void* v_ring,
+                  const int32_t* meta, int window, void* out, int batch,
+                  int ring_rows, int hq, int hkv, int d, int dtype,
+                  float scale, void* workspace, const DecodePlan& plan,
+                  hipStream_t stream);
+
+// Prefill.
+int launch_prefill(const void* q, const void* k, const void* v,
+                   const int32_t* cu, const int32_t* ids, int window,
+                   int mode, void* out, int total_tokens, int num_docs,
+                   int hq, int hkv, int d, int dtype, float scale,
+                   hipStream_t stream);
+
+}  // namespace swa

@@ -1,0 +1,130 @@
+"""The C ABI on the host (no GPU needed): libswa.so loads, exports every
+function include/swa.h declares, and rejects bad arguments before any HIP
+call (every check below returns without touching a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sliding_window_gqa_swa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            names += re.findall(r"SWA_API\s+[\w\s\*]+?\b(swa_\w+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 7
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_strerror_codes():
+    L = _lib.lib()
+    for code in (0, -1, -2, -3, -4, -99):
+        assert len(L.swa_strerror(code)) > 0
+
+
+# fake 16-byte-aligned "device" addresses: the calls below must fail in
+# host-side validation, before any pointer is dereferenced or any kernel runs
+A = 0x10000
+B = 0x20000
+
+
+def _prefill(**kw):
+    args = dict(q=A, k=A, v=A, cu=B, ids=None, window=16, mode=0, out=A, T=10, nd=1, hq=4,
+                hkv=2, d=128, dtype=0, scale=0.0)
+    args.update(kw)
+    return _lib.lib().swa_prefill(args["q"], args["k"], args["v"], args["cu"], args["ids"],
+                                  args["window"], args["mode"], args["out"], args["T"], args["nd"],
+                                  args["hq"], args["hkv"], args["d"], args["dtype"], args["scale"],
+                                  None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=100), _lib.SWA_EUNSUPPORTED),
+    (dict(d=320), _lib.SWA_EUNSUPPORTED),
+    (dict(dtype=7), _lib.SWA_EUNSUPPORTED),
+    (dict(mode=2), _lib.SWA_EUNSUPPORTED),
+    (dict(hq=3, hkv=2), _lib.SWA_EINVAL),
+    (dict(hkv=0), _lib.SWA_EINVAL),
+    (dict(T=-1), _lib.SWA_EINVAL),
+    (dict(nd=0), _lib.SWA_EINVAL),
+    (dict(q=None), _lib.SWA_EINVAL),
+    (dict(out=A + 8), _lib.SWA_EINVAL),
+    (dict(cu=None), _lib.SWA_EINVAL),
+    (dict(mode=1, ids=None), _lib.SWA_EINVAL),
+])
+def test_prefill_rejects(kw, code):
+    assert _prefill(**kw) == code
+
+
+def test_prefill_empty_is_a_no_op():
+    assert _prefill(T=0, q=None, k=None, v=None, out=None, cu=None) == _lib.SWA_OK
+
+
+def _decode(**kw):
+    a = dict(q=A, k=A, v=A, meta=B, window=1024, out=A, b=2, R=1088, hq=8, hkv=4, d=256,
+             dtype=0, ws=A, wsb=1 << 30)
+    a.update(kw)
+    return _lib.lib().swa_decode(a["q"], a["k"], a["v"], a["meta"], a["window"], a["out"], a["b"],
+                                 a["R"], a["hq"], a["hkv"], a["d"], a["dtype"], 0.0, a["ws"],
+                                 a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=0), _lib.SWA_EINVAL),
+    (dict(R=1024), _lib.SWA_EINVAL),
+    (dict(R=70000, window=1024), _lib.SWA_EUNSUPPORTED),
+    (dict(d=96), _lib.SWA_EUNSUPPORTED),
+    (dict(meta=None), _lib.SWA_EINVAL),
+    (dict(ws=None), _lib.SWA_EWORKSPACE),
+    (dict(wsb=16), _lib.SWA_EWORKSPACE),
+    (dict(hq=6, hkv=4), _lib.SWA_EINVAL),
+])
+def test_decode_rejects(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_workspace_depends_only_on_sizes():
+    L = _lib.lib()
+    a = L.swa_decode_workspace_bytes(64, 8, 4, 256, 1088)
+    assert a > 0 and a == L.swa_decode_workspace_bytes(64, 8, 4, 256, 1088)
+    assert L.swa_decode_workspace_bytes(0, 8, 4, 256, 1088) == 0
+    assert L.swa_decode_workspace_bytes(1, 8, 4, 100, 1088) == 0
+
+
+def test_ring_ops_reject():
+    L = _lib.lib()
+    # append: bad d / null meta
+    assert L.swa_cache_append(A, A, A, A, B, 2, 1088, 4, 100, 0, None) == _lib.SWA_EUNSUPPORTED
+    assert L.swa_cache_append(A, A, A, A, None, 2, 1088, 4, 256, 0, None) == _lib.SWA_EINVAL
+    assert L.swa_cache_append(A, A, A, A, B, 0, 1088, 4, 256, 0, None) == _lib.SWA_OK
+    # compact: ring no larger than the window
+    assert L.swa_cache_compact(A, A, B, None, None, 10, A, A, B, 1088, 2, 1088, 4, 256, 0,
+                               None) == _lib.SWA_EINVAL
+    assert L.swa_cache_compact(A, A, None, None, None, 10, A, A, B, 1024, 2, 1088, 4, 256, 0,
+                               None) == _lib.SWA_EINVAL
+    # roll: window < 1
+    assert L.swa_cache_roll(A, A, B, 0, 2, 1088, 4, 256, 0, None) == _lib.SWA_EINVAL
+    assert L.swa_cache_roll(A, A, B, 1024, 2, 1088, 4, 256, 5, None) == _lib.SWA_EUNSUPPORTED
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from sliding_window_gqa_swa_amd import api
+    q = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        api.prefill(q, q[:, :1].contiguous(), q[:, :1].contiguous(), cu)

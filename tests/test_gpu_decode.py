@@ -1,0 +1,177 @@
+"""GPU ring decode against the fp64 oracle's decode on a LINEAR cache, at
+every step of runs that span rolls, plus the two decode workloads at full
+size in the launch configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import swa_inputs as si
+from oracle import oracle as orc
+from sliding_window_gqa_swa_amd import api
+
+from gpu_util import assert_close, dev, host, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+class DecodeRun:
+    """Compacts rings on the GPU from a prompt tail and keeps the linear
+    history (prompt tail + every appended token) on the host for the oracle."""
+
+    def __init__(self, case: si.DecodeCase, dtype: str):
+        self.c, self.dtype = case, dtype
+        ks, vs = case.prompt_tail(dtype)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        B, hkv, R, d = case.batch, case.hkv, case.ring_rows, case.d
+        self.k = torch.zeros((B, hkv, R, d), dtype=tdt, device="cuda")
+        self.v = torch.zeros_like(self.k)
+        self.meta = torch.zeros((B, 4), dtype=torch.int32, device="cuda")
+        api.cache_compact(dev(ks), dev(vs), dev(case.cu_tail), self.k, self.v, self.meta,
+                          case.window, dev(case.prompt_lens), dev(case.left_pad))
+        cu = case.cu_tail
+        self.hist_k = [ks[cu[b]:cu[b + 1]] for b in range(B)]
+        self.hist_v = [vs[cu[b]:cu[b + 1]] for b in range(B)]
+        self.first = (case.prompt_lens - case.tail_lens).astype(np.int32)
+        self.pos = case.prompt_lens.astype(np.int64) - 1
+        self.ws = None
+
+    def step(self, s, check_seqs=None):
+        c = self.c
+        q, kn, vn = c.step_inputs(s, self.dtype)
+        api.cache_roll(self.k, self.v, self.meta, c.window)
+        api.cache_append(dev(kn), dev(vn), self.k, self.v, self.meta)
+        qd = dev(q)
+        if self.ws is None:
+            self.ws = api.decode_workspace(qd, self.k)
+        out = host(api.decode(qd, self.k, self.v, self.meta, c.window, workspace=self.ws))
+        self.pos += 1
+        for b in range(c.batch):
+            self.hist_k[b] = np.concatenate([self.hist_k[b], kn[b:b + 1]])
+            self.hist_v[b] = np.concatenate([self.hist_v[b], vn[b:b + 1]])
+        seqs = range(c.batch) if check_seqs is None else check_seqs
+        return q, out, list(seqs)
+
+    def oracle(self, q, seqs):
+        ks = np.concatenate([self.hist_k[b] for b in seqs])
+        vs = np.concatenate([self.hist_v[b] for b in seqs])
+        lens = np.array([self.hist_k[b].shape[0] for b in seqs], np.int32)
+        off = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+        return orc.decode_linear(q[seqs], ks, vs, off, self.first[seqs], lens,
+                                 self.pos[seqs].astype(np.int32), self.c.left_pad[seqs],
+                                 self.c.window)
+
+
+def _small_case(d, g, W, A, seed, B=6, steps=None):
+    rng = si.rng_for(seed)
+    L = rng.integers(1, 4 * W, size=B).astype(np.int32)
+    L[0] = 1
+    L[1] = W - 1 if W > 1 else 1
+    lo = np.array([rng.integers(0, min(int(l), 7)) for l in L], np.int32)
+    tail = np.minimum(L, W).astype(np.int32)
+    return si.DecodeCase("small", batch=B, hq=2 * g, hkv=2, d=d, window=W, ring_rows=W + A,
+                         prompt_lens=L, left_pad=lo, tail_lens=tail,
+                         steps=steps or 2 * A + 3, seed=seed)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d,g,W,A", [(64, 1, 40, 8), (128, 4, 100, 16), (256, 2, 50, 64),
+                                     (512, 2, 30, 8), (256, 8, 33, 5)])
+def test_ring_decode_equals_linear_decode_every_step(dtype, d, g, W, A):
+    require_gpu()
+    case = _small_case(d, g, W, A, seed=d + g + W)
+    run = DecodeRun(case, dtype)
+    for s in range(case.steps):
+        log("decode small d=%d g=%d W=%d A=%d %s step %d" % (d, g, W, A, dtype, s))
+        q, out, seqs = run.step(s)
+        want = run.oracle(q, seqs)
+        assert_close(out, want, dtype, "step %d" % s)
+    m = host(run.meta)
+    assert not (m[:, 3] < 0).any(), "a sequence overflowed its ring"
+
+
+def test_decode_window_one_is_exact():
+    """W = 1: the query reads only its own freshly appended row."""
+    require_gpu()
+    case = _small_case(256, 2, 1, 4, seed=9, steps=7)
+    run = DecodeRun(case, "bf16")
+    for s in range(case.steps):
+        q, out, _ = run.step(s)
+        _, kn, vn = case.step_inputs(s, "bf16")
+        np.testing.assert_array_equal(out, np.repeat(vn, 2, axis=1))
+
+
+def test_decode_needle_follows_the_window():
+    """fp32 sharpness: a dominant key is seen while inside the window and
+    dropped exactly when it leaves it (one-key errors move O by O(1))."""
+    require_gpu()
+    d, W, A = 128, 16, 4
+    case = si.DecodeCase("needle", batch=1, hq=2, hkv=1, d=d, window=W, ring_rows=W + A,
+                         prompt_lens=np.array([W], np.int32), left_pad=np.array([0], np.int32),
+                         tail_lens=np.array([W], np.int32), steps=1, seed=4)
+    run = DecodeRun(case, "f32")
+    direction = np.ones(d, np.float32) / np.sqrt(d)
+    for s in range(2 * W):
+        q, kn, vn = case.step_inputs(s, "f32")
+        q = (q * 0.1 + 4.0 * direction).astype(np.float32)
+        kn = (kn * 0.1).astype(np.float32)
+        if s == 0:
+            kn[0, 0] = 40.0 * direction  # the needle at position W
+        api.cache_roll(run.k, run.v, run.meta, W)
+        api.cache_append(dev(kn), dev(vn), run.k, run.v, run.meta)
+        out = host(api.decode(dev(q), run.k, run.v, run.meta, W))
+        run.pos += 1
+        run.hist_k[0] = np.concatenate([run.hist_k[0], kn])
+        run.hist_v[0] = np.concatenate([run.hist_v[0], vn])
+        want = run.oracle(q, [0])
+        assert_close(out, want, "f32", "needle step %d" % s)
+        needle_v = run.hist_v[0][W, 0].astype(np.float64)
+        sees = np.abs(out[0, 0] - needle_v).max() < 0.05
+        assert sees == (s < W), s
+
+
+def test_decode_batched_b64_70_steps():
+    """64 sequences at random positions in [1, 32768] with left pad 0..63,
+    70 steps spanning the roll: all sequences checked on the steps around
+    the roll, a rotating sample of 8 on every other step."""
+    require_gpu()
+    case = si.decode_b64_d256()
+    run = DecodeRun(case, "bf16")
+    rolled = False
+    for s in range(case.steps):
+        full = s in (0, 1, 62, 63, 64, 65, 69)
+        seqs = None if full else [(s * 8 + i) % case.batch for i in range(8)]
+        log("decode b64 step %d" % s)
+        q, out, seqs = run.step(s, seqs)
+        if s == 64:
+            rolled = True
+        want = run.oracle(q, seqs)
+        assert_close(out[seqs], want, "bf16", "b64 step %d" % s)
+    assert rolled
+    m = host(run.meta)
+    assert not (m[:, 3] < 0).any()
+    # the roll happened exactly once, at step 64: anchor = L - W + 64
+    np.testing.assert_array_equal(m[:, 1], case.prompt_lens - case.window + 64)
+
+
+def test_decode_single_sequence_position_3000():
+    require_gpu()
+    c = si.decode_single_d256()
+    for dtype in ("bf16", "f32"):
+        run = DecodeRun(c, dtype)
+        for s in range(-c.pre_appends, c.steps):
+            q, out, seqs = run.step(s)
+        assert host(run.meta)[0].tolist() == [3000, 1920, 832, 0]
+        want = run.oracle(q, seqs)
+        assert_close(out, want, dtype, "single %s" % dtype)
+
+
+def test_decode_deterministic_and_position_independent_launch():
+    """Two decodes of one state are bit-identical; the workspace size does
+    not depend on positions (one launch shape for every step)."""
+    require_gpu()
+    case = _small_case(256, 2, 64, 64, seed=3, B=4, steps=1)
+    run = DecodeRun(case, "bf16")
+    q, out, _ = run.step(0)
+    out2 = host(api.decode(dev(q), run.k, run.v, run.meta, case.window, workspace=run.ws))
+    np.testing.assert_array_equal(out, out2)
+    assert api.decode_workspace_bytes(4, 4, 2, 256, 128) == api.decode_workspace_bytes(4, 4, 2, 256, 128)

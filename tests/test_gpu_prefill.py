@@ -1,0 +1,178 @@
+"""GPU parity of swa_prefill against the fp64 CPU oracle.
+
+Small cases span several query and key tiles with ragged document tails and
+are compared element by element; the three full-size prefill workloads are
+compared on sampled rows in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import swa_inputs as si
+from oracle import oracle as orc
+from sliding_window_gqa_swa_amd import api
+
+from gpu_util import as_f64, assert_close, dev, host, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+CAUSAL, BLOCKWISE = si.CAUSAL, si.BLOCKWISE
+
+
+def _ids_for(T, cu, seed):
+    """A few image runs per document, including one crossing many rows."""
+    rng = si.rng_for(seed)
+    ids = np.full(T, -1, np.int32)
+    nid = 0
+    for a, b in zip(cu[:-1], cu[1:]):
+        a, b = int(a), int(b)
+        pos = a
+        while pos < b:
+            gap = int(rng.integers(0, 40))
+            ln = int(rng.integers(1, 150))
+            s, e = pos + gap, min(b, pos + gap + ln)
+            if s >= b:
+                break
+            ids[s:e] = nid
+            nid += 1
+            pos = e
+    return ids
+
+
+def _run(q, k, v, cu, ids, W, mode, dtype):
+    out = api.prefill(dev(q), dev(k), dev(v), dev(cu), None if ids is None else dev(ids), W, mode)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+CASES = []
+for d in (64, 128, 256, 512):
+    for dtype in ("bf16", "f32"):
+        for mode in (CAUSAL, BLOCKWISE):
+            CASES.append((d, dtype, mode))
+
+
+@pytest.mark.parametrize("d,dtype,mode", CASES)
+def test_prefill_small_ragged(d, dtype, mode):
+    require_gpu()
+    rng = si.rng_for(10 * d + (dtype == "f32") * 3 + mode)
+    T = 613 if d <= 256 else 389
+    cu = np.array([0, 1, 130, 130, 401, T], np.int32) if d <= 256 else np.array([0, 77, 78, 300, T], np.int32)
+    hkv, g = (2, 2) if d != 128 else (1, 4)
+    hq = hkv * g
+    q = si.normal(rng, (T, hq, d), dtype)
+    k = si.normal(rng, (T, hkv, d), dtype)
+    v = si.normal(rng, (T, hkv, d), dtype)
+    ids = _ids_for(T, cu, d + mode) if mode == BLOCKWISE else None
+    for W in (0, 37, 200):
+        log("prefill small d=%d %s mode=%d W=%d T=%d hq=%d hkv=%d" % (d, dtype, mode, W, T, hq, hkv))
+        got = _run(q, k, v, cu, ids, W, mode, dtype)
+        want = orc.prefill(q, k, v, cu, ids, W, mode)
+        assert_close(got, want, dtype, "d=%d %s mode=%d W=%d" % (d, dtype, mode, W))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_window_one_is_exact(d, dtype):
+    """W = 1: every row attends only to itself, so out = v[i] bit for bit."""
+    require_gpu()
+    rng = si.rng_for(77 + d)
+    T, hkv, g = 333, 2, 2
+    cu = np.array([0, 100, 101, T], np.int32)
+    q = si.normal(rng, (T, hkv * g, d), dtype)
+    k = si.normal(rng, (T, hkv, d), dtype)
+    v = si.normal(rng, (T, hkv, d), dtype)
+    log("prefill W=1 d=%d %s" % (d, dtype))
+    got = _run(q, k, v, cu, None, 1, CAUSAL, dtype)
+    want = np.repeat(v, g, axis=1)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_prefill_needle_marks_window_edge():
+    """bf16 sharpness check: key j carries a strong needle; query rows that
+    may see it output ~v[j], rows just outside the window do not."""
+    require_gpu()
+    d, hkv, g, W = 128, 1, 2, 64
+    T = 512
+    rng = si.rng_for(5)
+    qf = rng.standard_normal((T, hkv * g, d), dtype=np.float32) * 0.1
+    kf = rng.standard_normal((T, hkv, d), dtype=np.float32) * 0.1
+    vf = rng.standard_normal((T, hkv, d), dtype=np.float32)
+    j = 200
+    direction = np.ones(d, np.float32) / np.sqrt(d)
+    qf[:, :, :] += 4.0 * direction
+    kf[j, 0, :] = 40.0 * direction
+    q, k, v = (si.f32_to_bf16_bits(x) for x in (qf, kf, vf))
+    cu = np.array([0, T], np.int32)
+    log("prefill needle")
+    got_bits = _run(q, k, v, cu, None, W, CAUSAL, "bf16")
+    want = orc.prefill(q, k, v, cu, None, W, CAUSAL)
+    assert_close(got_bits, want, "bf16", "needle")
+    got = as_f64(got_bits)
+    vj = as_f64(v)[j, 0]
+    for i in (j - 1, j, j + W - 1, j + W):
+        near = np.abs(got[i, 0] - vj).max() < 0.1
+        assert near == (j <= i < j + W), (i, np.abs(got[i, 0] - vj).max())
+
+
+def test_prefill_edge_shapes():
+    """One token, documents of length 1, empty documents, T smaller than a
+    tile, and an empty batch."""
+    require_gpu()
+    d, hkv, g = 128, 2, 2
+    for cu_list in ([0, 1], [0, 1, 2, 3], [0, 0, 5, 5, 9], [0, 130]):
+        cu = np.array(cu_list, np.int32)
+        T = int(cu[-1])
+        rng = si.rng_for(T)
+        q = si.normal(rng, (T, hkv * g, d), "bf16")
+        k = si.normal(rng, (T, hkv, d), "bf16")
+        v = si.normal(rng, (T, hkv, d), "bf16")
+        for mode in (CAUSAL, BLOCKWISE):
+            ids = np.zeros(T, np.int32) if mode == BLOCKWISE else None
+            log("prefill edge cu=%s mode=%d" % (cu_list, mode))
+            got = _run(q, k, v, cu, ids, 3, mode, "bf16")
+            want = orc.prefill(q, k, v, cu, ids, 3, mode)
+            assert_close(got, want, "bf16", "edge %s" % cu_list)
+    # empty batch: a no-op
+    z = torch.zeros(0, 4, 128, dtype=torch.bfloat16, device="cuda")
+    zk = torch.zeros(0, 2, 128, dtype=torch.bfloat16, device="cuda")
+    api.prefill(z, zk, zk, torch.zeros(1, dtype=torch.int32, device="cuda"))
+
+
+def test_prefill_deterministic():
+    require_gpu()
+    c = si.prefill_vlm_4096_d256()
+    q, k, v = c.tensors("bf16")
+    args = (dev(q), dev(k), dev(v), dev(c.cu_seqlens), dev(c.ids), c.window, c.mode)
+    log("prefill determinism")
+    a = host(api.prefill(*args))
+    b = host(api.prefill(*args))
+    np.testing.assert_array_equal(a, b)
+
+
+def _sample_rows(c, n, seed):
+    rng = si.rng_for(seed)
+    T = c.T
+    special = [0, T - 1]
+    for s in c.cu_seqlens[:-1]:
+        special += [int(s), min(T - 1, int(s) + c.window - 1), min(T - 1, int(s) + c.window)]
+    if c.ids is not None:
+        edges = np.flatnonzero(np.diff(c.ids)) + 1
+        special += [int(x) for x in edges] + [int(x) - 1 for x in edges]
+    rows = sorted(set(special) | set(int(x) for x in rng.integers(0, T, size=n)))
+    return np.array([r for r in rows if 0 <= r < T], np.int32)
+
+
+@pytest.mark.parametrize("name", list(si.PREFILL_WORKLOADS))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_full_size_sampled_rows(name, dtype):
+    """The benchmark workloads at full size, checked on sampled rows
+    (document starts, window edges, image-block edges and random rows)."""
+    require_gpu()
+    c = si.PREFILL_WORKLOADS[name]()
+    q, k, v = c.tensors(dtype)
+    log("prefill full %s %s" % (name, dtype))
+    got = _run(q, k, v, c.cu_seqlens, c.ids, c.window, c.mode, dtype)
+    rows = _sample_rows(c, 24 if c.d == 512 else 48, 123)
+    want = orc.prefill(q, k, v, c.cu_seqlens, c.ids, c.window, c.mode, rows=rows)
+    assert_close(got[rows], want, dtype, name)
