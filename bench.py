@@ -236,16 +236,16 @@ def cpu_baseline(budget_s=15.0):
     keys = np.minimum(np.arange(c.T) - start + 1, c.window)
     done, flops, t0 = 0, 0, time.perf_counter()
     chunk = 256
-    while done < c.T and time.perf_counter() - t0 < budget_s:
-        rows = order[done:done + chunk]
+    while time.perf_counter() - t0 < budget_s and done < 8 * c.T:
+        rows = order[np.arange(done, done + chunk) % c.T]
         orc.prefill(q, k, v, cu, None, c.window, c.mode, rows=rows, nthreads=threads)
         flops += int(keys[rows].sum()) * 4 * c.d * c.hq
         done += rows.size
     dt = time.perf_counter() - t0
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": "%d of %d query rows (all %d heads) of %s, seeded random order, fp64, %.1f s"
-                  % (done, c.T, c.hq, HEADLINE, dt),
+        "sample": "%d query rows x %d heads of %s (%.2f passes over its %d rows, seeded "
+                  "random order), fp64, %.1f s" % (done, c.hq, HEADLINE, done / c.T, c.T, dt),
     }
 
 
@@ -256,6 +256,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy 4 times (known bytes, for "
+                         "scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this implementation has no multi-GPU path "
@@ -270,6 +273,15 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
 
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     head = bench_prefill(HEADLINE, args.steps, args.warmup, torch, api)
     print("headline %s: %.3f ms, %.1f TFLOP/s" % (HEADLINE, head["ms_per_call"], head["tflops"]),
           file=sys.stderr, flush=True)
