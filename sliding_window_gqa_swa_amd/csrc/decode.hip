@@ -14,13 +14,15 @@
 // Rows that fail it are never loaded, so HBM traffic is the valid rows only.
 //
 // Work split (HBM-bound, arithmetic intensity ~ g flop/byte):
-//   block = (split s of the R rows, kv head [, head block], sequence b);
-//   phase 1 streams K rows with 16-byte loads, each row spread over
-//   LPR lanes that each own 16 bytes, and forms the g query dot products with
-//   a lane-group butterfly; phase 2 turns the split's scores into
-//   exp2(x - m) with block max / sum; phase 3 streams V rows and accumulates
-//   the weighted sum.  Partials (m, l, o) go to the workspace and a second
-//   kernel combines the splits in a fixed order (deterministic).
+//   block = (split s of the R rows, kv head [, head block], sequence b).
+//   One pass: a row is spread over LPR lanes that each own 16 bytes; every
+//   lane keeps U rows of K and V in flight (buffer loads: masked rows use an
+//   out-of-range offset, so they return zeros and move no bytes), forms the
+//   query dot products with a lane-group butterfly and folds the rows into a
+//   running (max, sum, weighted V) state, online-softmax style.  The states
+//   of the row groups and waves are merged in a fixed order; partials
+//   (m, l, o) go to the workspace and a second kernel combines the splits in
+//   a fixed order (deterministic).
 #include <type_traits>
 
 #include "swa_common.h"
@@ -31,8 +33,8 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kMaxRowsPerSplit = 512;  // score buffer <= 16 KB at 8 heads
-constexpr int kTargetBlocks = 1024;  // 4 resident blocks per CU on 256 CUs
+constexpr int kMaxRowsPerSplit = 512;  // bounds the work of one block
+constexpr int kTargetBlocks = 2048;  // 8 resident blocks per CU on 256 CUs
 constexpr float kLog2e = 1.4426950408889634f;
 
 // 16-byte chunk of a row as fp32.
@@ -49,6 +51,21 @@ __device__ __forceinline__ void load_chunk<float>(const float* p, float* f) {
   f[1] = x[1];
   f[2] = x[2];
   f[3] = x[3];
+}
+
+// 16 raw bytes of a row as fp32.
+template <typename T>
+__device__ __forceinline__ void unpack_chunk(const u32x4 w, float* f);
+template <>
+__device__ __forceinline__ void unpack_chunk<__bf16>(const u32x4 w, float* f) {
+  unpack8(w, f);
+}
+template <>
+__device__ __forceinline__ void unpack_chunk<float>(const u32x4 w, float* f) {
+  f[0] = __uint_as_float(w[0]);
+  f[1] = __uint_as_float(w[1]);
+  f[2] = __uint_as_float(w[2]);
+  f[3] = __uint_as_float(w[3]);
 }
 
 template <int D, typename T>
@@ -70,10 +87,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     float qk_scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     int splits) {
   using G = DecGeom<D, T>;
-  extern __shared__ float smem[];
-  float* sc = smem;                                 // [rows_per_split][GB]
-  float* red = smem + (size_t)rows_per_split * GB;  // [waves][GB][D]
-  __shared__ float stat[kDecWaves][GB];
+  __shared__ float red_o[kDecWaves][GB][D];
+  __shared__ float red_m[kDecWaves][GB], red_l[kDecWaves][GB];
 
   const int s = blockIdx.x;
   const int kvh = blockIdx.y / head_blocks;
@@ -84,15 +99,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const int nh = min(GB, g - hb * GB);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int rg = lane / G::LPR;            // row within the wave step
-  const int li = lane - rg * G::LPR;       // lane within the row
+  const int rg = lane / G::LPR;       // row within the wave step
+  const int li = lane - rg * G::LPR;  // lane within the row
 
   const int r0 = s * rows_per_split;
   const int r1 = min(R, r0 + rows_per_split);
-  const int nrows = max(0, r1 - r0);
 
+  // ring state; the physical -> position map needs no division per row:
+  // j = r - start (+R if negative), a = anchor + j
   const int32_t* m = meta + 4 * (size_t)b;
-  const int64_t pos = m[0], anchor = m[1], start = m[2];
+  const int64_t pos = m[0], anchor = m[1];
+  const int start = (int)pos_mod(m[2], R);
   const int64_t lo = m[3] & 0x7fffffff;
   int64_t low = max(lo, (int64_t)0);
   if (W > 0) low = max(low, pos - W + 1);
@@ -112,155 +129,143 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     }
   }
 
-  const T* kbase = k_ring + ((size_t)b * hkv + kvh) * (size_t)R * D;
-  const T* vbase = v_ring + ((size_t)b * hkv + kvh) * (size_t)R * D;
+  // one buffer descriptor per ring: masked rows load from an out-of-range
+  // offset, which returns zeros without touching memory
+  const size_t ring_off = ((size_t)b * hkv + kvh) * (size_t)R * D;
+  const uint32_t ring_bytes = (uint32_t)((size_t)R * D * sizeof(T));
+  const i32x4 krs = make_buffer_rsrc(k_ring + ring_off, ring_bytes);
+  const i32x4 vrs = make_buffer_rsrc(v_ring + ring_off, ring_bytes);
 
-  auto row_valid = [&](int r) -> bool {
-    const int64_t a = anchor + pos_mod((int64_t)r - start, R);
-    return a >= low && a <= high;
-  };
-
-  // ---- phase 1: scores of the split's rows ------------------------------
-  constexpr int U = 4;  // row steps in flight per lane
-  for (int base = 0; base < nrows; base += G::RPI * U) {
-    float kf[U][G::ELT];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int rr = base + u * G::RPI + wave * G::RPW + rg;
-      ok[u] = rr < nrows && row_valid(r0 + rr);
-      if (ok[u]) {
-#pragma unroll
-        for (int c = 0; c < G::CPL; ++c)
-          load_chunk<T>(kbase + (size_t)(r0 + rr) * D + (size_t)(li + c * G::LPR) * G::VEC,
-                        &kf[u][c * G::VEC]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int rr = base + u * G::RPI + wave * G::RPW + rg;
-#pragma unroll
-      for (int j = 0; j < GB; ++j) {
-        float acc = 0.f;
-        if (ok[u]) {
-#pragma unroll
-          for (int e = 0; e < G::ELT; ++e) acc = fmaf(qv[j][e], kf[u][e], acc);
-        }
-        acc = group_sum<G::LPR>(acc);
-        if (li == 0 && rr < nrows) sc[rr * GB + j] = ok[u] ? acc : -INFINITY;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 2: split max and exp2 weights --------------------------------
-  float mj[GB], lj[GB];
+  float mrun[GB], lrun[GB], acc[GB][G::ELT];
 #pragma unroll
   for (int j = 0; j < GB; ++j) {
-    float x = -INFINITY;
-    for (int rr = threadIdx.x; rr < nrows; rr += kDecThreads) x = fmaxf(x, sc[rr * GB + j]);
-    x = group_max<kWave>(x);
-    if (lane == 0) stat[wave][j] = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    float x = stat[0][j];
-#pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) x = fmaxf(x, stat[w][j]);
-    mj[j] = x;
-  }
-  __syncthreads();  // stat[] is reused below
-#pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    const float mref = mj[j] == -INFINITY ? 0.f : mj[j];
-    float x = 0.f;
-    for (int rr = threadIdx.x; rr < nrows; rr += kDecThreads) {
-      const float p = __builtin_amdgcn_exp2f(sc[rr * GB + j] - mref);
-      sc[rr * GB + j] = p;
-      x += p;
-    }
-    x = group_sum<kWave>(x);
-    if (lane == 0) stat[wave][j] = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    float x = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) x += stat[w][j];
-    lj[j] = x;
-  }
-
-  // ---- phase 3: weighted sum of V rows ------------------------------------
-  float acc[GB][G::ELT];
-#pragma unroll
-  for (int j = 0; j < GB; ++j)
+    mrun[j] = -INFINITY;
+    lrun[j] = 0.f;
 #pragma unroll
     for (int e = 0; e < G::ELT; ++e) acc[j][e] = 0.f;
-  for (int base = 0; base < nrows; base += G::RPI * U) {
-    float vf[U][G::ELT];
+  }
+
+  constexpr int U = 4;  // row steps in flight per lane (K and V loads)
+  for (int base = r0; base < r1; base += G::RPI * U) {
+    u32x4 kw[U][G::CPL], vw[U][G::CPL];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int rr = base + u * G::RPI + wave * G::RPW + rg;
-      ok[u] = rr < nrows && row_valid(r0 + rr);
-      if (ok[u]) {
+      const int r = base + u * G::RPI + wave * G::RPW + rg;
+      int jj = r - start;
+      jj += jj < 0 ? R : 0;
+      const int64_t a = anchor + jj;
+      ok[u] = r < r1 && a >= low && a <= high;
+      const int32_t row_byte = r * (int32_t)(D * sizeof(T));
 #pragma unroll
-        for (int c = 0; c < G::CPL; ++c)
-          load_chunk<T>(vbase + (size_t)(r0 + rr) * D + (size_t)(li + c * G::LPR) * G::VEC,
-                        &vf[u][c * G::VEC]);
+      for (int c = 0; c < G::CPL; ++c) {
+        const int32_t off = ok[u] ? row_byte + (li + c * G::LPR) * 16 : kBufferOob;
+        kw[u][c] = buffer_load16(krs, off);
+        vw[u][c] = buffer_load16(vrs, off);
       }
     }
+    // scores (identical in every lane of a row group)
+    float sc[U][GB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (!ok[u]) continue;
-      const int rr = base + u * G::RPI + wave * G::RPW + rg;
+      float kf[G::ELT];
+#pragma unroll
+      for (int c = 0; c < G::CPL; ++c) unpack_chunk<T>(kw[u][c], &kf[c * G::VEC]);
 #pragma unroll
       for (int j = 0; j < GB; ++j) {
-        const float p = sc[rr * GB + j];
+        float x = 0.f;
 #pragma unroll
-        for (int e = 0; e < G::ELT; ++e) acc[j][e] = fmaf(p, vf[u][e], acc[j][e]);
+        for (int e = 0; e < G::ELT; ++e) x = fmaf(qv[j][e], kf[e], x);
+        x = group_sum<G::LPR>(x);
+        sc[u][j] = ok[u] ? x : -INFINITY;
+      }
+    }
+    // online softmax over the batch, then the weighted V rows
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      float bm = sc[0][j];
+#pragma unroll
+      for (int u = 1; u < U; ++u) bm = fmaxf(bm, sc[u][j]);
+      const float mnew = fmaxf(mrun[j], bm);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(mrun[j] - mref);
+      mrun[j] = mnew;
+      float p[U];
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        p[u] = __builtin_amdgcn_exp2f(sc[u][j] - mref);
+        psum += p[u];
+      }
+      lrun[j] = lrun[j] * alpha + psum;
+#pragma unroll
+      for (int e = 0; e < G::ELT; ++e) acc[j][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float vf[G::ELT];
+#pragma unroll
+        for (int c = 0; c < G::CPL; ++c) unpack_chunk<T>(vw[u][c], &vf[c * G::VEC]);
+#pragma unroll
+        for (int e = 0; e < G::ELT; ++e) acc[j][e] = fmaf(p[u], vf[e], acc[j][e]);
       }
     }
   }
-  // reduce over the row groups of the wave (lanes differing above LPR)
+
+  // merge the row groups of the wave (lanes that differ above LPR)
 #pragma unroll
-  for (int o = G::LPR; o < kWave; o <<= 1)
+  for (int o = G::LPR; o < kWave; o <<= 1) {
 #pragma unroll
-    for (int j = 0; j < GB; ++j)
+    for (int j = 0; j < GB; ++j) {
+      const float m2 = __shfl_xor(mrun[j], o, kWave);
+      const float l2 = __shfl_xor(lrun[j], o, kWave);
+      const float M = fmaxf(mrun[j], m2);
+      const float Mr = M == -INFINITY ? 0.f : M;
+      const float e1 = __builtin_amdgcn_exp2f(mrun[j] - Mr);
+      const float e2 = __builtin_amdgcn_exp2f(m2 - Mr);
+      lrun[j] = lrun[j] * e1 + l2 * e2;
 #pragma unroll
-      for (int e = 0; e < G::ELT; ++e) acc[j][e] += __shfl_xor(acc[j][e], o, kWave);
+      for (int e = 0; e < G::ELT; ++e) {
+        const float a2 = __shfl_xor(acc[j][e], o, kWave);
+        acc[j][e] = acc[j][e] * e1 + a2 * e2;
+      }
+      mrun[j] = M;
+    }
+  }
   if (rg == 0) {
 #pragma unroll
-    for (int j = 0; j < GB; ++j)
+    for (int j = 0; j < GB; ++j) {
 #pragma unroll
       for (int c = 0; c < G::CPL; ++c)
 #pragma unroll
         for (int e = 0; e < G::VEC; ++e)
-          red[((size_t)wave * GB + j) * D + (li + c * G::LPR) * G::VEC + e] =
-              acc[j][c * G::VEC + e];
+          red_o[wave][j][(li + c * G::LPR) * G::VEC + e] = acc[j][c * G::VEC + e];
+      if (li == 0) {
+        red_m[wave][j] = mrun[j];
+        red_l[wave][j] = lrun[j];
+      }
+    }
   }
   __syncthreads();
+  // merge the waves in a fixed order and write the split partial
   for (int idx = threadIdx.x; idx < nh * D; idx += kDecThreads) {
     const int j = idx / D, dd = idx - j * D;
-    float x = 0.f;
+    float M = red_m[0][j];
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) x += red[((size_t)w * GB + j) * D + dd];
+    for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, red_m[w][j]);
+    const float Mr = M == -INFINITY ? 0.f : M;
+    float x = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float e = __builtin_amdgcn_exp2f(red_m[w][j] - Mr);
+      x += red_o[w][j][dd] * e;
+      l += red_l[w][j] * e;
+    }
     ws_o[(((size_t)b * hq + h0 + j) * splits + s) * D + dd] = x;
-  }
-  if (threadIdx.x < nh) {
-    const int j = threadIdx.x;
-    float mm = 0.f, ll = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < GB; ++jj)
-      if (jj == j) {
-        mm = mj[jj];
-        ll = lj[jj];
-      }
-    float* ml = ws_ml + (((size_t)b * hq + h0 + j) * splits + s) * 2;
-    ml[0] = mm;
-    ml[1] = ll;
+    if (dd == 0) {
+      float* ml = ws_ml + (((size_t)b * hq + h0 + j) * splits + s) * 2;
+      ml[0] = M;
+      ml[1] = l;
+    }
   }
 }
 
@@ -298,9 +303,8 @@ int launch_decode_t(const void* q, const void* k_ring, const void* v_ring,
                     void* workspace, const DecodePlan& p, hipStream_t stream) {
   float* ws_o = (float*)workspace;
   float* ws_ml = ws_o + (size_t)batch * hq * p.splits * D;
-  const size_t lds = ((size_t)p.rows_per_split * GB + (size_t)kDecWaves * GB * D) * sizeof(float);
   dim3 grid(p.splits, hkv * p.head_blocks, batch);
-  hipLaunchKernelGGL((decode_split_kernel<D, T, GB>), grid, dim3(kDecThreads), lds, stream,
+  hipLaunchKernelGGL((decode_split_kernel<D, T, GB>), grid, dim3(kDecThreads), 0, stream,
                      (const T*)q, (const T*)k_ring, (const T*)v_ring, meta, window,
                      ring_rows, hq, hkv, p.head_blocks, p.rows_per_split,
                      scale * kLog2e, ws_o, ws_ml, p.splits);

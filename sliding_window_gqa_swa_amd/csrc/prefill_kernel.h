@@ -15,26 +15,35 @@
 //   hi_i = i                                      (causal)
 //   hi_i = max(i, last token of i's image run)    (blockwise, image token)
 // because an image block is a run of consecutive tokens and the window is
-// one-sided.  A work-group therefore needs only [min lo, max hi] of its rows
-// as its key range (tile skipping by document, window and block bounds:
-// masked key tiles cost nothing) and masks only the key tiles that are not
-// inside every row's interval.
+// one-sided.  A work-group therefore visits only the key tiles inside
+// [min lo, max hi] of its rows (tile skipping by document, window and block
+// bounds: masked key tiles cost nothing) and masks only the tiles that are
+// not inside every row's interval.
 //
-// Layout of the work ([SDPA] Summary notes that fused kernels there needed
-// K/V repeated per query head; here they are not):
-//   work-group = BM query rows x GH query heads of one kv head; K and V
-//   tiles of BN keys are staged once in LDS and read by every wave, so the
-//   GH heads of a group share them.  Each wave owns 16*MB query rows of one
-//   head.
-//   S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (fp32 inputs:
-//   v_mfma_f32_16x16x4_f32): K fragments come from LDS, Q fragments stay in
-//   registers, and the S^T accumulator puts one query row per lane, so the
-//   softmax row statistics live in the lane (plus a 4-lane butterfly).
-//   O^T += V^T P^T takes P straight from the S^T accumulator registers as
-//   the B operand; V is stored transposed in LDS ([d][key]) so that its A
-//   fragments are two 8-byte LDS reads.
-//   Online softmax in the log2 domain with exp2, fp32 accumulators, a final
-//   1/l and a round-to-nearest-even store.
+// Work layout:
+//   work-group = BM query rows x GH query heads of one kv head; the K and V
+//   tiles (BN keys) are staged once in LDS and read by every wave, so the
+//   GH heads of a GQA group share them ([SDPA] Summary: there K/V had to be
+//   repeated per query head).  Each wave owns 16*MB rows of one head.
+//   Work-groups are numbered so that each XCD (own L2) receives a
+//   contiguous run of (head group, query tile) work: the K/V rows of a
+//   head are fetched from HBM into one L2 instead of eight.
+//   Pipeline: while a tile is consumed from one LDS buffer, the next tile's
+//   rows are already in flight to registers; they are written to the other
+//   buffer afterwards (one barrier per tile).  LDS rows are padded (K by 16
+//   bytes, V by 32 bytes) so that the 16-byte K fragment reads and the
+//   transposed V reads hit distinct banks, and every fragment address is a
+//   lane base plus an immediate offset.
+//   bf16: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K fragments from LDS
+//   and Q fragments held in registers; the S^T accumulator holds one query
+//   row per lane, so the softmax row statistics stay in the lane (plus a
+//   4-lane butterfly).  O^T += V^T P^T takes P straight from the
+//   accumulator as the B operand and V^T fragments with ds_read_b64_tr_b16
+//   from the row-major V tile.  fp32 inputs use v_mfma_f32_16x16x4_f32 on
+//   the same pipeline, mask and softmax.
+//   Online softmax in the log2 domain: the running reference max moves only
+//   when a score exceeds it by more than kRescaleSlack (so most tiles skip
+//   the O rescale), p = exp2(s*c - m*c) is one FMA and one exp2.
 #pragma once
 
 #include <type_traits>
@@ -44,23 +53,29 @@
 namespace swa {
 
 constexpr float kPrefillLog2e = 1.4426950408889634f;
+// exp2 arguments stay <= this between reference-max moves (p <= 2^8)
+constexpr float kRescaleSlack = 8.0f;
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+
+// a*b - c with the product rounded on its own (never fused into an FMA)
+__device__ __forceinline__ float mul_then_sub(float a, float b, float c) {
+#pragma clang fp contract(off)
+  return a * b - c;
+}
 
 template <typename T>
 struct PfTraits;
-
 template <>
 struct PfTraits<__bf16> {
-  static constexpr int VEC = 8;   // elements per 16-byte chunk
-  static constexpr int KW = 32;   // head-dim elements per S^T MFMA
-  static constexpr int KPAD = 8;  // LDS row pad of Ks (elements = 16 bytes)
-  static constexpr int VPAD = 4;  // LDS row pad of Vt (elements = 8 bytes)
+  static constexpr int VEC = 8;  // elements per 16-byte chunk
+  static constexpr int KW = 32;  // head-dim elements per S^T MFMA step
 };
 template <>
 struct PfTraits<float> {
   static constexpr int VEC = 4;
-  static constexpr int KW = 16;   // one 16-byte LDS read feeds 4 MFMAs of 4
-  static constexpr int KPAD = 4;
-  static constexpr int VPAD = 4;
+  static constexpr int KW = 16;  // one 16-byte LDS read feeds 4 MFMAs of K=4
 };
 
 // Workgroup geometry.
@@ -71,29 +86,34 @@ struct PfGeom {
   static constexpr int WR = 16 * MB;        // query rows per wave
   static constexpr int RB = NW / GH;        // row blocks per work-group
   static constexpr int BM = RB * WR;        // query rows per work-group
-  static constexpr int KS = D + TR::KPAD;   // Ks row stride (elements)
-  static constexpr int VS = BN + TR::VPAD;  // Vt row stride (elements)
-  static constexpr int LDS_K = BN * KS;
-  static constexpr int LDS_V = D * VS;
+  static constexpr int CPR = D / TR::VEC;   // 16-byte chunks per K/V row
+  static constexpr int KS = D + TR::VEC;    // padded K row (elements): +16 bytes
+  static constexpr int VS = D + 2 * TR::VEC;  // padded V row: +32 bytes
+  static constexpr int TILE_K = BN * KS;
+  static constexpr int TILE_V = BN * VS;
+  static constexpr int UNITS = BN * CPR;    // 16-byte chunks per tile
+  static constexpr int UPT = UNITS / NT;    // chunks per thread per tile
   static constexpr int QREG = D / TR::KW;   // Q fragments per q-block
   static_assert(NW % GH == 0, "waves must split evenly over heads");
   static_assert(BN % (std::is_same<T, float>::value ? 16 : 32) == 0,
                 "key tile is a whole number of P^T fragments");
   static_assert(BM <= NT, "one thread per tile row in the prologue");
+  static_assert(UNITS % NT == 0, "tile chunks split evenly over threads");
 };
 
 template <int D, typename T, int MB, int BN, int NW, int GH>
-__global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
+__global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 256 && !std::is_same<T, float>::value) ? 2 : 1)
+void prefill_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ cu, int ndocs, const int32_t* __restrict__ ids,
     int W, int mode, T* __restrict__ out, int Ttot, int hq, int hkv,
-    float qk_scale_log2, int ntiles) {
+    float qk_scale_log2, int ntiles, int nwork, int work_per_xcd) {
   using G = PfGeom<D, T, MB, BN, NW, GH>;
   using TR = typename G::TR;
   constexpr bool kF32 = std::is_same<T, float>::value;
 
-  __shared__ __attribute__((aligned(16))) T Ks[G::LDS_K];
-  __shared__ __attribute__((aligned(16))) T Vt[G::LDS_V];
+  __shared__ __attribute__((aligned(16))) T Ks[2][G::TILE_K];
+  __shared__ __attribute__((aligned(16))) T Vs[2][G::TILE_V];
   __shared__ int lo_s[G::BM], hi_s[G::BM];
   __shared__ int red_s[4][NW];
   __shared__ unsigned long long runmask_s[(G::BM + 63) / 64];
@@ -105,15 +125,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
   const int c16 = lane & 15;  // MFMA column lane: one query row
   const int grp = lane >> 4;  // MFMA 4-lane group
 
-  // heavy (late) tiles first: causal work grows along a document
-  const int tile = ntiles - 1 - (int)blockIdx.x;
+  // XCD-aware numbering: blocks are dispatched round-robin over 8 XCDs, so
+  // block b runs on XCD b % 8; give that XCD a contiguous slice of work.
+  const int b = (int)blockIdx.x;
+  const int work = (b & 7) * work_per_xcd + (b >> 3);
+  if (work >= nwork) return;  // uniform per block
+  const int hg_index = work / ntiles;
+  const int tile = ntiles - 1 - (work - hg_index * ntiles);  // heavy tiles first
   const int q0 = tile * G::BM;
   const int g = hq / hkv;
   const int hgroups = g / GH;
-  const int kvh = blockIdx.y / hgroups;
-  const int hbase = kvh * g + (blockIdx.y - kvh * hgroups) * GH;
-  const int jh = wave % GH;        // head of this wave within the group
-  const int rb = wave / GH;        // row block of this wave
+  const int kvh = hg_index / hgroups;
+  const int hbase = kvh * g + (hg_index - kvh * hgroups) * GH;
+  const int jh = wave % GH;  // head of this wave within the group
+  const int rb = wave / GH;  // row block of this wave
   const int h = hbase + jh;
 
   // ---- prologue: per-row key interval [lo_i, hi_i] ------------------------
@@ -122,8 +147,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
     const int i = q0 + tid;
     int lo = 1, hi = 0;  // empty interval for rows past the end
     if (i < Ttot) {
-      // upper_bound over cu: first d with cu[d] > i
-      int a = 0, bnd = ndocs + 1;
+      int a = 0, bnd = ndocs + 1;  // upper_bound over cu: first d with cu[d] > i
       while (a < bnd) {
         const int mid = (a + bnd) >> 1;
         if (cu[mid] > i) bnd = mid; else a = mid + 1;
@@ -131,7 +155,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
       const int doc = a - 1;
       int ds = (doc >= 0 && doc < ndocs) ? cu[doc] : i;
       int de = (doc >= 0 && doc < ndocs) ? cu[doc + 1] : i + 1;
-      ds = min(max(ds, 0), i);       // clamp against malformed cu_seqlens
+      ds = min(max(ds, 0), i);  // clamp against malformed cu_seqlens
       de = max(min(de, Ttot), i + 1);
       lo = (W > 0) ? max(ds, i - W + 1) : ds;
       hi = i;
@@ -179,11 +203,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
     }
     __syncthreads();
     if (tid < G::BM && q0 + tid < Ttot && my_id >= 0) {
-      const int w = tid >> 6, b = tid & 63;
+      const int w = tid >> 6, bb = tid & 63;
       int end = -1;
       for (int ww = w; ww < (G::BM + 63) / 64 && end < 0; ++ww) {
         unsigned long long m = runmask_s[ww];
-        if (ww == w) m &= (~0ull) << b;
+        if (ww == w) m &= (~0ull) << bb;
         if (m) end = ww * 64 + __builtin_ctzll(m);
       }
       if (end >= G::BM) end = -1;  // bits past the tile belong to no row
@@ -226,19 +250,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
   }
   if (kmax < kmin) return;  // no valid row in this tile (uniform exit)
 
-  // this lane's rows: one per q-block
-  int row_i[MB], row_lo[MB], row_hi[MB];
+  // this lane's rows: one per q-block.  Key j is allowed iff
+  // (unsigned)(j - lo) <= (unsigned)(hi - lo); rows with an empty interval
+  // get lo far above every key so the test always fails.
+  int row_i[MB], row_lo[MB];
+  unsigned row_rng[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int t = rb * G::WR + mb * 16 + c16;
     row_i[mb] = q0 + t;
-    row_lo[mb] = lo_s[t];
-    row_hi[mb] = hi_s[t];
+    const int lo = lo_s[t], hi = hi_s[t];
+    row_lo[mb] = hi >= lo ? lo : 0x3fffffff;
+    row_rng[mb] = hi >= lo ? (unsigned)(hi - lo) : 0u;
   }
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ---------
   // bf16: fragment kk holds d = kk*32 + 8*grp + e (e < 8);
-  // fp32: lane group grp owns d = grp*D/4 + c, read 4 at a time.
+  // fp32: lane group grp owns d = grp*D/4 + ..., 4 per fragment.
   using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
   QF qf[MB][G::QREG];
 #pragma unroll
@@ -249,21 +277,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
 #pragma unroll
     for (int kk = 0; kk < G::QREG; ++kk) {
       const int d0 = kF32 ? grp * (D / 4) + kk * 4 : kk * 32 + 8 * grp;
-      QF x;
-      if (ok)
-        x = *reinterpret_cast<const QF*>(qrow + d0);
-      else
-        x = QF{};
+      QF x = QF{};
+      if (ok) x = *reinterpret_cast<const QF*>(qrow + d0);
       qf[mb][kk] = x;
     }
   }
 
   // ---- accumulators ----------------------------------------------------------
   floatx4 o_acc[MB][D / 16];
-  float m_run[MB], l_part[MB];
+  float m_ref[MB], l_part[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    m_run[mb] = -INFINITY;
+    m_ref[mb] = -INFINITY;
     l_part[mb] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) o_acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -272,49 +297,61 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
   const size_t kv_row_stride = (size_t)hkv * D;
   const T* kbase = k + (size_t)kvh * D;
   const T* vbase = v + (size_t)kvh * D;
-  constexpr int CPR = D / TR::VEC;  // 16-byte chunks per row
+  const float c_scale = qk_scale_log2;
+  const float slack = kRescaleSlack / c_scale;  // in raw score units
 
-  for (int k0 = (kmin / BN) * BN; k0 <= kmax; k0 += BN) {
-    __syncthreads();  // previous tile's LDS reads are done
-    // K tile -> Ks[key][d]
-    for (int u = tid; u < BN * CPR; u += G::NT) {
-      const int r = u / CPR, ch = u - r * CPR;
-      const int j = k0 + r;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (j < Ttot) x = *reinterpret_cast<const u32x4*>(kbase + (size_t)j * kv_row_stride + ch * TR::VEC);
-      *reinterpret_cast<u32x4*>(&Ks[r * G::KS + ch * TR::VEC]) = x;
-    }
-    // V tile -> Vt[d][key], 4 keys x one 16-byte chunk per unit
-    for (int u = tid; u < (BN / 4) * CPR; u += G::NT) {
-      const int kq = u % (BN / 4), ch = u / (BN / 4);
-      u32x4 x[4];
+  // global -> registers for one tile, registers -> padded LDS.  Rows past
+  // the end are clamped to the last row (finite data, masked out later).
+  u32x4 kreg[G::UPT], vreg[G::UPT];
+  int unit_off[G::UPT], unit_row[G::UPT];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = k0 + 4 * kq + r;
-        x[r] = u32x4{0u, 0u, 0u, 0u};
-        if (j < Ttot) x[r] = *reinterpret_cast<const u32x4*>(vbase + (size_t)j * kv_row_stride + ch * TR::VEC);
+  for (int i = 0; i < G::UPT; ++i) {
+    const int u = tid + i * G::NT;
+    const int r = u / G::CPR, ch = u - r * G::CPR;
+    unit_row[i] = r;
+    unit_off[i] = r * (int)kv_row_stride + ch * TR::VEC;
+  }
+  auto load_tile = [&](int k0) {
+    const T* kt = kbase + (size_t)k0 * kv_row_stride;  // uniform
+    const T* vt = vbase + (size_t)k0 * kv_row_stride;
+    if (k0 + BN <= Ttot) {
+#pragma unroll
+      for (int i = 0; i < G::UPT; ++i) {
+        kreg[i] = *reinterpret_cast<const u32x4*>(kt + unit_off[i]);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vt + unit_off[i]);
       }
-      if constexpr (kF32) {
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          u32x4 col = {x[0][e], x[1][e], x[2][e], x[3][e]};
-          *reinterpret_cast<u32x4*>(&Vt[(ch * 4 + e) * G::VS + 4 * kq]) = col;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          const bool hiw = e & 1;
-          uint32_t a0 = hiw ? (x[0][w] >> 16) : (x[0][w] & 0xffffu);
-          uint32_t a1 = hiw ? (x[1][w] >> 16) : (x[1][w] & 0xffffu);
-          uint32_t a2 = hiw ? (x[2][w] >> 16) : (x[2][w] & 0xffffu);
-          uint32_t a3 = hiw ? (x[3][w] >> 16) : (x[3][w] & 0xffffu);
-          u32x2 col = {a0 | (a1 << 16), a2 | (a3 << 16)};
-          *reinterpret_cast<u32x2*>(&Vt[(ch * 8 + e) * G::VS + 4 * kq]) = col;
-        }
+      for (int i = 0; i < G::UPT; ++i) {
+        const int back = max(k0 + unit_row[i] - (Ttot - 1), 0) * (int)kv_row_stride;
+        kreg[i] = *reinterpret_cast<const u32x4*>(kt + unit_off[i] - back);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vt + unit_off[i] - back);
       }
     }
-    __syncthreads();
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < G::UPT; ++i) {
+      const int u = tid + i * G::NT;
+      const int r = u / G::CPR, ch = u - r * G::CPR;
+      *reinterpret_cast<u32x4*>(&Ks[buf][r * G::KS + ch * TR::VEC]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&Vs[buf][r * G::VS + ch * TR::VEC]) = vreg[i];
+    }
+  };
+
+  const int kt0 = (kmin / BN) * BN;
+  const int ntile_k = (kmax - kt0) / BN + 1;
+  load_tile(kt0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int it = 0; it < ntile_k; ++it) {
+    const int k0 = kt0 + it * BN;
+    const int buf = it & 1;
+    const bool more = it + 1 < ntile_k;
+    if (more) load_tile(k0 + BN);  // in flight during the compute below
+    const T* Kb = Ks[buf];
+    const T* Vb = Vs[buf];
 
     // ---- S^T = K Q^T for this wave's rows ---------------------------------
     floatx4 s[MB][BN / 16];
@@ -326,17 +363,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
     for (int kk = 0; kk < G::QREG; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < BN / 16; ++kb) {
+        const int r = kb * 16 + c16;
         if constexpr (kF32) {
-          const floatx4 a = *reinterpret_cast<const floatx4*>(
-              &Ks[(kb * 16 + c16) * G::KS + grp * (D / 4) + kk * 4]);
+          const floatx4 a = *reinterpret_cast<const floatx4*>(&Kb[r * G::KS + grp * (D / 4) + kk * 4]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int st = 0; st < 4; ++st)
               s[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], qf[mb][kk][st], s[mb][kb], 0, 0, 0);
         } else {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &Ks[(kb * 16 + c16) * G::KS + kk * 32 + 8 * grp]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kb[r * G::KS + kk * 32 + 8 * grp]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             s[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[mb][kk], s[mb][kb], 0, 0, 0);
@@ -344,43 +380,55 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
       }
     }
 
-    // ---- mask, online softmax ---------------------------------------------
+    // ---- mask, online softmax (raw scores; exp2 argument s*c - m*c) ---------
     const bool full = (k0 >= lomax) && (k0 + BN - 1 <= himin);
+    bool any_move = false;
+    float alpha[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      if (!full) {  // uniform: only tiles on a diagonal, window or block edge
+        const int rel0 = k0 + 4 * grp - row_lo[mb];
+#pragma unroll
+        for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            s[mb][kb][r] = (unsigned)(rel0 + kb * 16 + r) <= row_rng[mb] ? s[mb][kb][r] : -INFINITY;
+      }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < BN / 16; ++kb) {
+      for (int kb = 0; kb < BN / 16; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = s[mb][kb][r] * qk_scale_log2;
-          if (!full) {
-            const int j = k0 + kb * 16 + 4 * grp + r;
-            if (j < row_lo[mb] || j > row_hi[mb]) x = -INFINITY;
-          }
-          s[mb][kb][r] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      }
+        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[mb][kb][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run[mb], tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[mb] - m_use);
-      m_run[mb] = m_new;
+      // move the reference only when a score exceeds it by the slack
+      const bool move = tmax > m_ref[mb] + slack;
+      const float m_new = move ? tmax : m_ref[mb];
+      alpha[mb] = move ? __builtin_amdgcn_exp2f((m_ref[mb] - m_new) * c_scale) : 1.f;
+      any_move |= move;
+      m_ref[mb] = m_new;
+      const float mc = m_new == -INFINITY ? 0.f : m_new * c_scale;
       float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < BN / 16; ++kb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[mb][kb][r] - m_use);
+          // fp32: exact s*c - m*c, so a row's maximum gets weight exactly 1;
+          // bf16 (P is rounded to bf16 anyway): one FMA
+          const float arg = kF32 ? mul_then_sub(s[mb][kb][r], c_scale, mc)
+                                 : __builtin_fmaf(s[mb][kb][r], c_scale, -mc);
+          const float p = __builtin_amdgcn_exp2f(arg);
           s[mb][kb][r] = p;
           lsum += p;
         }
       }
-      l_part[mb] = l_part[mb] * alpha + lsum;
+      l_part[mb] = l_part[mb] * alpha[mb] + lsum;
+    }
+    if (__builtin_amdgcn_ballot_w64(any_move)) {  // rare after the first tiles
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) o_acc[mb][dt] *= alpha;
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o_acc[mb][dt] *= alpha[mb];
     }
 
     // ---- O^T += V^T P^T --------------------------------------------------
@@ -389,16 +437,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
       for (int kb = 0; kb < BN / 16; ++kb) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          const floatx4 a = *reinterpret_cast<const floatx4*>(
-              &Vt[(dt * 16 + c16) * G::VS + kb * 16 + 4 * grp]);
+          const int d = dt * 16 + c16;
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
+          for (int st = 0; st < 4; ++st) {
+            const int r = kb * 16 + 4 * grp + st;
+            const float a = Vb[r * G::VS + d];
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
-              o_acc[mb][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], s[mb][kb][st], o_acc[mb][dt], 0, 0, 0);
+            for (int mb = 0; mb < MB; ++mb)
+              o_acc[mb][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[mb][kb][st], o_acc[mb][dt], 0, 0, 0);
+          }
         }
       }
     } else {
+      const int tr_r = (lane & 15) >> 2, tr_m = lane & 3;  // transpose-read lane role
 #pragma unroll
       for (int ks = 0; ks < BN / 32; ++ks) {
         // P^T fragment: keys 32ks + 4grp + (0..3) and 32ks + 16 + 4grp + (0..3)
@@ -411,19 +462,30 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
             pf[mb][4 + r] = (__bf16)s[mb][2 * ks + 1][r];
           }
         }
+        const int r0 = ks * 32 + 4 * grp + tr_r;  // row read by this lane (first half)
+        const int r1 = r0 + 16;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          const T* vrow = &Vt[(dt * 16 + c16) * G::VS + ks * 32 + 4 * grp];
-          const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + 16);
-          const u32x4 w = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          const bf16x8 a = __builtin_bit_cast(bf16x8, w);
+          // lane (grp, 4*tr_r + tr_m) addresses row r, elements dt*16 + 4*tr_m .. +4;
+          // the transpose read hands lane c16 the column dt*16 + c16 of rows
+          // 32ks + 4grp .. +3 (and +16 .. +19 for the second read)
+          const __bf16* p0 = &Vb[r0 * G::VS + dt * 16 + 4 * tr_m];
+          const __bf16* p1 = &Vb[r1 * G::VS + dt * 16 + 4 * tr_m];
+          const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4v*)(p0));
+          const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4v*)(p1));
+          const short8v x8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          const bf16x8 a = __builtin_bit_cast(bf16x8, x8);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             o_acc[mb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[mb], o_acc[mb][dt], 0, 0, 0);
         }
       }
     }
+
+    if (more) store_tile(buf ^ 1);  // the other buffer: free since the last barrier
+    __syncthreads();
   }
 
   // ---- epilogue: normalise and store ------------------------------------------
@@ -443,9 +505,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_fwd_kernel(
       if constexpr (kF32) {
         *reinterpret_cast<floatx4*>(orow + d0) = x;
       } else {
-        const u32x2 w = {float_to_bf16_bits(x[0]) | (float_to_bf16_bits(x[1]) << 16),
-                         float_to_bf16_bits(x[2]) | (float_to_bf16_bits(x[3]) << 16)};
-        *reinterpret_cast<u32x2*>(orow + d0) = w;
+        const bf16x4 w = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};  // RNE
+        *reinterpret_cast<bf16x4*>(orow + d0) = w;
       }
     }
   }

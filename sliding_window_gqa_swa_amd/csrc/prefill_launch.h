@@ -14,11 +14,13 @@ int launch_prefill_cfg(const void* q, const void* k, const void* v,
   using G = PfGeom<D, T, MB, BN, NW, GH>;
   const int ntiles = (total_tokens + G::BM - 1) / G::BM;
   const int g = hq / hkv;
-  dim3 grid(ntiles, hkv * (g / GH));
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, T, MB, BN, NW, GH>), grid, dim3(G::NT), 0,
-                     stream, (const T*)q, (const T*)k, (const T*)v, cu, num_docs, ids,
-                     window, mode, (T*)out, total_tokens, hq, hkv,
-                     scale * kPrefillLog2e, ntiles);
+  const long long nwork = (long long)ntiles * hkv * (g / GH);
+  const long long per_xcd = (nwork + 7) / 8;  // 8 XCDs, blocks round-robin over them
+  if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, T, MB, BN, NW, GH>), dim3((unsigned)(8 * per_xcd)),
+                     dim3(G::NT), 0, stream, (const T*)q, (const T*)k, (const T*)v, cu,
+                     num_docs, ids, window, mode, (T*)out, total_tokens, hq, hkv,
+                     scale * kPrefillLog2e, ntiles, (int)nwork, (int)per_xcd);
   return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
 }
 

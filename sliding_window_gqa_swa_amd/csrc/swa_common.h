@@ -45,6 +45,29 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
   }
 }
 
+// Raw buffer loads (MUBUF): a 128-bit descriptor {base, num_records bytes,
+// config}; a load whose offset is >= num_records returns zeros and makes no
+// memory access, which gives branch-free predication of HBM reads.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ u32x4 llvm_raw_buffer_load_v4i32(i32x4 rsrc, int32_t voffset, int32_t soffset,
+                                             int32_t aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+
+struct __attribute__((packed)) BufferDesc {
+  const void* base;
+  uint32_t num_records;
+  uint32_t config;
+};
+constexpr uint32_t kBufferConfigGfx9 = 0x00020000u;  // raw 32-bit dword access
+constexpr int32_t kBufferOob = 0x7fffffff;           // an offset that is always out of range
+
+__device__ __forceinline__ i32x4 make_buffer_rsrc(const void* base, uint32_t bytes) {
+  BufferDesc d{base, bytes, kBufferConfigGfx9};
+  return __builtin_bit_cast(i32x4, d);
+}
+__device__ __forceinline__ u32x4 buffer_load16(i32x4 rsrc, int32_t byte_offset) {
+  return llvm_raw_buffer_load_v4i32(rsrc, byte_offset, 0, 0);
+}
+
 // Butterfly sum / max over groups of `width` consecutive lanes (power of 2).
 template <int width>
 __device__ __forceinline__ float group_sum(float x) {
