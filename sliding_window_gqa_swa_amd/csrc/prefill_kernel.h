@@ -28,12 +28,16 @@
 //   Work-groups are numbered so that each XCD (own L2) receives a
 //   contiguous run of (head group, query tile) work: the K/V rows of a
 //   head are fetched from HBM into one L2 instead of eight.
-//   Pipeline: while a tile is consumed from one LDS buffer, the next tile's
-//   rows are already in flight to registers; they are written to the other
-//   buffer afterwards (one barrier per tile).  LDS rows are padded (K by 16
-//   bytes, V by 32 bytes) so that the 16-byte K fragment reads and the
-//   transposed V reads hit distinct banks, and every fragment address is a
-//   lane base plus an immediate offset.
+//   Pipeline: K and V tiles travel HBM -> LDS by direct-to-LDS loads
+//   (global_load_lds_dwordx4, 16 bytes per lane) into a ring of STAGES
+//   buffers, so STAGES-1 tiles are in flight while one is consumed and no
+//   registers are spent on staging.  The loads are issued from inline
+//   assembly, because the compiler would otherwise order every later LDS
+//   read behind all of them; completion is tracked with explicit vmcnt
+//   waits and a plain s_barrier (one per tile).  LDS rows are unpadded; the
+//   16-byte chunk c of row r sits at c ^ f(r) with
+//   f(r) = ((r & 3) << 1) | ((r >> 2) & 1), which keeps the 8-row K
+//   fragment reads and the 4-row transposed V reads on distinct banks.
 //   bf16: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K fragments from LDS
 //   and Q fragments held in registers; the S^T accumulator holds one query
 //   row per lane, so the softmax row statistics stay in the lane (plus a
@@ -53,11 +57,42 @@
 namespace swa {
 
 constexpr float kPrefillLog2e = 1.4426950408889634f;
+// cu_seqlens entries cached in LDS for the per-row document lookup; larger
+// batches of documents search global memory instead
+constexpr int kCuCache = 1024;
 // exp2 arguments stay <= this between reference-max moves (p <= 2^8)
 constexpr float kRescaleSlack = 8.0f;
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
+
+// Chunk swizzle of LDS tiles (16-byte chunk c of row r is stored at c ^ f(r)).
+__device__ __forceinline__ int chunk_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from g land at
+// LDS byte address lds_wave_base + 16 * l (lds_wave_base is wave-uniform).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_wave_base), "v"(g)
+               : "memory");
+}
+
+// s_waitcnt with vmcnt = n (expcnt and lgkmcnt left unconstrained).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Work-group barrier that orders LDS but leaves global/DMA loads in flight
+// (__syncthreads() would also wait for every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // a*b - c with the product rounded on its own (never fused into an FMA)
 __device__ __forceinline__ float mul_then_sub(float a, float b, float c) {
@@ -87,10 +122,13 @@ struct PfGeom {
   static constexpr int RB = NW / GH;        // row blocks per work-group
   static constexpr int BM = RB * WR;        // query rows per work-group
   static constexpr int CPR = D / TR::VEC;   // 16-byte chunks per K/V row
-  static constexpr int KS = D + TR::VEC;    // padded K row (elements): +16 bytes
-  static constexpr int VS = D + 2 * TR::VEC;  // padded V row: +32 bytes
-  static constexpr int TILE_K = BN * KS;
-  static constexpr int TILE_V = BN * VS;
+  static constexpr int TILE = BN * D;       // elements of one K or V tile (unpadded)
+  static constexpr int TILE_BYTES = TILE * (int)sizeof(T);
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V
+  // LDS ring depth: as many stages as fit 64 KB (2 work-groups per CU), at
+  // least 2 and at most 4
+  static constexpr int STAGES = (65536 / STAGE_BYTES) < 2 ? 2
+                                : ((65536 / STAGE_BYTES) > 4 ? 4 : 65536 / STAGE_BYTES);
   static constexpr int UNITS = BN * CPR;    // 16-byte chunks per tile
   static constexpr int UPT = UNITS / NT;    // chunks per thread per tile
   static constexpr int QREG = D / TR::KW;   // Q fragments per q-block
@@ -99,6 +137,8 @@ struct PfGeom {
                 "key tile is a whole number of P^T fragments");
   static_assert(BM <= NT, "one thread per tile row in the prologue");
   static_assert(UNITS % NT == 0, "tile chunks split evenly over threads");
+  static_assert(CPR >= 8, "the chunk swizzle needs 8 chunks per row");
+  static_assert(2 * UPT * (STAGES - 1) <= 63, "loads in flight exceed the vmcnt range");
 };
 
 template <int D, typename T, int MB, int BN, int NW, int GH>
@@ -112,12 +152,12 @@ void prefill_fwd_kernel(
   using TR = typename G::TR;
   constexpr bool kF32 = std::is_same<T, float>::value;
 
-  __shared__ __attribute__((aligned(16))) T Ks[2][G::TILE_K];
-  __shared__ __attribute__((aligned(16))) T Vs[2][G::TILE_V];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[G::STAGES][G::STAGE_BYTES];
   __shared__ int lo_s[G::BM], hi_s[G::BM];
   __shared__ int red_s[4][NW];
   __shared__ unsigned long long runmask_s[(G::BM + 63) / 64];
   __shared__ int ext_end_s, de_last_s;
+  __shared__ int cu_s[kCuCache];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -141,7 +181,65 @@ void prefill_fwd_kernel(
   const int rb = wave / GH;  // row block of this wave
   const int h = hbase + jh;
 
+  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers.  Issued
+  // first so that their latency overlaps the row-interval prologue.
+  // bf16: fragment kk holds d = kk*32 + 8*grp + e (e < 8);
+  // fp32: lane group grp owns d = grp*D/4 + ..., 4 per fragment.
+  using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
+  QF qf[MB][G::QREG];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int i = q0 + rb * G::WR + mb * 16 + c16;
+    const bool ok = i < Ttot;
+    const T* qrow = q + ((size_t)(ok ? i : 0) * hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < G::QREG; ++kk) {
+      const int d0 = kF32 ? grp * (D / 4) + kk * 4 : kk * 32 + 8 * grp;
+      QF x = QF{};
+      if (ok) x = *reinterpret_cast<const QF*>(qrow + d0);
+      qf[mb][kk] = x;
+    }
+  }
+
+  const size_t kv_row_stride = (size_t)hkv * D;
+  const T* kbase = k + (size_t)kvh * D;
+  const T* vbase = v + (size_t)kvh * D;
+  // Direct-to-LDS tile loads.  Wave w issues UPT loads per tensor per tile;
+  // load i covers LDS slots [(w*UPT + i)*64, +64) of 16 bytes, slot s being
+  // row s / CPR, stored chunk s % CPR, i.e. source chunk (s % CPR) ^ f(row).
+  // Rows past the end are clamped to the last row (finite data, masked).
+  int unit_off[G::UPT], unit_row[G::UPT];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+  for (int i = 0; i < G::UPT; ++i) {
+    const int slot = (wave_u * G::UPT + i) * 64 + lane;
+    const int r = slot / G::CPR, pc = slot - r * G::CPR;
+    unit_row[i] = r;
+    unit_off[i] = r * (int)kv_row_stride + (pc ^ chunk_swz(r)) * TR::VEC;
+  }
+  const uint32_t ring_base =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(&ring[0][0]);
+  auto dma_tile = [&](int k0, int stage) {
+    const T* kt = kbase + (size_t)k0 * kv_row_stride;  // uniform
+    const T* vt = vbase + (size_t)k0 * kv_row_stride;
+    const uint32_t kl = ring_base + stage * G::STAGE_BYTES + wave_u * G::UPT * 1024;
+    const uint32_t vl = kl + G::TILE_BYTES;
+    const bool whole = k0 + BN <= Ttot;
+#pragma unroll
+    for (int i = 0; i < G::UPT; ++i) {
+      const int back = whole ? 0 : max(k0 + unit_row[i] - (Ttot - 1), 0) * (int)kv_row_stride;
+      dma16(kt + unit_off[i] - back, kl + i * 1024);
+      dma16(vt + unit_off[i] - back, vl + i * 1024);
+    }
+  };
+
   // ---- prologue: per-row key interval [lo_i, hi_i] ------------------------
+  // cu_seqlens -> LDS with one cooperative load (one memory latency instead
+  // of log2(ndocs) dependent ones per row)
+  const bool cu_in_lds = ndocs + 1 <= kCuCache;
+  if (cu_in_lds)
+    for (int d = tid; d <= ndocs; d += G::NT) cu_s[d] = cu[d];
+  __syncthreads();
   int my_de = 0;
   if (tid < G::BM) {
     const int i = q0 + tid;
@@ -150,11 +248,12 @@ void prefill_fwd_kernel(
       int a = 0, bnd = ndocs + 1;  // upper_bound over cu: first d with cu[d] > i
       while (a < bnd) {
         const int mid = (a + bnd) >> 1;
-        if (cu[mid] > i) bnd = mid; else a = mid + 1;
+        const int c = cu_in_lds ? cu_s[mid] : cu[mid];
+        if (c > i) bnd = mid; else a = mid + 1;
       }
       const int doc = a - 1;
-      int ds = (doc >= 0 && doc < ndocs) ? cu[doc] : i;
-      int de = (doc >= 0 && doc < ndocs) ? cu[doc + 1] : i + 1;
+      int ds = (doc >= 0 && doc < ndocs) ? (cu_in_lds ? cu_s[doc] : cu[doc]) : i;
+      int de = (doc >= 0 && doc < ndocs) ? (cu_in_lds ? cu_s[doc + 1] : cu[doc + 1]) : i + 1;
       ds = min(max(ds, 0), i);  // clamp against malformed cu_seqlens
       de = max(min(de, Ttot), i + 1);
       lo = (W > 0) ? max(ds, i - W + 1) : ds;
@@ -215,6 +314,10 @@ void prefill_fwd_kernel(
     }
   }
   __syncthreads();
+  // Row q0 has the smallest lo of the tile (lo_i never decreases with i), so
+  // the first key tile is known now: start its loads before the reductions.
+  const int kt0 = (lo_s[0] / BN) * BN;
+  dma_tile(kt0, 0);
 
   // tile key range and the rectangle every row admits
   {
@@ -239,7 +342,7 @@ void prefill_fwd_kernel(
       red_s[3][wave] = himin;
     }
   }
-  __syncthreads();
+  lds_barrier();
   int kmin = red_s[0][0], kmax = red_s[1][0], lomax = red_s[2][0], himin = red_s[3][0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
@@ -248,7 +351,10 @@ void prefill_fwd_kernel(
     lomax = max(lomax, red_s[2][w]);
     himin = min(himin, red_s[3][w]);
   }
-  if (kmax < kmin) return;  // no valid row in this tile (uniform exit)
+  if (kmax < kmin) {  // no valid row (cannot happen: row q0 < Ttot); uniform exit
+    wait_vmcnt<0>();  // never leave with a load still writing this block's LDS
+    return;
+  }
 
   // this lane's rows: one per q-block.  Key j is allowed iff
   // (unsigned)(j - lo) <= (unsigned)(hi - lo); rows with an empty interval
@@ -264,25 +370,6 @@ void prefill_fwd_kernel(
     row_rng[mb] = hi >= lo ? (unsigned)(hi - lo) : 0u;
   }
 
-  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ---------
-  // bf16: fragment kk holds d = kk*32 + 8*grp + e (e < 8);
-  // fp32: lane group grp owns d = grp*D/4 + ..., 4 per fragment.
-  using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
-  QF qf[MB][G::QREG];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int i = row_i[mb];
-    const bool ok = i < Ttot;
-    const T* qrow = q + ((size_t)(ok ? i : 0) * hq + h) * D;
-#pragma unroll
-    for (int kk = 0; kk < G::QREG; ++kk) {
-      const int d0 = kF32 ? grp * (D / 4) + kk * 4 : kk * 32 + 8 * grp;
-      QF x = QF{};
-      if (ok) x = *reinterpret_cast<const QF*>(qrow + d0);
-      qf[mb][kk] = x;
-    }
-  }
-
   // ---- accumulators ----------------------------------------------------------
   floatx4 o_acc[MB][D / 16];
   float m_ref[MB], l_part[MB];
@@ -294,64 +381,44 @@ void prefill_fwd_kernel(
     for (int dt = 0; dt < D / 16; ++dt) o_acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const size_t kv_row_stride = (size_t)hkv * D;
-  const T* kbase = k + (size_t)kvh * D;
-  const T* vbase = v + (size_t)kvh * D;
   const float c_scale = qk_scale_log2;
   const float slack = kRescaleSlack / c_scale;  // in raw score units
 
-  // global -> registers for one tile, registers -> padded LDS.  Rows past
-  // the end are clamped to the last row (finite data, masked out later).
-  u32x4 kreg[G::UPT], vreg[G::UPT];
-  int unit_off[G::UPT], unit_row[G::UPT];
-#pragma unroll
-  for (int i = 0; i < G::UPT; ++i) {
-    const int u = tid + i * G::NT;
-    const int r = u / G::CPR, ch = u - r * G::CPR;
-    unit_row[i] = r;
-    unit_off[i] = r * (int)kv_row_stride + ch * TR::VEC;
-  }
-  auto load_tile = [&](int k0) {
-    const T* kt = kbase + (size_t)k0 * kv_row_stride;  // uniform
-    const T* vt = vbase + (size_t)k0 * kv_row_stride;
-    if (k0 + BN <= Ttot) {
-#pragma unroll
-      for (int i = 0; i < G::UPT; ++i) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(kt + unit_off[i]);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vt + unit_off[i]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < G::UPT; ++i) {
-        const int back = max(k0 + unit_row[i] - (Ttot - 1), 0) * (int)kv_row_stride;
-        kreg[i] = *reinterpret_cast<const u32x4*>(kt + unit_off[i] - back);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vt + unit_off[i] - back);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < G::UPT; ++i) {
-      const int u = tid + i * G::NT;
-      const int r = u / G::CPR, ch = u - r * G::CPR;
-      *reinterpret_cast<u32x4*>(&Ks[buf][r * G::KS + ch * TR::VEC]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&Vs[buf][r * G::VS + ch * TR::VEC]) = vreg[i];
-    }
-  };
-
-  const int kt0 = (kmin / BN) * BN;
   const int ntile_k = (kmax - kt0) / BN + 1;
-  load_tile(kt0);
-  store_tile(0);
-  __syncthreads();
+#pragma unroll
+  for (int st = 1; st < G::STAGES - 1; ++st)
+    if (st < ntile_k) dma_tile(kt0 + st * BN, st);
+  // Q must be in registers before the loop: the compiler does not see the
+  // asm loads, and at Q's first use inside the loop it would otherwise wait
+  // for every load in flight.  Waiting here also covers the tiles just
+  // issued, which the first iteration needs anyway.
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int kk = 0; kk < G::QREG; ++kk) asm volatile("" : : "v"(qf[mb][kk]));
 
   for (int it = 0; it < ntile_k; ++it) {
     const int k0 = kt0 + it * BN;
-    const int buf = it & 1;
-    const bool more = it + 1 < ntile_k;
-    if (more) load_tile(k0 + BN);  // in flight during the compute below
-    const T* Kb = Ks[buf];
-    const T* Vb = Vs[buf];
+    const int stage = it % G::STAGES;
+    // tiles issued after tile `it`: min(it + STAGES - 2, ntile_k - 1) - it
+    const int pending = min(G::STAGES - 2, ntile_k - 1 - it);
+    if (pending <= 0) wait_vmcnt<0>();
+    else if (pending == 1) wait_vmcnt<2 * G::UPT>();
+    else if (pending == 2) wait_vmcnt<(G::STAGES >= 4 ? 4 : 2) * G::UPT>();
+    else wait_vmcnt<(G::STAGES >= 4 ? 6 : 2) * G::UPT>();
+    // every wave's loads of tile `it` have landed, and every wave is done
+    // with the stage that the next load below overwrites.  The empty asm
+    // statements keep the compiler from moving LDS accesses across the
+    // barrier (s_barrier alone does not order memory for the compiler, and
+    // __syncthreads() would also wait for the loads still in flight).
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (it + G::STAGES - 1 < ntile_k)
+      dma_tile(k0 + (G::STAGES - 1) * BN, (it + G::STAGES - 1) % G::STAGES);
+    const T* Kb = reinterpret_cast<const T*>(&ring[stage][0]);
+    const T* Vb = reinterpret_cast<const T*>(&ring[stage][G::TILE_BYTES]);
+    __builtin_amdgcn_s_setprio(1);  // favour MFMA issue over the other wave's VALU
 
     // ---- S^T = K Q^T for this wave's rows ---------------------------------
     floatx4 s[MB][BN / 16];
@@ -365,14 +432,16 @@ void prefill_fwd_kernel(
       for (int kb = 0; kb < BN / 16; ++kb) {
         const int r = kb * 16 + c16;
         if constexpr (kF32) {
-          const floatx4 a = *reinterpret_cast<const floatx4*>(&Kb[r * G::KS + grp * (D / 4) + kk * 4]);
+          const int ch = grp * (D / 16) + kk;  // d = grp*D/4 + kk*4 .. +4
+          const floatx4 a = *reinterpret_cast<const floatx4*>(&Kb[(r * G::CPR + (ch ^ chunk_swz(r))) * 4]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int st = 0; st < 4; ++st)
               s[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], qf[mb][kk][st], s[mb][kb], 0, 0, 0);
         } else {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kb[r * G::KS + kk * 32 + 8 * grp]);
+          const int ch = kk * 4 + grp;  // d = kk*32 + 8*grp .. +8
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kb[(r * G::CPR + (ch ^ chunk_swz(r))) * 8]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             s[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[mb][kk], s[mb][kb], 0, 0, 0);
@@ -380,6 +449,7 @@ void prefill_fwd_kernel(
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- mask, online softmax (raw scores; exp2 argument s*c - m*c) ---------
     const bool full = (k0 >= lomax) && (k0 + BN - 1 <= himin);
     bool any_move = false;
@@ -441,7 +511,7 @@ void prefill_fwd_kernel(
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
             const int r = kb * 16 + 4 * grp + st;
-            const float a = Vb[r * G::VS + d];
+            const float a = Vb[(r * G::CPR + ((d >> 2) ^ chunk_swz(r))) * 4 + (d & 3)];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
               o_acc[mb][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[mb][kb][st], o_acc[mb][dt], 0, 0, 0);
@@ -469,8 +539,9 @@ void prefill_fwd_kernel(
           // lane (grp, 4*tr_r + tr_m) addresses row r, elements dt*16 + 4*tr_m .. +4;
           // the transpose read hands lane c16 the column dt*16 + c16 of rows
           // 32ks + 4grp .. +3 (and +16 .. +19 for the second read)
-          const __bf16* p0 = &Vb[r0 * G::VS + dt * 16 + 4 * tr_m];
-          const __bf16* p1 = &Vb[r1 * G::VS + dt * 16 + 4 * tr_m];
+          const int ch = 2 * dt + (tr_m >> 1), off = (tr_m & 1) * 4;
+          const __bf16* p0 = &Vb[(r0 * G::CPR + (ch ^ chunk_swz(r0))) * 8 + off];
+          const __bf16* p1 = &Vb[(r1 * G::CPR + (ch ^ chunk_swz(r1))) * 8 + off];
           const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) short4v*)(p0));
           const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -484,8 +555,6 @@ void prefill_fwd_kernel(
       }
     }
 
-    if (more) store_tile(buf ^ 1);  // the other buffer: free since the last barrier
-    __syncthreads();
   }
 
   // ---- epilogue: normalise and store ------------------------------------------
