@@ -244,7 +244,7 @@ def cpu_baseline(budget_s=15.0):
     keys = np.minimum(np.arange(c.T) - start + 1, c.window)
     done, flops, t0 = 0, 0, time.perf_counter()
     chunk = 256
-    while time.perf_counter() - t0 < budget_s and done < 8 * c.T:
+    while time.perf_counter() - t0 < budget_s and done < 32 * c.T:
         rows = order[np.arange(done, done + chunk) % c.T]
         orc.prefill(q, k, v, cu, None, c.window, c.mode, rows=rows, nthreads=threads)
         flops += int(keys[rows].sum()) * 4 * c.d * c.hq

@@ -111,8 +111,8 @@ SWA_API int swa_prefill(const void* q, const void* k, const void* v,
                         int32_t dtype, float scale, void* stream);
 
 /*
- * Bytes of workspace swa_decode needs for these sizes (fp32 split-K
- * partials).  Depends only on the sizes, never on positions.
+ * Bytes of workspace swa_decode needs for these sizes: split counters plus
+ * fp32 split-K partials.  Depends only on the sizes, never on positions.
  */
 SWA_API size_t swa_decode_workspace_bytes(int32_t batch, int32_t hq,
                                           int32_t hkv, int32_t d,
@@ -134,8 +134,12 @@ SWA_API size_t swa_decode_workspace_bytes(int32_t batch, int32_t hq,
  *   q [batch, hq, d]; k_ring, v_ring [batch, hkv, ring_rows, d];
  *   ring_meta int32 [batch, 4] (device); out [batch, hq, d].
  *   window >= 1; ring_rows > window.  scale <= 0 means 1 / sqrt(d).
- *   workspace: device buffer of swa_decode_workspace_bytes(...) bytes,
- *   overwritten; it must not be shared with a concurrent call.
+ *   workspace: device buffer of at least swa_decode_workspace_bytes(...)
+ *   bytes, zero-filled before its first use.  Its leading words are split
+ *   counters that every call returns to zero (in stream order), so later
+ *   calls with the SAME sizes can reuse it as is; zero it again before a
+ *   call with different sizes (the counter region moves with the sizes).
+ *   Calls that overlap (different streams) must not share a workspace.
  * The launch grid depends only on (batch, hq, hkv, d, ring_rows).
  */
 SWA_API int swa_decode(const void* q, const void* k_ring, const void* v_ring,

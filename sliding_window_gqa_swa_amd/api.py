@@ -70,10 +70,11 @@ def decode_workspace_bytes(batch, hq, hkv, d, ring_rows) -> int:
 
 
 def decode_workspace(q, k_ring) -> torch.Tensor:
-    """A workspace tensor of the size swa_decode needs for these shapes."""
+    """A zero-filled workspace of the size swa_decode needs for these shapes
+    (zero once; swa_decode leaves its counters at zero after every call)."""
     B, hq, d = q.shape
     nbytes = decode_workspace_bytes(B, hq, k_ring.shape[1], d, k_ring.shape[2])
-    return torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    return torch.zeros(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
 
 
 def decode(q, k_ring, v_ring, ring_meta, window, out=None, workspace=None, scale=0.0):

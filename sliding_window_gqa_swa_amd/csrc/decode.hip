@@ -21,8 +21,9 @@
 //   query dot products with a lane-group butterfly and folds the rows into a
 //   running (max, sum, weighted V) state, online-softmax style.  The states
 //   of the row groups and waves are merged in a fixed order; partials
-//   (m, l, o) go to the workspace and a second kernel combines the splits in
-//   a fixed order (deterministic).
+//   (m, l, o) go to the workspace; the last split block of each sequence and
+//   head block (a device-scope counter in the workspace) combines the splits
+//   in a fixed order (deterministic), so one launch does the whole decode.
 #include <type_traits>
 
 #include "swa_common.h"
@@ -34,7 +35,8 @@ namespace {
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kMaxRowsPerSplit = 512;  // bounds the work of one block
-constexpr int kTargetBlocks = 2048;  // 8 resident blocks per CU on 256 CUs
+constexpr int kTargetBlocks = 256;  // about one block per CU before the row cap adds more
+constexpr int kMaxSplits = 256;      // (m, l) of every split fit the combine's LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
 // 16-byte chunk of a row as fp32.
@@ -68,6 +70,14 @@ __device__ __forceinline__ void unpack_chunk<float>(const u32x4 w, float* f) {
   f[3] = __uint_as_float(w[3]);
 }
 
+// Device-coherent (agent-scope, relaxed) 4-byte store / load.
+__device__ __forceinline__ void st_agent(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int D, typename T>
 struct DecGeom {
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16 bytes
@@ -84,8 +94,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ k_ring,
     const T* __restrict__ v_ring, const int32_t* __restrict__ meta, int W,
     int R, int hq, int hkv, int head_blocks, int rows_per_split,
-    float qk_scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    int splits) {
+    float qk_scale_log2, float* ws_o, float* ws_ml, int splits, uint32_t* counters,
+    T* __restrict__ out) {
   using G = DecGeom<D, T>;
   __shared__ float red_o[kDecWaves][GB][D];
   __shared__ float red_m[kDecWaves][GB], red_l[kDecWaves][GB];
@@ -260,40 +270,59 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       x += red_o[w][j][dd] * e;
       l += red_l[w][j] * e;
     }
-    ws_o[(((size_t)b * hq + h0 + j) * splits + s) * D + dd] = x;
+    // agent-scope stores write through to the device coherence point, so
+    // the combining block (possibly on another XCD) reads them back
+    st_agent(&ws_o[(((size_t)b * hq + h0 + j) * splits + s) * D + dd], x);
     if (dd == 0) {
       float* ml = ws_ml + (((size_t)b * hq + h0 + j) * splits + s) * 2;
-      ml[0] = M;
-      ml[1] = l;
+      st_agent(&ml[0], M);
+      st_agent(&ml[1], l);
     }
   }
-}
 
-// Fixed-order combine of the split partials of one (sequence, query head).
-template <typename T>
-__global__ __launch_bounds__(256) void decode_combine_kernel(
-    const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
-    T* __restrict__ out, int D, int splits) {
-  const size_t bh = blockIdx.x;
-  const float* ml = ws_ml + bh * splits * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
-  const float Mref = M == -INFINITY ? 0.f : M;
-  float L = 0.f;
-  for (int s = 0; s < splits; ++s) L += __builtin_amdgcn_exp2f(ml[2 * s] - Mref) * ml[2 * s + 1];
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int dd = threadIdx.x; dd < D; dd += blockDim.x) {
-    float x = 0.f;
-    for (int s = 0; s < splits; ++s)
-      x += __builtin_amdgcn_exp2f(ml[2 * s] - Mref) * ws_o[(bh * splits + s) * D + dd];
-    x *= inv;
+  // The last split block of this (sequence, head block) combines all splits
+  // in a fixed order.  The barrier waits for this block's stores to
+  // complete before the counter moves; the combining block reads with
+  // agent-scope loads (no stale L2 lines).  No L2-wide fence is needed.  The
+  // counter goes back to zero for the next call.
+  __shared__ int is_last;
+  __syncthreads();
+  uint32_t* cnt = counters + (size_t)b * gridDim.y + blockIdx.y;
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (uint32_t)(splits - 1);
+  __syncthreads();
+  if (!is_last) return;
+  // (m, l) of every split -> LDS in one batch of independent loads
+  __shared__ float cm[GB][kMaxSplits], cl[GB][kMaxSplits];
+  for (int idx = threadIdx.x; idx < nh * splits; idx += kDecThreads) {
+    const int j = idx / splits, ss = idx - j * splits;
+    const float* ml = ws_ml + (((size_t)b * hq + h0 + j) * splits + ss) * 2;
+    cm[j][ss] = ld_agent(&ml[0]);
+    cl[j][ss] = ld_agent(&ml[1]);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nh * D; idx += kDecThreads) {
+    const int j = idx / D, dd = idx - j * D;
+    const size_t bh = (size_t)b * hq + h0 + j;
+    float M = -INFINITY;
+    for (int ss = 0; ss < splits; ++ss) M = fmaxf(M, cm[j][ss]);
+    const float Mref = M == -INFINITY ? 0.f : M;
+    float L = 0.f, x = 0.f;
+#pragma unroll 16
+    for (int ss = 0; ss < splits; ++ss) {
+      const float e = __builtin_amdgcn_exp2f(cm[j][ss] - Mref);
+      L += e * cl[j][ss];
+      x += e * ld_agent(&ws_o[(bh * splits + ss) * D + dd]);
+    }
+    x = L > 0.f ? x / L : 0.f;
     if constexpr (std::is_same<T, float>::value) {
       out[bh * D + dd] = x;
     } else {
-      const uint16_t h = (uint16_t)float_to_bf16_bits(x);
-      reinterpret_cast<uint16_t*>(out)[bh * D + dd] = h;
+      reinterpret_cast<uint16_t*>(out)[bh * D + dd] = (uint16_t)float_to_bf16_bits(x);
     }
   }
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, typename T, int GB>
@@ -301,17 +330,14 @@ int launch_decode_t(const void* q, const void* k_ring, const void* v_ring,
                     const int32_t* meta, int window, void* out, int batch,
                     int ring_rows, int hq, int hkv, float scale,
                     void* workspace, const DecodePlan& p, hipStream_t stream) {
-  float* ws_o = (float*)workspace;
-  float* ws_ml = ws_o + (size_t)batch * hq * p.splits * D;
+  uint32_t* counters = (uint32_t*)workspace;
+  float* ws_ml = (float*)((char*)workspace + p.counter_bytes);
+  float* ws_o = ws_ml + (size_t)batch * hq * p.splits * 2;
   dim3 grid(p.splits, hkv * p.head_blocks, batch);
   hipLaunchKernelGGL((decode_split_kernel<D, T, GB>), grid, dim3(kDecThreads), 0, stream,
                      (const T*)q, (const T*)k_ring, (const T*)v_ring, meta, window,
                      ring_rows, hq, hkv, p.head_blocks, p.rows_per_split,
-                     scale * kLog2e, ws_o, ws_ml, p.splits);
-  if (hipGetLastError() != hipSuccess) return SWA_ELAUNCH;
-  hipLaunchKernelGGL((decode_combine_kernel<T>), dim3(batch * hq), dim3(D < 256 ? D : 256),
-                     0, stream, (const float*)ws_o, (const float*)ws_ml, (T*)out, D,
-                     p.splits);
+                     scale * kLog2e, ws_o, ws_ml, p.splits, counters, (T*)out);
   return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
 }
 
@@ -333,17 +359,24 @@ DecodePlan plan_decode(int batch, int hq, int hkv, int d, int ring_rows) {
   p.head_blocks = (g + p.heads_per_block - 1) / p.heads_per_block;
   const long long units = (long long)batch * hkv * p.head_blocks;
   long long want = (kTargetBlocks + units - 1) / (units > 0 ? units : 1);
-  const long long max_splits = (ring_rows + 31) / 32;
+  long long max_splits = (ring_rows + 31) / 32;
+  if (max_splits > kMaxSplits) max_splits = kMaxSplits;
   const long long min_splits = (ring_rows + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit;
   if (want > max_splits) want = max_splits;
   if (want < min_splits) want = min_splits;
   if (want < 1) want = 1;
   int rps = (int)((ring_rows + want - 1) / want);
   rps = (rps + 31) / 32 * 32;
-  if (rps > kMaxRowsPerSplit) rps = kMaxRowsPerSplit;
+  // at most kMaxSplits splits: rows per split >= ring_rows / kMaxSplits
+  const int rps_min = (int)(((ring_rows + kMaxSplits - 1) / kMaxSplits + 31) / 32 * 32);
+  if (rps < rps_min) rps = rps_min;
   p.rows_per_split = rps;
   p.splits = (ring_rows + rps - 1) / rps;
-  p.workspace_bytes = (size_t)batch * hq * p.splits * ((size_t)d + 2) * sizeof(float);
+  // [counters: one uint32 per (sequence, kv head, head block), 256-byte
+  //  padded][(m, l) per (sequence, query head, split)][o per ... and d]
+  p.counter_bytes = ((size_t)batch * hkv * p.head_blocks * sizeof(uint32_t) + 255) / 256 * 256;
+  p.workspace_bytes =
+      p.counter_bytes + (size_t)batch * hq * p.splits * ((size_t)d + 2) * sizeof(float);
   return p;
 }
 
