@@ -62,6 +62,10 @@ constexpr float kPrefillLog2e = 1.4426950408889634f;
 constexpr int kCuCache = 1024;
 // exp2 arguments stay <= this between reference-max moves (p <= 2^8)
 constexpr float kRescaleSlack = 8.0f;
+// Work order: cost buckets of the counting sort, and the largest slice of
+// work items one XCD may hold for the sort (one byte each, in the LDS ring)
+constexpr int kPlanBuckets = 256;
+constexpr int kPlanMaxItems = 65536;
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
@@ -141,6 +145,104 @@ struct PfGeom {
   static_assert(2 * UPT * (STAGES - 1) <= 63, "loads in flight exceed the vmcnt range");
 };
 
+// First d with cu[d] > i (upper bound), cu cached in LDS.
+__device__ __forceinline__ int cu_upper(const int* cu_s, int ndocs, int i) {
+  int a = 0, bnd = ndocs + 1;
+  while (a < bnd) {
+    const int mid = (a + bnd) >> 1;
+    if (cu_s[mid] > i) bnd = mid; else a = mid + 1;
+  }
+  return a;
+}
+
+// Cost bucket of query tile `tile`: the number of key tiles a causal /
+// windowed tile visits (the image-block extension is left out: the value
+// only orders the work).
+template <int BM, int BN>
+__device__ __forceinline__ int tile_cost_bucket(const int* cu_s, int ndocs, int tile, int Ttot,
+                                                int W) {
+  const int r0 = tile * BM;
+  const int r1 = min(r0 + BM, Ttot) - 1;
+  const int doc = cu_upper(cu_s, ndocs, r0) - 1;
+  int ds = (doc >= 0 && doc < ndocs) ? cu_s[doc] : r0;
+  ds = min(max(ds, 0), r0);
+  const int lo = W > 0 ? max(ds, r0 - W + 1) : ds;
+  return min(r1 / BN - lo / BN + 1, kPlanBuckets - 1);
+}
+
+// Longest-first order of one XCD's slice of work [w0, w0 + P): returns the
+// offset in the slice of the item at sorted position `pos` (descending cost
+// bucket, ties by ascending offset).  Blocks of one XCD are dispatched in
+// ascending `pos` as CUs free up, so this is list scheduling with the
+// longest items first, which keeps the tail of the grid short when item
+// costs vary (causal tiles of many documents).  A counting sort: bucket of
+// every item (kept in `bk`, P bytes), histogram, the bucket holding `pos`,
+// then the rank inside that bucket by a block-wide scan.  Deterministic.
+// Called by all NT threads; ends with a barrier.
+template <int NT, int BM, int BN>
+__device__ int lpt_slot(const int* cu_s, int ndocs, int Ttot, int W, int ntiles, int w0, int P,
+                        int pos, unsigned char* bk, int* hist_s, int* wsum_s, int* sel_s) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NWV = NT / 64;
+  for (int i = tid; i < P; i += NT) {
+    const int w = w0 + i;
+    const int c = tile_cost_bucket<BM, BN>(cu_s, ndocs, ntiles - 1 - (w % ntiles), Ttot, W);
+    bk[i] = (unsigned char)c;
+    atomicAdd(&hist_s[c], 1);
+  }
+  __syncthreads();
+  if (wave == 0) {  // bucket holding position pos, scanning buckets high to low
+    static_assert(kPlanBuckets == 4 * 64, "four buckets per lane");
+    int n[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      n[j] = hist_s[kPlanBuckets - 1 - 4 * lane - j];
+      sum += n[j];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    int start = incl - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (pos >= start && pos < start + n[j]) {
+        sel_s[0] = kPlanBuckets - 1 - 4 * lane - j;
+        sel_s[1] = pos - start;
+      }
+      start += n[j];
+    }
+  }
+  __syncthreads();
+  const int tb = sel_s[0], tr = sel_s[1];
+  const int chunk = (P + NT - 1) / NT;
+  const int i0 = min(tid * chunk, P), i1 = min(i0 + chunk, P);
+  int cnt = 0;
+  for (int i = i0; i < i1; ++i) cnt += bk[i] == tb;
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum_s[wave] = incl;
+  __syncthreads();
+  int before = incl - cnt;
+  for (int w = 0; w < NWV; ++w) before += w < wave ? wsum_s[w] : 0;
+  if (tr >= before && tr < before + cnt) {
+    int r = tr - before;
+    for (int i = i0; i < i1; ++i)
+      if (bk[i] == tb) {
+        if (r == 0) sel_s[2] = i;
+        --r;
+      }
+  }
+  __syncthreads();
+  return min(max(sel_s[2], 0), P - 1);
+}
+
 template <int D, typename T, int MB, int BN, int NW, int GH>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 256 && !std::is_same<T, float>::value) ? 2 : 1)
 void prefill_fwd_kernel(
@@ -158,6 +260,8 @@ void prefill_fwd_kernel(
   __shared__ unsigned long long runmask_s[(G::BM + 63) / 64];
   __shared__ int ext_end_s, de_last_s;
   __shared__ int cu_s[kCuCache];
+  __shared__ int hist_s[kPlanBuckets];
+  __shared__ int plan_s[3 + NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -166,10 +270,27 @@ void prefill_fwd_kernel(
   const int grp = lane >> 4;  // MFMA 4-lane group
 
   // XCD-aware numbering: blocks are dispatched round-robin over 8 XCDs, so
-  // block b runs on XCD b % 8; give that XCD a contiguous slice of work.
+  // block b runs on XCD b % 8; give that XCD a contiguous slice of work
+  // (the tiles of the same heads, so their K/V rows meet in one L2), taken
+  // longest first.
   const int b = (int)blockIdx.x;
-  const int work = (b & 7) * work_per_xcd + (b >> 3);
-  if (work >= nwork) return;  // uniform per block
+  const int w0 = (b & 7) * work_per_xcd;
+  const int P = min(work_per_xcd, nwork - w0);
+  const int pos = b >> 3;
+  if (pos >= P) return;  // uniform per block
+  // cu_seqlens -> LDS with one cooperative load (one memory latency instead
+  // of log2(ndocs) dependent ones per row)
+  const bool cu_in_lds = ndocs + 1 <= kCuCache;
+  if (cu_in_lds)
+    for (int d = tid; d <= ndocs; d += G::NT) cu_s[d] = cu[d];
+  const bool plan = cu_in_lds && P > 1 && P <= kPlanMaxItems;
+  if (plan)
+    for (int c = tid; c < kPlanBuckets; c += G::NT) hist_s[c] = 0;
+  __syncthreads();
+  const int work = w0 + (plan ? lpt_slot<G::NT, G::BM, BN>(cu_s, ndocs, Ttot, W, ntiles, w0, P,
+                                                           pos, &ring[0][0], hist_s, plan_s + 3,
+                                                           plan_s)
+                              : pos);
   const int hg_index = work / ntiles;
   const int tile = ntiles - 1 - (work - hg_index * ntiles);  // heavy tiles first
   const int q0 = tile * G::BM;
@@ -182,7 +303,8 @@ void prefill_fwd_kernel(
   const int h = hbase + jh;
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept in registers.  Issued
-  // first so that their latency overlaps the row-interval prologue.
+  // before the row-interval prologue so that their latency overlaps it and
+  // the first key tile's loads.
   // bf16: fragment kk holds d = kk*32 + 8*grp + e (e < 8);
   // fp32: lane group grp owns d = grp*D/4 + ..., 4 per fragment.
   using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
@@ -234,12 +356,6 @@ void prefill_fwd_kernel(
   };
 
   // ---- prologue: per-row key interval [lo_i, hi_i] ------------------------
-  // cu_seqlens -> LDS with one cooperative load (one memory latency instead
-  // of log2(ndocs) dependent ones per row)
-  const bool cu_in_lds = ndocs + 1 <= kCuCache;
-  if (cu_in_lds)
-    for (int d = tid; d <= ndocs; d += G::NT) cu_s[d] = cu[d];
-  __syncthreads();
   int my_de = 0;
   if (tid < G::BM) {
     const int i = q0 + tid;

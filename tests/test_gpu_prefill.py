@@ -139,6 +139,30 @@ def test_prefill_edge_shapes():
     api.prefill(z, zk, zk, torch.zeros(1, dtype=torch.int32, device="cuda"))
 
 
+@pytest.mark.parametrize("ndocs", [300, 1500])
+@pytest.mark.parametrize("mode", [CAUSAL, BLOCKWISE])
+def test_prefill_many_documents(ndocs, mode):
+    """Many short documents of random length (1..24 tokens, some empty):
+    tiles that span several documents and work items of many different
+    costs.  1500 documents exceed the length table kept in LDS, which takes
+    the other lookup path."""
+    require_gpu()
+    rng = si.rng_for(7000 + ndocs + mode)
+    lens = rng.integers(0, 25, size=ndocs)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    d, hkv, g = 64, 2, 2
+    q = si.normal(rng, (T, hkv * g, d), "bf16")
+    k = si.normal(rng, (T, hkv, d), "bf16")
+    v = si.normal(rng, (T, hkv, d), "bf16")
+    ids = _ids_for(T, cu, 7100 + ndocs) if mode == BLOCKWISE else None
+    for W in (0, 5):
+        log("prefill many docs ndocs=%d T=%d mode=%d W=%d" % (ndocs, T, mode, W))
+        got = _run(q, k, v, cu, ids, W, mode, "bf16")
+        want = orc.prefill(q, k, v, cu, ids, W, mode)
+        assert_close(got, want, "bf16", "many docs %d W=%d" % (ndocs, W))
+
+
 def test_prefill_deterministic():
     require_gpu()
     c = si.prefill_vlm_4096_d256()
