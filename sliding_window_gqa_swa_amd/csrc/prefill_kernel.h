@@ -34,10 +34,9 @@
 //   registers are spent on staging.  The loads are issued from inline
 //   assembly, because the compiler would otherwise order every later LDS
 //   read behind all of them; completion is tracked with explicit vmcnt
-//   waits and a plain s_barrier (one per tile).  LDS rows are unpadded; the
-//   16-byte chunk c of row r sits at c ^ f(r) with
-//   f(r) = ((r & 3) << 1) | ((r >> 2) & 1), which keeps the 8-row K
-//   fragment reads and the 4-row transposed V reads on distinct banks.
+//   waits and a plain s_barrier (one per tile).  LDS rows are unpadded and
+//   their 16-byte chunks permuted per row (chunk_pos below) so that the K
+//   fragment reads and the transposed V reads are free of bank conflicts.
 //   bf16: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with K fragments from LDS
 //   and Q fragments held in registers; the S^T accumulator holds one query
 //   row per lane, so the softmax row statistics stay in the lane (plus a
@@ -70,8 +69,24 @@ constexpr int kPlanMaxItems = 65536;
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 
-// Chunk swizzle of LDS tiles (16-byte chunk c of row r is stored at c ^ f(r)).
-__device__ __forceinline__ int chunk_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// LDS tile layout: 16-byte chunk ch of row r is stored at chunk position
+// chunk_pos(r, ch) of that row, a bijection on each row's CPR chunks.  With
+// 16 or more chunks per row the chunks of each aligned block of 16 rotate by
+// 2 per row, which gives the bank pattern of a 32-byte row padding (the
+// 16-row K fragment reads and the transposed V reads are conflict-free)
+// while every row stays 16-byte contiguous for the DMA.  Rows of 8 chunks
+// use an XOR pattern instead.
+template <int CPR>
+__device__ __forceinline__ int chunk_pos(int r, int ch) {
+  if constexpr (CPR >= 16) return (ch & ~15) | ((ch + 2 * r) & 15);
+  else return ch ^ (((r & 3) << 1) | ((r >> 2) & 1));
+}
+// inverse: the chunk stored at position pc of row r
+template <int CPR>
+__device__ __forceinline__ int chunk_src(int r, int pc) {
+  if constexpr (CPR >= 16) return (pc & ~15) | ((pc - 2 * r) & 15);
+  else return pc ^ (((r & 3) << 1) | ((r >> 2) & 1));
+}
 
 // One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from g land at
 // LDS byte address lds_wave_base + 16 * l (lds_wave_base is wave-uniform).
@@ -87,6 +102,28 @@ template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n >= 0 && n <= 63, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt vmcnt(k * UPT) for a uniform run-time k; k > K waits for K * UPT
+// (a stronger wait, still correct).
+template <int UPT, int K>
+__device__ __forceinline__ void wait_vmcnt_units(int k) {
+  if constexpr (K == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (k >= K) wait_vmcnt<K * UPT>();
+    else wait_vmcnt_units<UPT, K - 1>(k);
+  }
+}
+
+// One 16-byte-per-lane direct-to-LDS buffer load: lane l's 16 bytes at
+// byte offset voff of the buffer land at LDS byte lds_wave_base + 16 * l; a
+// lane whose offset is outside the buffer writes zeros and reads nothing.
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, int voff, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_wave_base), "v"(voff), "s"(rsrc)
+               : "memory");
 }
 
 // Work-group barrier that orders LDS but leaves global/DMA loads in flight
@@ -118,7 +155,7 @@ struct PfTraits<float> {
 };
 
 // Workgroup geometry.
-template <int D, typename T, int MB, int BN, int NW, int GH>
+template <int D, typename T, int MB, int BN, int NW, int GH, bool PL = false>
 struct PfGeom {
   using TR = PfTraits<T>;
   static constexpr int NT = NW * kWave;
@@ -129,10 +166,11 @@ struct PfGeom {
   static constexpr int TILE = BN * D;       // elements of one K or V tile (unpadded)
   static constexpr int TILE_BYTES = TILE * (int)sizeof(T);
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K then V
-  // LDS ring depth: as many stages as fit 64 KB (2 work-groups per CU), at
-  // least 2 and at most 4
-  static constexpr int STAGES = (65536 / STAGE_BYTES) < 2 ? 2
-                                : ((65536 / STAGE_BYTES) > 4 ? 4 : 65536 / STAGE_BYTES);
+  // LDS ring depth: as many stages as fit the ring budget (64 KB with two
+  // work-groups per CU, 128 KB with one), at least 2 and at most 4
+  static constexpr int RING_BUDGET = (NW == 8) ? 131072 : 65536;
+  static constexpr int STAGES = (RING_BUDGET / STAGE_BYTES) < 2 ? 2
+                                : ((RING_BUDGET / STAGE_BYTES) > 4 ? 4 : RING_BUDGET / STAGE_BYTES);
   static constexpr int UNITS = BN * CPR;    // 16-byte chunks per tile
   static constexpr int UPT = UNITS / NT;    // chunks per thread per tile
   static constexpr int QREG = D / TR::KW;   // Q fragments per q-block
@@ -243,14 +281,14 @@ __device__ int lpt_slot(const int* cu_s, int ndocs, int Ttot, int W, int ntiles,
   return min(max(sel_s[2], 0), P - 1);
 }
 
-template <int D, typename T, int MB, int BN, int NW, int GH>
+template <int D, typename T, int MB, int BN, int NW, int GH, bool PL>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 256 && !std::is_same<T, float>::value) ? 2 : 1)
 void prefill_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ cu, int ndocs, const int32_t* __restrict__ ids,
     int W, int mode, T* __restrict__ out, int Ttot, int hq, int hkv,
     float qk_scale_log2, int ntiles, int nwork, int work_per_xcd) {
-  using G = PfGeom<D, T, MB, BN, NW, GH>;
+  using G = PfGeom<D, T, MB, BN, NW, GH, PL>;
   using TR = typename G::TR;
   constexpr bool kF32 = std::is_same<T, float>::value;
 
@@ -328,7 +366,8 @@ void prefill_fwd_kernel(
   const T* vbase = v + (size_t)kvh * D;
   // Direct-to-LDS tile loads.  Wave w issues UPT loads per tensor per tile;
   // load i covers LDS slots [(w*UPT + i)*64, +64) of 16 bytes, slot s being
-  // row s / CPR, stored chunk s % CPR, i.e. source chunk (s % CPR) ^ f(row).
+  // row s / CPR, stored chunk position s % CPR, i.e. source chunk
+  // chunk_src(row, s % CPR).
   // Rows past the end are clamped to the last row (finite data, masked).
   int unit_off[G::UPT], unit_row[G::UPT];
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -337,7 +376,7 @@ void prefill_fwd_kernel(
     const int slot = (wave_u * G::UPT + i) * 64 + lane;
     const int r = slot / G::CPR, pc = slot - r * G::CPR;
     unit_row[i] = r;
-    unit_off[i] = r * (int)kv_row_stride + (pc ^ chunk_swz(r)) * TR::VEC;
+    unit_off[i] = r * (int)kv_row_stride + chunk_src<G::CPR>(r, pc) * TR::VEC;
   }
   const uint32_t ring_base =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(&ring[0][0]);
@@ -354,6 +393,13 @@ void prefill_fwd_kernel(
       dma16(vt + unit_off[i] - back, vl + i * 1024);
     }
   };
+
+  if constexpr (PL) {
+    // the pipelined loop's first iteration reads the last V stage with zero
+    // weights before anything is loaded there: give it finite contents
+    u32x4* vz = reinterpret_cast<u32x4*>(&ring[0][0] + (2 * G::STAGES - 1) * G::TILE_BYTES);
+    for (int i = tid; i < G::TILE_BYTES / 16; i += G::NT) vz[i] = u32x4{0u, 0u, 0u, 0u};
+  }
 
   // ---- prologue: per-row key interval [lo_i, hi_i] ------------------------
   int my_de = 0;
@@ -432,8 +478,26 @@ void prefill_fwd_kernel(
   __syncthreads();
   // Row q0 has the smallest lo of the tile (lo_i never decreases with i), so
   // the first key tile is known now: start its loads before the reductions.
-  const int kt0 = (lo_s[0] / BN) * BN;
-  dma_tile(kt0, 0);
+  const int kt0 = __builtin_amdgcn_readfirstlane((lo_s[0] / BN) * BN);
+  // pipelined layout: K ring of STAGES tiles, then V ring of STAGES tiles
+  const uint32_t kring = ring_base, vring = ring_base + G::STAGES * G::TILE_BYTES;
+  int voff[G::UPT];
+#pragma unroll
+  for (int i = 0; i < G::UPT; ++i) voff[i] = unit_off[i] * (int)sizeof(T);
+  // one K or V tile (keys k0 .. k0+BN-1 of this kv head) into an LDS stage;
+  // rows at or past Ttot fall outside the buffer and arrive as zeros
+  auto dma_pl = [&](const T* tb, int k0, uint32_t lds_stage) {
+    const T* p0 = tb + (size_t)k0 * kv_row_stride;
+    const long long rem = (long long)(Ttot - k0) * (long long)kv_row_stride * (long long)sizeof(T);
+    const i32x4 rsrc = make_buffer_rsrc(p0, rem > 0xffffffffLL ? 0xffffffffu : (uint32_t)rem);
+    const uint32_t lw = lds_stage + wave_u * G::UPT * 1024;
+#pragma unroll
+    for (int i = 0; i < G::UPT; ++i) dma16_buf(rsrc, voff[i], lw + i * 1024);
+  };
+  if constexpr (PL)
+    dma_pl(kbase, kt0, kring);
+  else
+    dma_tile(kt0, 0);
 
   // tile key range and the rectangle every row admits
   {
@@ -484,6 +548,284 @@ void prefill_fwd_kernel(
     const int lo = lo_s[t], hi = hi_s[t];
     row_lo[mb] = hi >= lo ? lo : 0x3fffffff;
     row_rng[mb] = hi >= lo ? (unsigned)(hi - lo) : 0u;
+  }
+
+  if constexpr (PL) {
+    // ---- software-pipelined loop (bf16) ----------------------------------------
+    // Iteration t issues the S^T MFMAs of key tile t+1 and the O^T MFMAs of
+    // tile t-1 next to the softmax VALU work of tile t, all independent, so
+    // matrix-core and vector instructions of one wave overlap.  K tiles live
+    // in a ring of STAGES stages, V tiles in a second ring two tiles behind:
+    // load group m = {K_m, V_(m-2)} is issued STAGES-1 iterations before it
+    // is needed.  Row sums come from one extra MFMA per 32 keys with a ones
+    // A operand (the sum of the bf16 weights that also weight V).
+    static_assert(!kF32, "the pipelined loop is bf16 only");
+    constexpr int S = G::STAGES;
+    constexpr int TB = G::TILE_BYTES;
+    constexpr int ROWB = D * 2;     // bytes of one K/V row in LDS
+    constexpr int NKB = BN / 16;    // 16-key blocks per tile
+    constexpr int NKS = BN / 32;    // 32-key P^T fragments per tile
+    constexpr int NDT = D / 16;     // 16-wide head-dim blocks
+    const int n = (kmax - kt0) / BN + 1;  // key tiles of the work-group
+
+    // this wave's rows: key range, and the rectangle every one of them admits
+    int wlo = 0x7fffffff, whi = -1, wlomax = -1, whimin = 0x7fffffff;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (row_i[mb] < Ttot && row_lo[mb] != 0x3fffffff) {
+        const int lo = row_lo[mb], hi = lo + (int)row_rng[mb];
+        wlo = min(wlo, lo);
+        whi = max(whi, hi);
+        wlomax = max(wlomax, lo);
+        whimin = min(whimin, hi);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      wlo = min(wlo, __shfl_xor(wlo, o, 64));
+      whi = max(whi, __shfl_xor(whi, o, 64));
+      wlomax = max(wlomax, __shfl_xor(wlomax, o, 64));
+      whimin = min(whimin, __shfl_xor(whimin, o, 64));
+    }
+    // active key tiles of this wave: [ta, tb] (empty for a wave past the end)
+    const int ta = __builtin_amdgcn_readfirstlane(whi >= wlo ? (wlo - kt0) / BN : n);
+    const int tb = __builtin_amdgcn_readfirstlane(whi >= wlo ? min((whi - kt0) / BN, n - 1) : -1);
+    wlomax = __builtin_amdgcn_readfirstlane(wlomax);
+    whimin = __builtin_amdgcn_readfirstlane(whimin);
+
+    // loads of group m: UPT for K_m (m < n) and UPT for V_(m-2) (2 <= m <= n+1)
+    auto loads_in = [&](int a, int b2) {  // groups a .. b2
+      const int kc = max(0, min(b2, n - 1) - a + 1);
+      const int vc = max(0, min(b2, n + 1) - max(a, 2) + 1);
+      return kc + vc;
+    };
+#pragma unroll
+    for (int m = 1; m < S; ++m) {
+      if (m < n) dma_pl(kbase, kt0 + m * BN, kring + m * TB);
+      if (m >= 2 && m - 2 < n) dma_pl(vbase, kt0 + (m - 2) * BN, vring + (m - 2) * TB);
+    }
+
+    // fixed per-lane LDS offsets: chunk_pos(r + 16 j, ch + 16 m) =
+    // chunk_pos(r, ch) + 16 m, so the K fragment of head-dim step kk reads
+    // kofs[kk % 4] + (kk / 4) * 256 bytes + kb * 16 rows, and the V^T
+    // fragment dt reads vofs[dt % 8] + (dt / 8) * 256 bytes + ks * 32 rows
+    // (+16 rows for its second half)
+    typedef __attribute__((address_space(3))) const unsigned char lds_u8;
+    lds_u8* lds0 = (lds_u8*)(&ring[0][0]);
+    constexpr int NKO = G::QREG < 4 ? G::QREG : 4;
+    constexpr int NVO = NDT < 8 ? NDT : 8;
+    static_assert(G::CPR >= 16 || (G::QREG <= 2 && NDT <= 4), "offset blocks of 16 chunks");
+    int kofs[NKO], vofs[NVO];
+#pragma unroll
+    for (int kk = 0; kk < NKO; ++kk)
+      kofs[kk] = c16 * ROWB + chunk_pos<G::CPR>(c16, 4 * kk + grp) * 16;
+    const int tr_r = (lane & 15) >> 2, tr_m = lane & 3;
+    const int vrow = 4 * grp + tr_r;
+#pragma unroll
+    for (int b = 0; b < NVO; ++b)
+      vofs[b] = vrow * ROWB + chunk_pos<G::CPR>(vrow, 2 * b + (tr_m >> 1)) * 16 + (tr_m & 1) * 8;
+
+    auto compute_s = [&](floatx4 (&sacc)[MB][NKB], int kst) {
+      lds_u8* kb0 = lds0 + kst;
+#pragma unroll
+      for (int kk = 0; kk < G::QREG; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+              kb0 + kofs[kk % NKO] + (kk / NKO) * 256 + kb * 16 * ROWB);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            sacc[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, qf[mb][kk], kk == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sacc[mb][kb], 0, 0, 0);
+        }
+      }
+    };
+
+    floatx4 o_acc[MB][NDT], l_acc[MB];
+    float m_ref[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      m_ref[mb] = -INFINITY;
+      l_acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    const __bf16 one = (__bf16)1.0f;
+    const bf16x8 ones = {one, one, one, one, one, one, one, one};
+
+    auto pv = [&](const bf16x8 (&pf)[MB][NKS], int vst) {
+      lds_u8* vb = lds0 + vst;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          lds_u8* p0 = vb + vofs[dt % NVO] + (dt / NVO) * 256 + ks * 32 * ROWB;
+          const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4v*)(p0));
+          const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4v*)(p0 + 16 * ROWB));
+          const short8v x8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          const bf16x8 a = __builtin_bit_cast(bf16x8, x8);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            o_acc[mb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[mb][ks], o_acc[mb][dt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          l_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[mb][ks], l_acc[mb], 0, 0, 0);
+      }
+    };
+
+    const float c_scale = qk_scale_log2;
+    const float slack = kRescaleSlack / c_scale;  // in raw score units
+    // mask + online softmax of tile t in place; weights out as bf16 P^T
+    // fragments; returns whether a reference max moved (alpha < 1)
+    // mask of tile t (only tiles not inside every row's interval); a tile
+    // outside the wave's range is masked whole (its scores may come from a
+    // stale or never-written stage)
+    auto mask = [&](int t, bool act, floatx4 (&sc)[MB][NKB]) {
+      const int k0 = kt0 + t * BN;
+      const bool full = act && (k0 >= wlomax) && (k0 + BN - 1 <= whimin);
+      if (!full) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int rel0 = k0 + 4 * grp - (act ? row_lo[mb] : 0x3fffffff);
+          const unsigned rng = act ? row_rng[mb] : 0u;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              sc[mb][kb][r] = (unsigned)(rel0 + kb * 16 + r) <= rng ? sc[mb][kb][r] : -INFINITY;
+        }
+      }
+    };
+    // online softmax of the masked tile in place; weights out as bf16 P^T
+    // fragments; returns whether a reference max moved (alpha < 1)
+    auto softmax = [&](floatx4 (&sc)[MB][NKB], bf16x8 (&pf)[MB][NKS], float (&alpha)[MB]) {
+      bool any_move = false;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sc[mb][kb][r]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const bool move = tmax > m_ref[mb] + slack;
+        const float m_new = move ? tmax : m_ref[mb];
+        alpha[mb] = move ? __builtin_amdgcn_exp2f((m_ref[mb] - m_new) * c_scale) : 1.f;
+        any_move |= move;
+        m_ref[mb] = m_new;
+        const float mc = m_new == -INFINITY ? 0.f : m_new * c_scale;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pf[mb][ks][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][2 * ks][r], c_scale, -mc));
+            pf[mb][ks][4 + r] =
+                (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][2 * ks + 1][r], c_scale, -mc));
+          }
+        }
+      }
+      return any_move;
+    };
+
+    auto rescale = [&](const float (&alpha)[MB]) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        l_acc[mb] *= alpha[mb];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] *= alpha[mb];
+      }
+    };
+
+    floatx4 sA[MB][NKB], sB[MB][NKB];
+    bf16x8 pA[MB][NKS], pB[MB][NKS];
+    // weights of tiles a wave skips stay 0, so their O^T products add 0
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        pA[mb][ks] = bf16x8{};
+        pB[mb][ks] = bf16x8{};
+      }
+
+    // Q in registers before the first product (the compiler does not count
+    // the asm loads, so its own wait here covers every load in flight)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int kk = 0; kk < G::QREG; ++kk) asm volatile("" : : "v"(qf[mb][kk]));
+    // group 0 (K_0) landed in every wave: later groups may stay in flight
+    wait_vmcnt_units<G::UPT, 2 * S - 3>(loads_in(1, S - 1));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ta == 0) compute_s(sA, 0);
+
+    // one iteration: scores of tile t in sc (in), of tile t+1 into sn;
+    // weights of tile t-1 in pp (in), of tile t into pc
+    auto step = [&](int t, floatx4 (&sc)[MB][NKB], floatx4 (&sn)[MB][NKB],
+                    const bf16x8 (&pp)[MB][NKS], bf16x8 (&pc)[MB][NKS]) {
+      // group t+1 = {K_(t+1), V_(t-1)} landed; groups up to t+S-1 issued
+      wait_vmcnt_units<G::UPT, 2 * (S - 2)>(loads_in(t + 2, t + S - 1));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // every wave is done with K_t and V_(t-2): refill their stages
+      if (t + S < n) dma_pl(kbase, kt0 + (t + S) * BN, kring + (t % S) * TB);
+      if (t + S - 2 < n) dma_pl(vbase, kt0 + (t + S - 2) * BN, vring + ((t + S - 2) % S) * TB);
+      const bool a_nxt = t + 1 >= ta && t + 1 <= tb;
+      const bool a_cur = t >= ta && t <= tb;
+      const bool a_prv = t - 1 >= ta && t - 1 <= tb;
+      const int kst = ((t + 1) % S) * TB;
+      const int vst = S * TB + ((t + S - 1) % S) * TB;
+      float alpha[MB];
+      bool moved = false;
+      if (t + 1 >= ta && t <= tb + 1) {
+        mask(t, a_cur, sc);
+        // one basic block: the two MFMA chains and the softmax VALU interleave
+        compute_s(sn, kst);
+        pv(pp, vst);
+        moved = softmax(sc, pc, alpha);
+      }
+      if (__builtin_amdgcn_ballot_w64(moved)) rescale(alpha);
+    };
+
+    int t = 0;
+    for (; t + 1 < n; t += 2) {
+      step(t, sA, sB, pB, pA);
+      step(t + 1, sB, sA, pA, pB);
+    }
+    if (t < n) step(t, sA, sB, pB, pA);
+    // the last tile's O^T product: V_(n-1) (group n+1) landed in every wave
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (n - 1 >= ta && n - 1 <= tb) {
+      const int vst = S * TB + ((n - 1) % S) * TB;
+      if (n & 1) pv(pA, vst);
+      else pv(pB, vst);
+    }
+
+    // ---- epilogue: normalise and store ----------------------------------------
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const float l = l_acc[mb][0];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int i = row_i[mb];
+      if (i >= Ttot) continue;
+      T* orow = out + ((size_t)i * hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const floatx4 x = o_acc[mb][dt] * inv;
+        const bf16x4 w = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};  // RNE
+        *reinterpret_cast<bf16x4*>(orow + dt * 16 + 4 * grp) = w;
+      }
+    }
+    return;
   }
 
   // ---- accumulators ----------------------------------------------------------
@@ -549,7 +891,7 @@ void prefill_fwd_kernel(
         const int r = kb * 16 + c16;
         if constexpr (kF32) {
           const int ch = grp * (D / 16) + kk;  // d = grp*D/4 + kk*4 .. +4
-          const floatx4 a = *reinterpret_cast<const floatx4*>(&Kb[(r * G::CPR + (ch ^ chunk_swz(r))) * 4]);
+          const floatx4 a = *reinterpret_cast<const floatx4*>(&Kb[(r * G::CPR + chunk_pos<G::CPR>(r, ch)) * 4]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -557,7 +899,7 @@ void prefill_fwd_kernel(
               s[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], qf[mb][kk][st], s[mb][kb], 0, 0, 0);
         } else {
           const int ch = kk * 4 + grp;  // d = kk*32 + 8*grp .. +8
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kb[(r * G::CPR + (ch ^ chunk_swz(r))) * 8]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kb[(r * G::CPR + chunk_pos<G::CPR>(r, ch)) * 8]);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
             s[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[mb][kk], s[mb][kb], 0, 0, 0);
@@ -627,7 +969,7 @@ void prefill_fwd_kernel(
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
             const int r = kb * 16 + 4 * grp + st;
-            const float a = Vb[(r * G::CPR + ((d >> 2) ^ chunk_swz(r))) * 4 + (d & 3)];
+            const float a = Vb[(r * G::CPR + chunk_pos<G::CPR>(r, d >> 2)) * 4 + (d & 3)];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
               o_acc[mb][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[mb][kb][st], o_acc[mb][dt], 0, 0, 0);
@@ -656,8 +998,8 @@ void prefill_fwd_kernel(
           // the transpose read hands lane c16 the column dt*16 + c16 of rows
           // 32ks + 4grp .. +3 (and +16 .. +19 for the second read)
           const int ch = 2 * dt + (tr_m >> 1), off = (tr_m & 1) * 4;
-          const __bf16* p0 = &Vb[(r0 * G::CPR + (ch ^ chunk_swz(r0))) * 8 + off];
-          const __bf16* p1 = &Vb[(r1 * G::CPR + (ch ^ chunk_swz(r1))) * 8 + off];
+          const __bf16* p0 = &Vb[(r0 * G::CPR + chunk_pos<G::CPR>(r0, ch)) * 8 + off];
+          const __bf16* p1 = &Vb[(r1 * G::CPR + chunk_pos<G::CPR>(r1, ch)) * 8 + off];
           const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) short4v*)(p0));
           const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(

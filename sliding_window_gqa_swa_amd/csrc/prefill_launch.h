@@ -6,18 +6,18 @@
 
 namespace swa {
 
-template <int D, typename T, int MB, int BN, int NW, int GH>
+template <int D, typename T, int MB, int BN, int NW, int GH, bool PL = false>
 int launch_prefill_cfg(const void* q, const void* k, const void* v,
                        const int32_t* cu, const int32_t* ids, int window,
                        int mode, void* out, int total_tokens, int num_docs,
                        int hq, int hkv, float scale, hipStream_t stream) {
-  using G = PfGeom<D, T, MB, BN, NW, GH>;
+  using G = PfGeom<D, T, MB, BN, NW, GH, PL>;
   const int ntiles = (total_tokens + G::BM - 1) / G::BM;
   const int g = hq / hkv;
   const long long nwork = (long long)ntiles * hkv * (g / GH);
   const long long per_xcd = (nwork + 7) / 8;  // 8 XCDs, blocks round-robin over them
   if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, T, MB, BN, NW, GH>), dim3((unsigned)(8 * per_xcd)),
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL>), dim3((unsigned)(8 * per_xcd)),
                      dim3(G::NT), 0, stream, (const T*)q, (const T*)k, (const T*)v, cu,
                      num_docs, ids, window, mode, (T*)out, total_tokens, hq, hkv,
                      scale * kPrefillLog2e, ntiles, (int)nwork, (int)per_xcd);
