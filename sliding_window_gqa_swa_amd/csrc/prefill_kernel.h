@@ -810,19 +810,38 @@ void prefill_fwd_kernel(
       else pv(pB, vst);
     }
 
-    // ---- epilogue: normalise and store ----------------------------------------
+    // ---- epilogue: normalise, transpose through LDS, store whole rows --------
+    // O^T fragments give each lane 4 head-dim values of one row, i.e. 8-byte
+    // pieces of 16 rows per store; staging the wave's rows in LDS lets 16
+    // lanes write each 2*D-byte output row contiguously.  Every wave is done
+    // with the rings after this barrier.
+    lds_barrier();
+    {
+      constexpr int CPO = D / 8;  // 16-byte chunks per output row
+      unsigned char* ost = &ring[0][0] + wave * (G::WR * ROWB);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const float l = l_acc[mb][0];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int i = row_i[mb];
-      if (i >= Ttot) continue;
-      T* orow = out + ((size_t)i * hq + h) * D;
+      for (int mb = 0; mb < MB; ++mb) {
+        const float l = l_acc[mb][0];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const int rr = mb * 16 + c16;  // row within the wave
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const floatx4 x = o_acc[mb][dt] * inv;
-        const bf16x4 w = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};  // RNE
-        *reinterpret_cast<bf16x4*>(orow + dt * 16 + 4 * grp) = w;
+        for (int dt = 0; dt < NDT; ++dt) {
+          const floatx4 x = o_acc[mb][dt] * inv;
+          const bf16x4 w = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};  // RNE
+          // chunk (2 dt + grp/2) of row rr, rotated by rr within blocks of 16
+          const int ch = 2 * dt + (grp >> 1);
+          const int pc = (ch & ~15) | ((ch + rr) & 15);
+          *reinterpret_cast<bf16x4*>(ost + rr * ROWB + pc * 16 + (grp & 1) * 8) = w;
+        }
+      }
+      constexpr int RPI = 64 / CPO;  // rows per wave-wide store
+#pragma unroll
+      for (int j = 0; j < G::WR / RPI; ++j) {
+        const int rr = j * RPI + lane / CPO, ch = lane % CPO;
+        const int pc = (ch & ~15) | ((ch + rr) & 15);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(ost + rr * ROWB + pc * 16);
+        const int i = q0 + rb * G::WR + rr;
+        if (i < Ttot) *reinterpret_cast<u32x4*>(out + ((size_t)i * hq + h) * D + ch * 8) = x;
       }
     }
     return;
