@@ -50,10 +50,14 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "swa_common.h"
 
 namespace swa {
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
 
 constexpr float kPrefillLog2e = 1.4426950408889634f;
 // cu_seqlens entries cached in LDS for the per-row document lookup; larger
@@ -66,8 +70,6 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr int kPlanBuckets = 256;
 constexpr int kPlanMaxItems = 65536;
 
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef short short8v __attribute__((ext_vector_type(8)));
 
 // LDS tile layout: 16-byte chunk ch of row r is stored at chunk position
 // chunk_pos(r, ch) of that row, a bijection on each row's CPR chunks.  With
@@ -124,6 +126,57 @@ __device__ __forceinline__ void dma16_buf(i32x4 rsrc, int voff, uint32_t lds_wav
                :
                : "s"(lds_wave_base), "v"(voff), "s"(rsrc)
                : "memory");
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// LDS reads issued from inline assembly, so that the compiler keeps them in
+// the order written (it otherwise keeps one or two reads in flight).  The
+// compiler does not count them: lgkm_wait<N>(x...) waits until at most N
+// LDS operations are outstanding and passes the registers it guards through
+// the wait, so no instruction that reads them is moved above it.
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t addr) {
+  bf16x8 x;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(x) : "v"(addr), "i"(OFF));
+  return x;
+}
+template <int OFF>
+__device__ __forceinline__ short4v lds_tr16_b64(uint32_t addr) {
+  short4v x;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(x) : "v"(addr), "i"(OFF));
+  return x;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(bf16x8& a, bf16x8& b, bf16x8& c, bf16x8& d) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(bf16x8& a, bf16x8& b) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(short4v& a, short4v& b, short4v& c, short4v& d) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
+}
+
+// Maximum of x over lanes l, l^16, l^32, l^48 (gfx950 lane-row swaps; no LDS).
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Work-group barrier that orders LDS but leaves global/DMA loads in flight
@@ -394,13 +447,6 @@ void prefill_fwd_kernel(
     }
   };
 
-  if constexpr (PL) {
-    // the pipelined loop's first iteration reads the last V stage with zero
-    // weights before anything is loaded there: give it finite contents
-    u32x4* vz = reinterpret_cast<u32x4*>(&ring[0][0] + (2 * G::STAGES - 1) * G::TILE_BYTES);
-    for (int i = tid; i < G::TILE_BYTES / 16; i += G::NT) vz[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-
   // ---- prologue: per-row key interval [lo_i, hi_i] ------------------------
   int my_de = 0;
   if (tid < G::BM) {
@@ -551,14 +597,17 @@ void prefill_fwd_kernel(
   }
 
   if constexpr (PL) {
-    // ---- software-pipelined loop (bf16) ----------------------------------------
-    // Iteration t issues the S^T MFMAs of key tile t+1 and the O^T MFMAs of
-    // tile t-1 next to the softmax VALU work of tile t, all independent, so
-    // matrix-core and vector instructions of one wave overlap.  K tiles live
-    // in a ring of STAGES stages, V tiles in a second ring two tiles behind:
-    // load group m = {K_m, V_(m-2)} is issued STAGES-1 iterations before it
-    // is needed.  Row sums come from one extra MFMA per 32 keys with a ones
-    // A operand (the sum of the bf16 weights that also weight V).
+    // ---- software-pipelined loop (bf16, D = 128, 64-key tiles) -----------------
+    // Iteration t runs the S^T MFMAs of key tile t+1 next to the softmax of
+    // tile t, then the O^T MFMAs of tile t.  K tiles live in a 2-stage ring
+    // and V tiles in a second 2-stage ring one tile behind: load group
+    // m = {K_m, V_(m-1)} is issued in iteration m-2 and consumed in iteration
+    // m-1.  The LDS fragment reads are issued by hand ahead of their MFMAs
+    // (the compiler keeps one or two in flight, exposing the LDS latency),
+    // and scheduling barriers keep each group of MFMAs next to the vector
+    // work meant to run under it.  Row sums come from one extra MFMA per 32
+    // keys against a ones A operand: the sum of the same bf16 weights that
+    // weight V.  A wave skips the key tiles outside its own rows.
     static_assert(!kF32, "the pipelined loop is bf16 only");
     constexpr int S = G::STAGES;
     constexpr int TB = G::TILE_BYTES;
@@ -566,6 +615,8 @@ void prefill_fwd_kernel(
     constexpr int NKB = BN / 16;    // 16-key blocks per tile
     constexpr int NKS = BN / 32;    // 32-key P^T fragments per tile
     constexpr int NDT = D / 16;     // 16-wide head-dim blocks
+    static_assert(D == 128 && BN == 64 && MB == 2 && S == 2 && G::QREG == 4,
+                  "schedule written for D = 128, 64-key tiles, 32 rows per wave, 2 stages");
     const int n = (kmax - kt0) / BN + 1;  // key tiles of the work-group
 
     // this wave's rows: key range, and the rectangle every one of them admits
@@ -593,53 +644,27 @@ void prefill_fwd_kernel(
     wlomax = __builtin_amdgcn_readfirstlane(wlomax);
     whimin = __builtin_amdgcn_readfirstlane(whimin);
 
-    // loads of group m: UPT for K_m (m < n) and UPT for V_(m-2) (2 <= m <= n+1)
-    auto loads_in = [&](int a, int b2) {  // groups a .. b2
-      const int kc = max(0, min(b2, n - 1) - a + 1);
-      const int vc = max(0, min(b2, n + 1) - max(a, 2) + 1);
-      return kc + vc;
-    };
+    // group 1 = {K_1, V_0} (group 0 = {K_0} is in flight already)
+    if (1 < n) dma_pl(kbase, kt0 + BN, kring + TB);
+    dma_pl(vbase, kt0, vring);
+
+    // LDS byte addresses of this lane's fragments (see chunk_pos):
+    // chunk_pos(r + 16 j, ch) = chunk_pos(r, ch) for 16-chunk rows, so the
+    // K fragment of head-dim step kk and key block kb is at kaddr[kk] +
+    // stage + kb * 16 rows, and the V^T fragment dt of 32-key step ks at
+    // vaddr[dt] + stage + ks * 32 rows (+16 rows for its second half)
+    uint32_t kaddr[4], vaddr[8];
 #pragma unroll
-    for (int m = 1; m < S; ++m) {
-      if (m < n) dma_pl(kbase, kt0 + m * BN, kring + m * TB);
-      if (m >= 2 && m - 2 < n) dma_pl(vbase, kt0 + (m - 2) * BN, vring + (m - 2) * TB);
+    for (int kk = 0; kk < 4; ++kk)
+      kaddr[kk] = ring_base + c16 * ROWB + chunk_pos<G::CPR>(c16, 4 * kk + grp) * 16;
+    {
+      const int tr_r = (lane & 15) >> 2, tr_m = lane & 3;
+      const int vrow = 4 * grp + tr_r;
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        vaddr[b] = ring_base + vrow * ROWB + chunk_pos<G::CPR>(vrow, 2 * b + (tr_m >> 1)) * 16 +
+                   (tr_m & 1) * 8;
     }
-
-    // fixed per-lane LDS offsets: chunk_pos(r + 16 j, ch + 16 m) =
-    // chunk_pos(r, ch) + 16 m, so the K fragment of head-dim step kk reads
-    // kofs[kk % 4] + (kk / 4) * 256 bytes + kb * 16 rows, and the V^T
-    // fragment dt reads vofs[dt % 8] + (dt / 8) * 256 bytes + ks * 32 rows
-    // (+16 rows for its second half)
-    typedef __attribute__((address_space(3))) const unsigned char lds_u8;
-    lds_u8* lds0 = (lds_u8*)(&ring[0][0]);
-    constexpr int NKO = G::QREG < 4 ? G::QREG : 4;
-    constexpr int NVO = NDT < 8 ? NDT : 8;
-    static_assert(G::CPR >= 16 || (G::QREG <= 2 && NDT <= 4), "offset blocks of 16 chunks");
-    int kofs[NKO], vofs[NVO];
-#pragma unroll
-    for (int kk = 0; kk < NKO; ++kk)
-      kofs[kk] = c16 * ROWB + chunk_pos<G::CPR>(c16, 4 * kk + grp) * 16;
-    const int tr_r = (lane & 15) >> 2, tr_m = lane & 3;
-    const int vrow = 4 * grp + tr_r;
-#pragma unroll
-    for (int b = 0; b < NVO; ++b)
-      vofs[b] = vrow * ROWB + chunk_pos<G::CPR>(vrow, 2 * b + (tr_m >> 1)) * 16 + (tr_m & 1) * 8;
-
-    auto compute_s = [&](floatx4 (&sacc)[MB][NKB], int kst) {
-      lds_u8* kb0 = lds0 + kst;
-#pragma unroll
-      for (int kk = 0; kk < G::QREG; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-              kb0 + kofs[kk % NKO] + (kk / NKO) * 256 + kb * 16 * ROWB);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            sacc[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a, qf[mb][kk], kk == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sacc[mb][kb], 0, 0, 0);
-        }
-      }
-    };
 
     floatx4 o_acc[MB][NDT], l_acc[MB];
     float m_ref[MB];
@@ -652,37 +677,12 @@ void prefill_fwd_kernel(
     }
     const __bf16 one = (__bf16)1.0f;
     const bf16x8 ones = {one, one, one, one, one, one, one, one};
-
-    auto pv = [&](const bf16x8 (&pf)[MB][NKS], int vst) {
-      lds_u8* vb = lds0 + vst;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          lds_u8* p0 = vb + vofs[dt % NVO] + (dt / NVO) * 256 + ks * 32 * ROWB;
-          const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4v*)(p0));
-          const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4v*)(p0 + 16 * ROWB));
-          const short8v x8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-          const bf16x8 a = __builtin_bit_cast(bf16x8, x8);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            o_acc[mb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[mb][ks], o_acc[mb][dt], 0, 0, 0);
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          l_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[mb][ks], l_acc[mb], 0, 0, 0);
-      }
-    };
-
     const float c_scale = qk_scale_log2;
     const float slack = kRescaleSlack / c_scale;  // in raw score units
-    // mask + online softmax of tile t in place; weights out as bf16 P^T
-    // fragments; returns whether a reference max moved (alpha < 1)
+
     // mask of tile t (only tiles not inside every row's interval); a tile
     // outside the wave's range is masked whole (its scores may come from a
-    // stale or never-written stage)
+    // stale stage)
     auto mask = [&](int t, bool act, floatx4 (&sc)[MB][NKB]) {
       const int k0 = kt0 + t * BN;
       const bool full = act && (k0 >= wlomax) && (k0 + BN - 1 <= whimin);
@@ -699,116 +699,198 @@ void prefill_fwd_kernel(
         }
       }
     };
-    // online softmax of the masked tile in place; weights out as bf16 P^T
-    // fragments; returns whether a reference max moved (alpha < 1)
-    auto softmax = [&](floatx4 (&sc)[MB][NKB], bf16x8 (&pf)[MB][NKS], float (&alpha)[MB]) {
+
+    // K fragments of key blocks (2 kp, 2 kp + 1) of head-dim step kk
+    auto issue_k = [&](auto kkc, auto kpc, auto kstc, bf16x8 (&dst)[2]) {
+      constexpr int kk = decltype(kkc)::value, kp = decltype(kpc)::value, KST = decltype(kstc)::value;
+      dst[0] = lds_b128<KST + (2 * kp) * 16 * ROWB>(kaddr[kk]);
+      dst[1] = lds_b128<KST + (2 * kp + 1) * 16 * ROWB>(kaddr[kk]);
+    };
+    auto s_mfmas = [&](auto kkc, auto kpc, const bf16x8 (&kf)[2], floatx4 (&sn)[MB][NKB]) {
+      constexpr int kk = decltype(kkc)::value, kp = decltype(kpc)::value;
+      static_for<2>([&](auto ic) {
+        constexpr int kb = 2 * kp + decltype(ic)::value;
+        static_for<2>([&](auto mbc) {
+          constexpr int mb = decltype(mbc)::value;
+          sn[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              kf[decltype(ic)::value], qf[mb][kk], kk == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sn[mb][kb],
+              0, 0, 0);
+        });
+      });
+    };
+    // V^T fragments of head-dim blocks (2 (j % 4), +1) of 32-key step j / 4
+    auto issue_v = [&](auto jc, auto vstc, short4v (&dst)[4]) {
+      constexpr int j = decltype(jc)::value, VST = decltype(vstc)::value;
+      constexpr int ks = j / 4, dt0 = 2 * (j % 4);
+      dst[0] = lds_tr16_b64<VST + ks * 32 * ROWB>(vaddr[dt0]);
+      dst[1] = lds_tr16_b64<VST + ks * 32 * ROWB + 16 * ROWB>(vaddr[dt0]);
+      dst[2] = lds_tr16_b64<VST + ks * 32 * ROWB>(vaddr[dt0 + 1]);
+      dst[3] = lds_tr16_b64<VST + ks * 32 * ROWB + 16 * ROWB>(vaddr[dt0 + 1]);
+    };
+    auto pv_mfmas = [&](auto jc, const short4v (&v4)[4], const bf16x8 (&pf)[MB][NKS]) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int ks = j / 4, dt0 = 2 * (j % 4);
+      static_for<2>([&](auto hc) {
+        constexpr int hh = decltype(hc)::value;
+        const short8v x8 = {v4[2 * hh][0], v4[2 * hh][1], v4[2 * hh][2], v4[2 * hh][3],
+                            v4[2 * hh + 1][0], v4[2 * hh + 1][1], v4[2 * hh + 1][2], v4[2 * hh + 1][3]};
+        const bf16x8 a = __builtin_bit_cast(bf16x8, x8);
+        static_for<2>([&](auto mbc) {
+          constexpr int mb = decltype(mbc)::value;
+          o_acc[mb][dt0 + hh] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[mb][ks], o_acc[mb][dt0 + hh], 0, 0, 0);
+        });
+      });
+    };
+
+    floatx4 sA[MB][NKB], sB[MB][NKB];
+
+    // one iteration (t of parity par): scores of tile t in sc, of t+1 into sn
+    auto step = [&](auto parc, int t, floatx4 (&sc)[MB][NKB], floatx4 (&sn)[MB][NKB]) {
+      constexpr int par = decltype(parc)::value;
+      constexpr std::integral_constant<int, ((par + 1) % 2) * TB> KST{};  // K stage of tile t+1
+      constexpr std::integral_constant<int, 2 * TB + par * TB> VST{};     // V stage of tile t
+      // group t+1 = {K_(t+1), V_t}, the latest issued, landed in every wave
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // every wave is done with K_t and V_(t-1): refill their stages
+      if (t + 2 < n) dma_pl(kbase, kt0 + (t + 2) * BN, kring + par * TB);
+      if (t + 1 < n) dma_pl(vbase, kt0 + (t + 1) * BN, vring + ((par + 1) % 2) * TB);
+      if (!(t + 1 >= ta && t <= tb)) return;
+      const bool a_cur = t >= ta && t <= tb;
+      mask(t, a_cur, sc);
+
+      // -- phase 1: S^T of tile t+1 with the softmax of tile t --------------------
+      float alpha[MB], mc[MB];
       bool any_move = false;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
+      auto row_stats = [&](auto mbc) {
+        constexpr int mb = decltype(mbc)::value;
         float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sc[mb][kb][r]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = max_over_lane_groups(tmax);
         const bool move = tmax > m_ref[mb] + slack;
         const float m_new = move ? tmax : m_ref[mb];
         alpha[mb] = move ? __builtin_amdgcn_exp2f((m_ref[mb] - m_new) * c_scale) : 1.f;
         any_move |= move;
         m_ref[mb] = m_new;
-        const float mc = m_new == -INFINITY ? 0.f : m_new * c_scale;
+        mc[mb] = m_new == -INFINITY ? 0.f : m_new * c_scale;
+      };
+      bf16x8 pc[MB][NKS];
+      // weights of keys kb*16 + 4 grp + (2 rp, 2 rp + 1) of q-block mb
+      auto exp_pair = [&](auto mbc, auto kbc, auto rpc) {
+        constexpr int mb = decltype(mbc)::value, kb = decltype(kbc)::value, rp = decltype(rpc)::value;
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp], c_scale, -mc[mb]));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp + 1], c_scale, -mc[mb]));
+        pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp] = (__bf16)e0;
+        pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp + 1] = (__bf16)e1;
+      };
+      // exp pairs e*4 .. e*4+3 of q-block mb, keys 0..31 (e = 0) or 32..63 (e = 1)
+      auto exp_quarter = [&](auto mbc, auto ec) {
+        constexpr int e = decltype(ec)::value;
+        static_for<2>([&](auto kc) {
+          static_for<2>([&](auto rpc) {
+            exp_pair(mbc, std::integral_constant<int, 2 * e + decltype(kc)::value>{}, rpc);
+          });
+        });
+      };
+      constexpr std::integral_constant<int, 0> I0{};
+      constexpr std::integral_constant<int, 1> I1{};
+      constexpr std::integral_constant<int, 2> I2{};
+      constexpr std::integral_constant<int, 3> I3{};
+      // K fragments stream in pairs: 8 pairs (kk, kp), two in flight
+      bf16x8 kf[3][2];
+      issue_k(I0, I0, KST, kf[0]);
+      issue_k(I0, I1, KST, kf[1]);
+      row_stats(I0);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<8>([&](auto qc) {
+        constexpr int qq = decltype(qc)::value;  // pair index: kk = qq / 2, kp = qq % 2
+        if constexpr (qq + 2 < 8)
+          issue_k(std::integral_constant<int, (qq + 2) / 2>{}, std::integral_constant<int, (qq + 2) % 2>{},
+                  KST, kf[(qq + 2) % 3]);
+        if constexpr (qq + 2 < 8)
+          lgkm_wait<4>(kf[qq % 3][0], kf[qq % 3][1]);
+        else if constexpr (qq + 1 < 8)
+          lgkm_wait<2>(kf[qq % 3][0], kf[qq % 3][1]);
+        else
+          lgkm_wait<0>(kf[qq % 3][0], kf[qq % 3][1]);
+        s_mfmas(std::integral_constant<int, qq / 2>{}, std::integral_constant<int, qq % 2>{}, kf[qq % 3], sn);
+        if constexpr (qq == 0) row_stats(I1);
+        // (each finished fragment is pinned by an empty asm: the compiler
+        // would otherwise sink the work to its use after the rescale branch)
+        if constexpr (qq == 1) { exp_quarter(I0, I0); asm volatile("" : "+v"(pc[0][0])); }
+        if constexpr (qq == 3) { exp_quarter(I0, I1); asm volatile("" : "+v"(pc[0][1])); }
+        if constexpr (qq == 5) { exp_quarter(I1, I0); asm volatile("" : "+v"(pc[1][0])); }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      short4v vf[2][4];
+      issue_v(I0, VST, vf[0]);
+      if (__builtin_amdgcn_ballot_w64(any_move)) {  // rare after the first tiles
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+        for (int mb = 0; mb < MB; ++mb) {
+          l_acc[mb] *= alpha[mb];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pf[mb][ks][r] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][2 * ks][r], c_scale, -mc));
-            pf[mb][ks][4 + r] =
-                (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][2 * ks + 1][r], c_scale, -mc));
-          }
+          for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] *= alpha[mb];
         }
       }
-      return any_move;
+      // -- phase 2: O^T += V^T P^T of tile t, q-block 1's last weights alongside
+      static_for<8>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j + 1 < 8) issue_v(std::integral_constant<int, j + 1>{}, VST, vf[(j + 1) % 2]);
+        if constexpr (j == 0) { exp_quarter(I1, I1); asm volatile("" : "+v"(pc[1][1])); }
+        if constexpr (j + 1 < 8)
+          lgkm_wait<4>(vf[j % 2][0], vf[j % 2][1], vf[j % 2][2], vf[j % 2][3]);
+        else
+          lgkm_wait<0>(vf[j % 2][0], vf[j % 2][1], vf[j % 2][2], vf[j % 2][3]);
+        pv_mfmas(jc, vf[j % 2], pc);
+        if constexpr (j % 4 == 3) {
+          static_for<2>([&](auto mbc) {
+            constexpr int mb = decltype(mbc)::value;
+            l_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[mb][j / 4], l_acc[mb], 0, 0, 0);
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
-
-    auto rescale = [&](const float (&alpha)[MB]) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        l_acc[mb] *= alpha[mb];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] *= alpha[mb];
-      }
-    };
-
-    floatx4 sA[MB][NKB], sB[MB][NKB];
-    bf16x8 pA[MB][NKS], pB[MB][NKS];
-    // weights of tiles a wave skips stay 0, so their O^T products add 0
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        pA[mb][ks] = bf16x8{};
-        pB[mb][ks] = bf16x8{};
-      }
 
     // Q in registers before the first product (the compiler does not count
-    // the asm loads, so its own wait here covers every load in flight)
+    // the asm loads, so its own wait here covers every load in flight), and
+    // group 0 (K_0) landed in every wave
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int kk = 0; kk < G::QREG; ++kk) asm volatile("" : : "v"(qf[mb][kk]));
-    // group 0 (K_0) landed in every wave: later groups may stay in flight
-    wait_vmcnt_units<G::UPT, 2 * S - 3>(loads_in(1, S - 1));
+    wait_vmcnt_units<G::UPT, 2>((1 < n ? 1 : 0) + 1);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (ta == 0) compute_s(sA, 0);
+    if (ta == 0) {
+      static_for<4>([&](auto kkc) {
+        constexpr int kk = decltype(kkc)::value;
+        static_for<2>([&](auto kpc) {
+          bf16x8 kf[2];
+          issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
+          lgkm_wait<0>(kf[0], kf[1]);
+          s_mfmas(kkc, kpc, kf, sA);
+        });
+        (void)kk;
+      });
+    }
 
-    // one iteration: scores of tile t in sc (in), of tile t+1 into sn;
-    // weights of tile t-1 in pp (in), of tile t into pc
-    auto step = [&](int t, floatx4 (&sc)[MB][NKB], floatx4 (&sn)[MB][NKB],
-                    const bf16x8 (&pp)[MB][NKS], bf16x8 (&pc)[MB][NKS]) {
-      // group t+1 = {K_(t+1), V_(t-1)} landed; groups up to t+S-1 issued
-      wait_vmcnt_units<G::UPT, 2 * (S - 2)>(loads_in(t + 2, t + S - 1));
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      // every wave is done with K_t and V_(t-2): refill their stages
-      if (t + S < n) dma_pl(kbase, kt0 + (t + S) * BN, kring + (t % S) * TB);
-      if (t + S - 2 < n) dma_pl(vbase, kt0 + (t + S - 2) * BN, vring + ((t + S - 2) % S) * TB);
-      const bool a_nxt = t + 1 >= ta && t + 1 <= tb;
-      const bool a_cur = t >= ta && t <= tb;
-      const bool a_prv = t - 1 >= ta && t - 1 <= tb;
-      const int kst = ((t + 1) % S) * TB;
-      const int vst = S * TB + ((t + S - 1) % S) * TB;
-      float alpha[MB];
-      bool moved = false;
-      if (t + 1 >= ta && t <= tb + 1) {
-        mask(t, a_cur, sc);
-        // one basic block: the two MFMA chains and the softmax VALU interleave
-        compute_s(sn, kst);
-        pv(pp, vst);
-        moved = softmax(sc, pc, alpha);
-      }
-      if (__builtin_amdgcn_ballot_w64(moved)) rescale(alpha);
-    };
-
+    constexpr std::integral_constant<int, 0> EVEN{};
+    constexpr std::integral_constant<int, 1> ODD{};
     int t = 0;
     for (; t + 1 < n; t += 2) {
-      step(t, sA, sB, pB, pA);
-      step(t + 1, sB, sA, pA, pB);
+      step(EVEN, t, sA, sB);
+      step(ODD, t + 1, sB, sA);
     }
-    if (t < n) step(t, sA, sB, pB, pA);
-    // the last tile's O^T product: V_(n-1) (group n+1) landed in every wave
-    wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (n - 1 >= ta && n - 1 <= tb) {
-      const int vst = S * TB + ((n - 1) % S) * TB;
-      if (n & 1) pv(pA, vst);
-      else pv(pB, vst);
-    }
+    if (t < n) step(EVEN, t, sA, sB);
+    wait_vmcnt<0>();  // nothing may still be writing LDS below
 
     // ---- epilogue: normalise, transpose through LDS, store whole rows --------
     // O^T fragments give each lane 4 head-dim values of one row, i.e. 8-byte
