@@ -393,27 +393,6 @@ void prefill_fwd_kernel(
   const int rb = wave / GH;  // row block of this wave
   const int h = hbase + jh;
 
-  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers.  Issued
-  // before the row-interval prologue so that their latency overlaps it and
-  // the first key tile's loads.
-  // bf16: fragment kk holds d = kk*32 + 8*grp + e (e < 8);
-  // fp32: lane group grp owns d = grp*D/4 + ..., 4 per fragment.
-  using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
-  QF qf[MB][G::QREG];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int i = q0 + rb * G::WR + mb * 16 + c16;
-    const bool ok = i < Ttot;
-    const T* qrow = q + ((size_t)(ok ? i : 0) * hq + h) * D;
-#pragma unroll
-    for (int kk = 0; kk < G::QREG; ++kk) {
-      const int d0 = kF32 ? grp * (D / 4) + kk * 4 : kk * 32 + 8 * grp;
-      QF x = QF{};
-      if (ok) x = *reinterpret_cast<const QF*>(qrow + d0);
-      qf[mb][kk] = x;
-    }
-  }
-
   const size_t kv_row_stride = (size_t)hkv * D;
   const T* kbase = k + (size_t)kvh * D;
   const T* vbase = v + (size_t)kvh * D;
@@ -446,6 +425,70 @@ void prefill_fwd_kernel(
       dma16(vt + unit_off[i] - back, vl + i * 1024);
     }
   };
+
+  // first key tile of the work-group: row q0 has the smallest lo of the
+  // tile (lo_i never decreases with i), computed here from cu_seqlens alone
+  // so that the first K/V loads go out together with the Q loads
+  int kt0;
+  {
+    int a = 0, bnd = ndocs + 1;  // upper_bound over cu: first d with cu[d] > q0
+    while (a < bnd) {
+      const int mid = (a + bnd) >> 1;
+      const int c = cu_in_lds ? cu_s[mid] : cu[mid];
+      if (c > q0) bnd = mid; else a = mid + 1;
+    }
+    const int doc = a - 1;
+    int ds = (doc >= 0 && doc < ndocs) ? (cu_in_lds ? cu_s[doc] : cu[doc]) : q0;
+    ds = min(max(ds, 0), q0);
+    const int lo0 = (W > 0) ? max(ds, q0 - W + 1) : ds;
+    kt0 = __builtin_amdgcn_readfirstlane((lo0 / BN) * BN);
+  }
+  // pipelined layout: K ring of STAGES tiles, then V ring of STAGES tiles
+  const uint32_t kring = ring_base, vring = ring_base + G::STAGES * G::TILE_BYTES;
+  int voff[G::UPT];
+#pragma unroll
+  for (int i = 0; i < G::UPT; ++i) voff[i] = unit_off[i] * (int)sizeof(T);
+  // one K or V tile (keys k0 .. k0+BN-1 of this kv head) into an LDS stage;
+  // rows at or past Ttot fall outside the buffer and arrive as zeros
+  auto dma_pl = [&](const T* tb, int k0, uint32_t lds_stage) {
+    const T* p0 = tb + (size_t)k0 * kv_row_stride;
+    const long long rem = (long long)(Ttot - k0) * (long long)kv_row_stride * (long long)sizeof(T);
+    const uint32_t nrec = rem <= 0 ? 0u : (rem > 0xffffffffLL ? 0xffffffffu : (uint32_t)rem);
+    const i32x4 rsrc = make_buffer_rsrc(p0, nrec);
+    const uint32_t lw = lds_stage + wave_u * G::UPT * 1024;
+#pragma unroll
+    for (int i = 0; i < G::UPT; ++i) dma16_buf(rsrc, voff[i], lw + i * 1024);
+  };
+  if constexpr (PL) {
+    // groups 0 = {K_0} and 1 = {K_1, V_0} of the pipelined loop (K_1 is
+    // loaded even when the work-group has a single key tile: unused then)
+    dma_pl(kbase, kt0, kring);
+    dma_pl(kbase, kt0 + BN, kring + G::TILE_BYTES);
+    dma_pl(vbase, kt0, vring);
+  } else {
+    dma_tile(kt0, 0);
+  }
+
+  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers.  Issued
+  // before the row-interval prologue so that their latency overlaps it and
+  // the first key tile's loads.
+  // bf16: fragment kk holds d = kk*32 + 8*grp + e (e < 8);
+  // fp32: lane group grp owns d = grp*D/4 + ..., 4 per fragment.
+  using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
+  QF qf[MB][G::QREG];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int i = q0 + rb * G::WR + mb * 16 + c16;
+    const bool ok = i < Ttot;
+    const T* qrow = q + ((size_t)(ok ? i : 0) * hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < G::QREG; ++kk) {
+      const int d0 = kF32 ? grp * (D / 4) + kk * 4 : kk * 32 + 8 * grp;
+      QF x = QF{};
+      if (ok) x = *reinterpret_cast<const QF*>(qrow + d0);
+      qf[mb][kk] = x;
+    }
+  }
 
   // ---- prologue: per-row key interval [lo_i, hi_i] ------------------------
   int my_de = 0;
@@ -522,60 +565,50 @@ void prefill_fwd_kernel(
     }
   }
   __syncthreads();
-  // Row q0 has the smallest lo of the tile (lo_i never decreases with i), so
-  // the first key tile is known now: start its loads before the reductions.
-  const int kt0 = __builtin_amdgcn_readfirstlane((lo_s[0] / BN) * BN);
-  // pipelined layout: K ring of STAGES tiles, then V ring of STAGES tiles
-  const uint32_t kring = ring_base, vring = ring_base + G::STAGES * G::TILE_BYTES;
-  int voff[G::UPT];
-#pragma unroll
-  for (int i = 0; i < G::UPT; ++i) voff[i] = unit_off[i] * (int)sizeof(T);
-  // one K or V tile (keys k0 .. k0+BN-1 of this kv head) into an LDS stage;
-  // rows at or past Ttot fall outside the buffer and arrive as zeros
-  auto dma_pl = [&](const T* tb, int k0, uint32_t lds_stage) {
-    const T* p0 = tb + (size_t)k0 * kv_row_stride;
-    const long long rem = (long long)(Ttot - k0) * (long long)kv_row_stride * (long long)sizeof(T);
-    const i32x4 rsrc = make_buffer_rsrc(p0, rem > 0xffffffffLL ? 0xffffffffu : (uint32_t)rem);
-    const uint32_t lw = lds_stage + wave_u * G::UPT * 1024;
-#pragma unroll
-    for (int i = 0; i < G::UPT; ++i) dma16_buf(rsrc, voff[i], lw + i * 1024);
-  };
-  if constexpr (PL)
-    dma_pl(kbase, kt0, kring);
-  else
-    dma_tile(kt0, 0);
 
-  // tile key range and the rectangle every row admits
-  {
-    int kmin = 0x7fffffff, kmax = -1, lomax = -1, himin = 0x7fffffff;
-    if (tid < G::BM && q0 + tid < Ttot) {
-      kmin = lo_s[tid];
-      kmax = hi_s[tid];
-      lomax = lo_s[tid];
-      himin = hi_s[tid];
-    }
+  // tile key range and the rectangle every row admits.  Causal intervals
+  // are monotone in the row (lo_i and hi_i = i never decrease), so the
+  // bounds are those of the first and last valid rows; blockwise intervals
+  // are reduced over all rows.
+  const int last_row = min(G::BM, Ttot - q0) - 1;  // >= 0: q0 < Ttot
+  int kmin, kmax, lomax, himin;
+  if (mode != SWA_BLOCKWISE) {
+    kmin = lo_s[0];
+    himin = hi_s[0];
+    kmax = hi_s[last_row];
+    lomax = lo_s[last_row];
+  } else {
+    {
+      int a0 = 0x7fffffff, a1 = -1, a2 = -1, a3 = 0x7fffffff;
+      if (tid < G::BM && q0 + tid < Ttot) {
+        a0 = lo_s[tid];
+        a1 = hi_s[tid];
+        a2 = lo_s[tid];
+        a3 = hi_s[tid];
+      }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      kmin = min(kmin, __shfl_xor(kmin, o, 64));
-      kmax = max(kmax, __shfl_xor(kmax, o, 64));
-      lomax = max(lomax, __shfl_xor(lomax, o, 64));
-      himin = min(himin, __shfl_xor(himin, o, 64));
+      for (int o = 32; o > 0; o >>= 1) {
+        a0 = min(a0, __shfl_xor(a0, o, 64));
+        a1 = max(a1, __shfl_xor(a1, o, 64));
+        a2 = max(a2, __shfl_xor(a2, o, 64));
+        a3 = min(a3, __shfl_xor(a3, o, 64));
+      }
+      if (lane == 0) {
+        red_s[0][wave] = a0;
+        red_s[1][wave] = a1;
+        red_s[2][wave] = a2;
+        red_s[3][wave] = a3;
+      }
     }
-    if (lane == 0) {
-      red_s[0][wave] = kmin;
-      red_s[1][wave] = kmax;
-      red_s[2][wave] = lomax;
-      red_s[3][wave] = himin;
-    }
-  }
-  lds_barrier();
-  int kmin = red_s[0][0], kmax = red_s[1][0], lomax = red_s[2][0], himin = red_s[3][0];
+    lds_barrier();
+    kmin = red_s[0][0], kmax = red_s[1][0], lomax = red_s[2][0], himin = red_s[3][0];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    kmin = min(kmin, red_s[0][w]);
-    kmax = max(kmax, red_s[1][w]);
-    lomax = max(lomax, red_s[2][w]);
-    himin = min(himin, red_s[3][w]);
+    for (int w = 1; w < NW; ++w) {
+      kmin = min(kmin, red_s[0][w]);
+      kmax = max(kmax, red_s[1][w]);
+      lomax = max(lomax, red_s[2][w]);
+      himin = min(himin, red_s[3][w]);
+    }
   }
   if (kmax < kmin) {  // no valid row (cannot happen: row q0 < Ttot); uniform exit
     wait_vmcnt<0>();  // never leave with a load still writing this block's LDS
@@ -620,23 +653,34 @@ void prefill_fwd_kernel(
     const int n = (kmax - kt0) / BN + 1;  // key tiles of the work-group
 
     // this wave's rows: key range, and the rectangle every one of them admits
+    // (monotone causal intervals: first and last valid rows of the wave)
     int wlo = 0x7fffffff, whi = -1, wlomax = -1, whimin = 0x7fffffff;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (row_i[mb] < Ttot && row_lo[mb] != 0x3fffffff) {
-        const int lo = row_lo[mb], hi = lo + (int)row_rng[mb];
-        wlo = min(wlo, lo);
-        whi = max(whi, hi);
-        wlomax = max(wlomax, lo);
-        whimin = min(whimin, hi);
+    if (mode != SWA_BLOCKWISE) {
+      const int r0 = rb * G::WR, r1 = min(r0 + G::WR - 1, last_row);
+      if (r0 <= last_row) {
+        wlo = lo_s[r0];
+        whimin = hi_s[r0];
+        whi = hi_s[r1];
+        wlomax = lo_s[r1];
       }
-    }
+    } else {
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      wlo = min(wlo, __shfl_xor(wlo, o, 64));
-      whi = max(whi, __shfl_xor(whi, o, 64));
-      wlomax = max(wlomax, __shfl_xor(wlomax, o, 64));
-      whimin = min(whimin, __shfl_xor(whimin, o, 64));
+      for (int mb = 0; mb < MB; ++mb) {
+        if (row_i[mb] < Ttot && row_lo[mb] != 0x3fffffff) {
+          const int lo = row_lo[mb], hi = lo + (int)row_rng[mb];
+          wlo = min(wlo, lo);
+          whi = max(whi, hi);
+          wlomax = max(wlomax, lo);
+          whimin = min(whimin, hi);
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        wlo = min(wlo, __shfl_xor(wlo, o, 64));
+        whi = max(whi, __shfl_xor(whi, o, 64));
+        wlomax = max(wlomax, __shfl_xor(wlomax, o, 64));
+        whimin = min(whimin, __shfl_xor(whimin, o, 64));
+      }
     }
     // active key tiles of this wave: [ta, tb] (empty for a wave past the end)
     const int ta = __builtin_amdgcn_readfirstlane(whi >= wlo ? (wlo - kt0) / BN : n);
@@ -644,9 +688,6 @@ void prefill_fwd_kernel(
     wlomax = __builtin_amdgcn_readfirstlane(wlomax);
     whimin = __builtin_amdgcn_readfirstlane(whimin);
 
-    // group 1 = {K_1, V_0} (group 0 = {K_0} is in flight already)
-    if (1 < n) dma_pl(kbase, kt0 + BN, kring + TB);
-    dma_pl(vbase, kt0, vring);
 
     // LDS byte addresses of this lane's fragments (see chunk_pos):
     // chunk_pos(r + 16 j, ch) = chunk_pos(r, ch) for 16-chunk rows, so the
@@ -865,7 +906,7 @@ void prefill_fwd_kernel(
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int kk = 0; kk < G::QREG; ++kk) asm volatile("" : : "v"(qf[mb][kk]));
-    wait_vmcnt_units<G::UPT, 2>((1 < n ? 1 : 0) + 1);
+    wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -895,12 +936,16 @@ void prefill_fwd_kernel(
     // ---- epilogue: normalise, transpose through LDS, store whole rows --------
     // O^T fragments give each lane 4 head-dim values of one row, i.e. 8-byte
     // pieces of 16 rows per store; staging the wave's rows in LDS lets 16
-    // lanes write each 2*D-byte output row contiguously.  Every wave is done
-    // with the rings after this barrier.
-    lds_barrier();
+    // lanes write each 2*D-byte output row contiguously.  No barrier: once
+    // this wave is past the last iteration, every wave is past iteration
+    // n-2, and iteration n-1 reads neither K stage (n-1) % 2 nor V stage
+    // n % 2, and no load is still headed there.  Waves 0-1 stage in the
+    // former, waves 2-3 in the latter.
     {
+      static_assert(NW == 4 && 2 * G::WR * ROWB == TB, "two waves per free stage");
       constexpr int CPO = D / 8;  // 16-byte chunks per output row
-      unsigned char* ost = &ring[0][0] + wave * (G::WR * ROWB);
+      const int free_stage = wave < 2 ? ((n - 1) & 1) * TB : 2 * TB + (n & 1) * TB;
+      unsigned char* ost = &ring[0][0] + free_stage + (wave & 1) * (G::WR * ROWB);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const float l = l_acc[mb][0];
