@@ -1,6 +1,6 @@
 // prefill_d512.hip -- prefill instantiations for head dimension 512.
 // Template arguments: <D, element, q-blocks of 16 rows per wave, key tile,
-// waves, query heads per work-group sharing the K/V tiles>.
+// waves, query heads per work-group sharing the K/V tiles, pipelined loop>.
 #include "prefill_launch.h"
 
 namespace swa {
@@ -11,9 +11,9 @@ int launch_prefill_d512(const void* q, const void* k, const void* v, const int32
   const int g = hq / hkv;
   if (dtype == SWA_BF16) {
     if (g % 2 == 0)
-      return launch_prefill_cfg<512, __bf16, 1, 32, 8, 2>(q, k, v, cu, ids, window, mode, out,
+      return launch_prefill_cfg<512, __bf16, 2, 32, 4, 2, true>(q, k, v, cu, ids, window, mode, out,
                                                        total_tokens, num_docs, hq, hkv, scale, s);
-    return launch_prefill_cfg<512, __bf16, 1, 32, 8, 1>(q, k, v, cu, ids, window, mode, out,
+    return launch_prefill_cfg<512, __bf16, 2, 32, 4, 1, true>(q, k, v, cu, ids, window, mode, out,
                                                      total_tokens, num_docs, hq, hkv, scale, s);
   }
   return launch_prefill_cfg<512, float, 1, 16, 4, 1>(q, k, v, cu, ids, window, mode, out,

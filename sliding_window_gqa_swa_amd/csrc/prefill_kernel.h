@@ -65,6 +65,9 @@ constexpr float kPrefillLog2e = 1.4426950408889634f;
 constexpr int kCuCache = 1024;
 // exp2 arguments stay <= this between reference-max moves (p <= 2^8)
 constexpr float kRescaleSlack = 8.0f;
+// fixed-reference loop: largest rise (log2 units) of a row's scores above its
+// reference before the key loop is repeated with the true maxima (p <= 2^32)
+constexpr float kFixedRefLimit = 32.0f;
 // Work order: cost buckets of the counting sort, and the largest slice of
 // work items one XCD may hold for the sort (one byte each, in the LDS ring)
 constexpr int kPlanBuckets = 256;
@@ -171,6 +174,26 @@ __device__ __forceinline__ void lgkm_wait(short4v& a, short4v& b, short4v& c, sh
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
 }
 
+// S^T products issued from inline assembly with the accumulator in VGPRs.
+// When a kernel may use more than 256 registers the compiler gives every
+// MFMA builtin an AGPR accumulator; at D = 512 the O^T accumulators alone
+// fill the 256 AGPRs, so the score products are written by hand to keep
+// theirs in VGPRs.  The compiler does not see these as matrix instructions:
+// a VALU read of `acc` must come at least kMfmaDrain wait states after the
+// last product that wrote it (the callers guarantee that), and a product
+// whose C operand is the previous product's result with the same registers
+// is forwarded by the hardware.
+__device__ __forceinline__ void mfma_bf16_vacc(floatx4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_bf16_vacc0(floatx4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+// wait states that cover an 8-pass product's result latency (with margin)
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 // Maximum of x over lanes l, l^16, l^32, l^48 (gfx950 lane-row swaps; no LDS).
 __device__ __forceinline__ float max_over_lane_groups(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -205,6 +228,19 @@ template <>
 struct PfTraits<float> {
   static constexpr int VEC = 4;
   static constexpr int KW = 16;  // one 16-byte LDS read feeds 4 MFMAs of K=4
+};
+
+// Pipelined loop: LDS fragment lookahead (K fragment pairs, V^T fragment
+// groups) per head dimension.
+template <int D>
+struct PfLookahead {
+#ifndef SWA_PF_KLA
+  static constexpr int K = D == 128 ? 2 : 3;
+  static constexpr int V = D == 128 ? 1 : 2;
+#else
+  static constexpr int K = D == 128 ? 2 : SWA_PF_KLA;
+  static constexpr int V = D == 128 ? 1 : SWA_PF_VLA;
+#endif
 };
 
 // Workgroup geometry.
@@ -335,7 +371,7 @@ __device__ int lpt_slot(const int* cu_s, int ndocs, int Ttot, int W, int ntiles,
 }
 
 template <int D, typename T, int MB, int BN, int NW, int GH, bool PL>
-__global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 256 && !std::is_same<T, float>::value) ? 2 : 1)
+__global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 256 && (D <= 128 || !PL) && !std::is_same<T, float>::value) ? 2 : 1)
 void prefill_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ cu, int ndocs, const int32_t* __restrict__ ids,
@@ -648,8 +684,21 @@ void prefill_fwd_kernel(
     constexpr int NKB = BN / 16;    // 16-key blocks per tile
     constexpr int NKS = BN / 32;    // 32-key P^T fragments per tile
     constexpr int NDT = D / 16;     // 16-wide head-dim blocks
-    static_assert(D == 128 && BN == 64 && MB == 2 && S == 2 && G::QREG == 4,
-                  "schedule written for D = 128, 64-key tiles, 32 rows per wave, 2 stages");
+    constexpr int QR = G::QREG;     // 32-wide head-dim steps of S^T
+    constexpr int NP = QR * (NKB / 2);  // K fragment pairs per tile (4 MFMAs each)
+    constexpr int NJ = NKS * (NDT / 2); // V^T fragment groups per tile (4 MFMAs each)
+    // LDS fragment lookahead: K pairs and V groups requested ahead of use
+    constexpr int KLA = PfLookahead<D>::K, VLA = PfLookahead<D>::V;
+    static_assert(2 * KLA <= 15 && 4 * VLA <= 15, "lgkmcnt range");
+    // D >= 256: score products by hand (VGPR accumulators, see mfma_bf16_vacc)
+    // and row sums on the VALU, so that the AGPRs hold O^T alone
+    constexpr bool kAsmS = D >= 256;
+    static_assert(MB == 2 && S == 2 && NW == 4 && BN % 32 == 0 && D % 128 == 0,
+                  "schedule written for 32 rows per wave, 4 waves, 2 stages, D a multiple of 128");
+    // every LDS fragment offset below is an instruction immediate (16 bits)
+    static_assert(TB + (NKB - 1) * 16 * ROWB + (QR / 4 - 1) * 256 < 65536, "K offsets fit");
+    static_assert(TB + (NKS - 1) * 32 * ROWB + 16 * ROWB + (NDT / 8 - 1) * 256 < 65536,
+                  "V offsets fit");
     const int n = (kmax - kt0) / BN + 1;  // key tiles of the work-group
 
     // this wave's rows: key range, and the rectangle every one of them admits
@@ -690,28 +739,34 @@ void prefill_fwd_kernel(
 
 
     // LDS byte addresses of this lane's fragments (see chunk_pos):
-    // chunk_pos(r + 16 j, ch) = chunk_pos(r, ch) for 16-chunk rows, so the
-    // K fragment of head-dim step kk and key block kb is at kaddr[kk] +
-    // stage + kb * 16 rows, and the V^T fragment dt of 32-key step ks at
-    // vaddr[dt] + stage + ks * 32 rows (+16 rows for its second half)
+    // chunk_pos(r + 16 j, ch) = chunk_pos(r, ch) for 16-chunk rows, and the
+    // rotation stays inside each aligned block of 16 chunks (256 bytes), so
+    // the K fragment of head-dim step kk and key block kb is at
+    // kaddr[kk % 4] + stage + kb * 16 rows + (kk / 4) * 256, and the V^T
+    // fragment dt of 32-key step ks at vaddr[dt % 8] + stage + ks * 32 rows
+    // (+16 rows for its second half) + (dt / 8) * 256.  K addresses start at
+    // the K ring, V addresses at the V ring.
     uint32_t kaddr[4], vaddr[8];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      kaddr[kk] = ring_base + c16 * ROWB + chunk_pos<G::CPR>(c16, 4 * kk + grp) * 16;
+      kaddr[kk] = kring + c16 * ROWB + chunk_pos<G::CPR>(c16, 4 * kk + grp) * 16;
     {
       const int tr_r = (lane & 15) >> 2, tr_m = lane & 3;
       const int vrow = 4 * grp + tr_r;
 #pragma unroll
       for (int b = 0; b < 8; ++b)
-        vaddr[b] = ring_base + vrow * ROWB + chunk_pos<G::CPR>(vrow, 2 * b + (tr_m >> 1)) * 16 +
+        vaddr[b] = vring + vrow * ROWB + chunk_pos<G::CPR>(vrow, 2 * b + (tr_m >> 1)) * 16 +
                    (tr_m & 1) * 8;
     }
 
     floatx4 o_acc[MB][NDT], l_acc[MB];
-    float m_ref[MB];
+    float m_ref[MB], l_part[MB];  // l_part: this lane's share of the row sum (kAsmS)
+    float dmax[MB];               // kAsmS: rise of later tile maxima above m_ref
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       m_ref[mb] = -INFINITY;
+      dmax[mb] = -INFINITY;
+      l_part[mb] = 0.f;
       l_acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -744,8 +799,9 @@ void prefill_fwd_kernel(
     // K fragments of key blocks (2 kp, 2 kp + 1) of head-dim step kk
     auto issue_k = [&](auto kkc, auto kpc, auto kstc, bf16x8 (&dst)[2]) {
       constexpr int kk = decltype(kkc)::value, kp = decltype(kpc)::value, KST = decltype(kstc)::value;
-      dst[0] = lds_b128<KST + (2 * kp) * 16 * ROWB>(kaddr[kk]);
-      dst[1] = lds_b128<KST + (2 * kp + 1) * 16 * ROWB>(kaddr[kk]);
+      constexpr int OFF = KST + (kk / 4) * 256;
+      dst[0] = lds_b128<OFF + (2 * kp) * 16 * ROWB>(kaddr[kk % 4]);
+      dst[1] = lds_b128<OFF + (2 * kp + 1) * 16 * ROWB>(kaddr[kk % 4]);
     };
     auto s_mfmas = [&](auto kkc, auto kpc, const bf16x8 (&kf)[2], floatx4 (&sn)[MB][NKB]) {
       constexpr int kk = decltype(kkc)::value, kp = decltype(kpc)::value;
@@ -753,24 +809,31 @@ void prefill_fwd_kernel(
         constexpr int kb = 2 * kp + decltype(ic)::value;
         static_for<2>([&](auto mbc) {
           constexpr int mb = decltype(mbc)::value;
-          sn[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              kf[decltype(ic)::value], qf[mb][kk], kk == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sn[mb][kb],
-              0, 0, 0);
+          if constexpr (kAsmS) {
+            if constexpr (kk == 0) mfma_bf16_vacc0(sn[mb][kb], kf[decltype(ic)::value], qf[mb][kk]);
+            else mfma_bf16_vacc(sn[mb][kb], kf[decltype(ic)::value], qf[mb][kk]);
+          } else {
+            sn[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                kf[decltype(ic)::value], qf[mb][kk], kk == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sn[mb][kb],
+                0, 0, 0);
+          }
         });
       });
     };
-    // V^T fragments of head-dim blocks (2 (j % 4), +1) of 32-key step j / 4
+    // V^T fragments of head-dim blocks (dt0, dt0 + 1), dt0 = 2 (j % (NDT/2)),
+    // of 32-key step j / (NDT/2)
     auto issue_v = [&](auto jc, auto vstc, short4v (&dst)[4]) {
       constexpr int j = decltype(jc)::value, VST = decltype(vstc)::value;
-      constexpr int ks = j / 4, dt0 = 2 * (j % 4);
-      dst[0] = lds_tr16_b64<VST + ks * 32 * ROWB>(vaddr[dt0]);
-      dst[1] = lds_tr16_b64<VST + ks * 32 * ROWB + 16 * ROWB>(vaddr[dt0]);
-      dst[2] = lds_tr16_b64<VST + ks * 32 * ROWB>(vaddr[dt0 + 1]);
-      dst[3] = lds_tr16_b64<VST + ks * 32 * ROWB + 16 * ROWB>(vaddr[dt0 + 1]);
+      constexpr int ks = j / (NDT / 2), dt0 = 2 * (j % (NDT / 2));
+      constexpr int OFF = VST + ks * 32 * ROWB + (dt0 / 8) * 256;
+      dst[0] = lds_tr16_b64<OFF>(vaddr[dt0 % 8]);
+      dst[1] = lds_tr16_b64<OFF + 16 * ROWB>(vaddr[dt0 % 8]);
+      dst[2] = lds_tr16_b64<OFF>(vaddr[dt0 % 8 + 1]);
+      dst[3] = lds_tr16_b64<OFF + 16 * ROWB>(vaddr[dt0 % 8 + 1]);
     };
     auto pv_mfmas = [&](auto jc, const short4v (&v4)[4], const bf16x8 (&pf)[MB][NKS]) {
       constexpr int j = decltype(jc)::value;
-      constexpr int ks = j / 4, dt0 = 2 * (j % 4);
+      constexpr int ks = j / (NDT / 2), dt0 = 2 * (j % (NDT / 2));
       static_for<2>([&](auto hc) {
         constexpr int hh = decltype(hc)::value;
         const short8v x8 = {v4[2 * hh][0], v4[2 * hh][1], v4[2 * hh][2], v4[2 * hh][3],
@@ -790,7 +853,7 @@ void prefill_fwd_kernel(
     auto step = [&](auto parc, int t, floatx4 (&sc)[MB][NKB], floatx4 (&sn)[MB][NKB]) {
       constexpr int par = decltype(parc)::value;
       constexpr std::integral_constant<int, ((par + 1) % 2) * TB> KST{};  // K stage of tile t+1
-      constexpr std::integral_constant<int, 2 * TB + par * TB> VST{};     // V stage of tile t
+      constexpr std::integral_constant<int, par * TB> VST{};              // V stage of tile t
       // group t+1 = {K_(t+1), V_t}, the latest issued, landed in every wave
       wait_vmcnt<0>();
       asm volatile("" ::: "memory");
@@ -814,12 +877,20 @@ void prefill_fwd_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sc[mb][kb][r]);
         tmax = max_over_lane_groups(tmax);
-        const bool move = tmax > m_ref[mb] + slack;
-        const float m_new = move ? tmax : m_ref[mb];
-        alpha[mb] = move ? __builtin_amdgcn_exp2f((m_ref[mb] - m_new) * c_scale) : 1.f;
-        any_move |= move;
-        m_ref[mb] = m_new;
-        mc[mb] = m_new == -INFINITY ? 0.f : m_new * c_scale;
+        if constexpr (kAsmS) {
+          // fixed reference: the maximum of the row's first tile with an
+          // allowed key; later maxima only record how far they rose above it
+          if (m_ref[mb] == -INFINITY) m_ref[mb] = tmax;
+          else dmax[mb] = fmaxf(dmax[mb], tmax - m_ref[mb]);
+          mc[mb] = m_ref[mb] == -INFINITY ? 0.f : m_ref[mb] * c_scale;
+        } else {
+          const bool move = tmax > m_ref[mb] + slack;
+          const float m_new = move ? tmax : m_ref[mb];
+          alpha[mb] = move ? __builtin_amdgcn_exp2f((m_ref[mb] - m_new) * c_scale) : 1.f;
+          any_move |= move;
+          m_ref[mb] = m_new;
+          mc[mb] = m_new == -INFINITY ? 0.f : m_new * c_scale;
+        }
       };
       bf16x8 pc[MB][NKS];
       // weights of keys kb*16 + 4 grp + (2 rp, 2 rp + 1) of q-block mb
@@ -827,8 +898,16 @@ void prefill_fwd_kernel(
         constexpr int mb = decltype(mbc)::value, kb = decltype(kbc)::value, rp = decltype(rpc)::value;
         const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp], c_scale, -mc[mb]));
         const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp + 1], c_scale, -mc[mb]));
-        pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp] = (__bf16)e0;
-        pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp + 1] = (__bf16)e1;
+        const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
+        pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp] = b0;
+        pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp + 1] = b1;
+        // the row sum adds the same bf16 weights that multiply V
+        if constexpr (kAsmS) l_part[mb] += (float)b0 + (float)b1;
+      };
+      auto exp_pair_pinned = [&](auto mbc, auto kbc, auto rpc) {
+        exp_pair(mbc, kbc, rpc);
+        bf16x8& x = pc[decltype(mbc)::value][decltype(kbc)::value / 2];
+        asm volatile("" : "+v"(x));
       };
       // exp pairs e*4 .. e*4+3 of q-block mb, keys 0..31 (e = 0) or 32..63 (e = 1)
       auto exp_quarter = [&](auto mbc, auto ec) {
@@ -843,56 +922,79 @@ void prefill_fwd_kernel(
       constexpr std::integral_constant<int, 1> I1{};
       constexpr std::integral_constant<int, 2> I2{};
       constexpr std::integral_constant<int, 3> I3{};
-      // K fragments stream in pairs: 8 pairs (kk, kp), two in flight
-      bf16x8 kf[3][2];
-      issue_k(I0, I0, KST, kf[0]);
-      issue_k(I0, I1, KST, kf[1]);
+      // K fragments stream in pairs (kk, kp) = (qq / (NKB/2), qq % (NKB/2)),
+      // two pairs in flight
+      bf16x8 kf[KLA + 1][2];
+      static_for<(KLA < NP ? KLA : NP)>([&](auto pc0) {
+        constexpr int q0 = decltype(pc0)::value;
+        issue_k(std::integral_constant<int, q0 / (NKB / 2)>{}, std::integral_constant<int, q0 % (NKB / 2)>{},
+                KST, kf[q0]);
+      });
       row_stats(I0);
       __builtin_amdgcn_sched_barrier(0);
-      static_for<8>([&](auto qc) {
-        constexpr int qq = decltype(qc)::value;  // pair index: kk = qq / 2, kp = qq % 2
-        if constexpr (qq + 2 < 8)
-          issue_k(std::integral_constant<int, (qq + 2) / 2>{}, std::integral_constant<int, (qq + 2) % 2>{},
-                  KST, kf[(qq + 2) % 3]);
-        if constexpr (qq + 2 < 8)
-          lgkm_wait<4>(kf[qq % 3][0], kf[qq % 3][1]);
-        else if constexpr (qq + 1 < 8)
-          lgkm_wait<2>(kf[qq % 3][0], kf[qq % 3][1]);
-        else
-          lgkm_wait<0>(kf[qq % 3][0], kf[qq % 3][1]);
-        s_mfmas(std::integral_constant<int, qq / 2>{}, std::integral_constant<int, qq % 2>{}, kf[qq % 3], sn);
+      // weights of tile t: for D = 128 four quarters of 8 exps (the last one
+      // waits for phase 2, whose first half does not read it); otherwise
+      // exp pairs spread evenly over the K pairs
+      constexpr int NE = MB * NKB * 2;  // exp pairs per tile
+      static_for<NP>([&](auto qc) {
+        constexpr int qq = decltype(qc)::value;
+        if constexpr (qq + KLA < NP)
+          issue_k(std::integral_constant<int, (qq + KLA) / (NKB / 2)>{},
+                  std::integral_constant<int, (qq + KLA) % (NKB / 2)>{}, KST, kf[(qq + KLA) % (KLA + 1)]);
+        // pairs qq+1 .. min(qq+KLA, NP-1) may stay in flight
+        constexpr int kahead = (NP - 1 - qq) < KLA ? (NP - 1 - qq) : KLA;
+        lgkm_wait<2 * kahead>(kf[qq % (KLA + 1)][0], kf[qq % (KLA + 1)][1]);
+        s_mfmas(std::integral_constant<int, qq / (NKB / 2)>{}, std::integral_constant<int, qq % (NKB / 2)>{},
+                kf[qq % (KLA + 1)], sn);
         if constexpr (qq == 0) row_stats(I1);
         // (each finished fragment is pinned by an empty asm: the compiler
         // would otherwise sink the work to its use after the rescale branch)
-        if constexpr (qq == 1) { exp_quarter(I0, I0); asm volatile("" : "+v"(pc[0][0])); }
-        if constexpr (qq == 3) { exp_quarter(I0, I1); asm volatile("" : "+v"(pc[0][1])); }
-        if constexpr (qq == 5) { exp_quarter(I1, I0); asm volatile("" : "+v"(pc[1][0])); }
+        if constexpr (D == 128) {
+          if constexpr (qq == 1) { exp_quarter(I0, I0); asm volatile("" : "+v"(pc[0][0])); }
+          if constexpr (qq == 3) { exp_quarter(I0, I1); asm volatile("" : "+v"(pc[0][1])); }
+          if constexpr (qq == 5) { exp_quarter(I1, I0); asm volatile("" : "+v"(pc[1][0])); }
+        } else {
+          static_for<NE>([&](auto ec) {
+            constexpr int e = decltype(ec)::value;
+            if constexpr (qq == 1 + e * (NP - 1) / NE) {
+              exp_pair_pinned(std::integral_constant<int, e / (NKB * 2)>{},
+                              std::integral_constant<int, (e / 2) % NKB>{},
+                              std::integral_constant<int, e % 2>{});
+            }
+          });
+        }
         __builtin_amdgcn_sched_barrier(0);
       });
-      short4v vf[2][4];
-      issue_v(I0, VST, vf[0]);
-      if (__builtin_amdgcn_ballot_w64(any_move)) {  // rare after the first tiles
+      short4v vf[VLA + 1][4];
+      static_for<(VLA < NJ ? VLA : NJ)>([&](auto jc0) {
+        constexpr int j0 = decltype(jc0)::value;
+        issue_v(std::integral_constant<int, j0>{}, VST, vf[j0]);
+      });
+      if constexpr (!kAsmS) {
+        if (__builtin_amdgcn_ballot_w64(any_move)) {  // rare after the first tiles
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          l_acc[mb] *= alpha[mb];
+          for (int mb = 0; mb < MB; ++mb) {
+            l_acc[mb] *= alpha[mb];
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] *= alpha[mb];
+            for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] *= alpha[mb];
+          }
         }
       }
-      // -- phase 2: O^T += V^T P^T of tile t, q-block 1's last weights alongside
-      static_for<8>([&](auto jc) {
+      // -- phase 2: O^T += V^T P^T of tile t (D = 128: q-block 1's last
+      // weights alongside)
+      static_for<NJ>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
-        if constexpr (j + 1 < 8) issue_v(std::integral_constant<int, j + 1>{}, VST, vf[(j + 1) % 2]);
-        if constexpr (j == 0) { exp_quarter(I1, I1); asm volatile("" : "+v"(pc[1][1])); }
-        if constexpr (j + 1 < 8)
-          lgkm_wait<4>(vf[j % 2][0], vf[j % 2][1], vf[j % 2][2], vf[j % 2][3]);
-        else
-          lgkm_wait<0>(vf[j % 2][0], vf[j % 2][1], vf[j % 2][2], vf[j % 2][3]);
-        pv_mfmas(jc, vf[j % 2], pc);
-        if constexpr (j % 4 == 3) {
+        if constexpr (j + VLA < NJ)
+          issue_v(std::integral_constant<int, j + VLA>{}, VST, vf[(j + VLA) % (VLA + 1)]);
+        if constexpr (D == 128 && j == 0) { exp_quarter(I1, I1); asm volatile("" : "+v"(pc[1][1])); }
+        constexpr int vahead = (NJ - 1 - j) < VLA ? (NJ - 1 - j) : VLA;
+        constexpr int vs = j % (VLA + 1);
+        lgkm_wait<4 * vahead>(vf[vs][0], vf[vs][1], vf[vs][2], vf[vs][3]);
+        pv_mfmas(jc, vf[vs], pc);
+        if constexpr (!kAsmS && j % (NDT / 2) == NDT / 2 - 1) {
           static_for<2>([&](auto mbc) {
             constexpr int mb = decltype(mbc)::value;
-            l_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[mb][j / 4], l_acc[mb], 0, 0, 0);
+            l_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[mb][j / (NDT / 2)], l_acc[mb], 0, 0, 0);
           });
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -900,27 +1002,51 @@ void prefill_fwd_kernel(
     };
 
     // Q in registers before the first product (the compiler does not count
-    // the asm loads, so its own wait here covers every load in flight), and
-    // group 0 (K_0) landed in every wave
+    // the asm loads, so its own wait here covers every load in flight)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int kk = 0; kk < G::QREG; ++kk) asm volatile("" : : "v"(qf[mb][kk]));
+    // kAsmS: weights are exp2 of (score - reference) with a reference that
+    // never moves, so O^T is never rescaled (an in-loop rescale would give
+    // the AGPR accumulators VALU definitions, which the compiler resolves by
+    // copying them through VGPRs every iteration).  A weight can exceed 1 by
+    // at most 2^kFixedRefLimit, far inside fp32 and bf16 range.  If a row of
+    // the work-group rose further, the whole key loop runs a second time with
+    // every row's true maximum as its reference (all weights <= 1 then).
+    if constexpr (kAsmS) {
+      if (tid == 0) plan_s[0] = 0;  // redo flag (the plan is done with it)
+    }
+#pragma nounroll
+    for (int pass = 0;; ++pass) {
+    if (pass > 0) {  // second pass: state reset, first load groups again
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        m_ref[mb] = m_ref[mb] == -INFINITY ? m_ref[mb] : m_ref[mb] + fmaxf(dmax[mb], 0.f);
+        dmax[mb] = -INFINITY;
+        l_part[mb] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      dma_pl(kbase, kt0, kring);
+      dma_pl(kbase, kt0 + BN, kring + G::TILE_BYTES);
+      dma_pl(vbase, kt0, vring);
+    }
+    // group 0 (K_0) landed in every wave
     wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (ta == 0) {
-      static_for<4>([&](auto kkc) {
-        constexpr int kk = decltype(kkc)::value;
-        static_for<2>([&](auto kpc) {
+      static_for<QR>([&](auto kkc) {
+        static_for<NKB / 2>([&](auto kpc) {
           bf16x8 kf[2];
           issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
           lgkm_wait<0>(kf[0], kf[1]);
           s_mfmas(kkc, kpc, kf, sA);
         });
-        (void)kk;
       });
+      if constexpr (kAsmS) mfma_drain();  // the first step's VALU reads sA
     }
 
     constexpr std::integral_constant<int, 0> EVEN{};
@@ -932,23 +1058,50 @@ void prefill_fwd_kernel(
     }
     if (t < n) step(EVEN, t, sA, sB);
     wait_vmcnt<0>();  // nothing may still be writing LDS below
+    if constexpr (!kAsmS) {
+      break;
+    } else {
+      if (pass > 0) break;
+      bool rose = false;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) rose |= dmax[mb] * c_scale > kFixedRefLimit;
+      if (__builtin_amdgcn_ballot_w64(rose) && lane == 0) plan_s[0] = 1;
+      lds_barrier();
+      if (plan_s[0] == 0) break;
+    }
+    }  // pass
 
     // ---- epilogue: normalise, transpose through LDS, store whole rows --------
     // O^T fragments give each lane 4 head-dim values of one row, i.e. 8-byte
     // pieces of 16 rows per store; staging the wave's rows in LDS lets 16
-    // lanes write each 2*D-byte output row contiguously.  No barrier: once
-    // this wave is past the last iteration, every wave is past iteration
-    // n-2, and iteration n-1 reads neither K stage (n-1) % 2 nor V stage
-    // n % 2, and no load is still headed there.  Waves 0-1 stage in the
-    // former, waves 2-3 in the latter.
+    // lanes write each 2*D-byte output row contiguously.  D = 128: no
+    // barrier: once this wave is past the last iteration, every wave is past
+    // iteration n-2, and iteration n-1 reads neither K stage (n-1) % 2 nor V
+    // stage n % 2, and no load is still headed there; waves 0-1 stage in the
+    // former, waves 2-3 in the latter.  Larger D: one barrier, then each wave
+    // stages in its own quarter of the ring.
     {
-      static_assert(NW == 4 && 2 * G::WR * ROWB == TB, "two waves per free stage");
       constexpr int CPO = D / 8;  // 16-byte chunks per output row
-      const int free_stage = wave < 2 ? ((n - 1) & 1) * TB : 2 * TB + (n & 1) * TB;
-      unsigned char* ost = &ring[0][0] + free_stage + (wave & 1) * (G::WR * ROWB);
+      unsigned char* ost;
+      if constexpr (D == 128) {
+        static_assert(2 * G::WR * ROWB == TB, "two waves per free stage");
+        const int free_stage = wave < 2 ? ((n - 1) & 1) * TB : 2 * TB + (n & 1) * TB;
+        ost = &ring[0][0] + free_stage + (wave & 1) * (G::WR * ROWB);
+      } else {
+        static_assert(NW * G::WR * ROWB <= 4 * TB, "every wave's rows fit the ring");
+        lds_barrier();
+        ost = &ring[0][0] + wave * (G::WR * ROWB);
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const float l = l_acc[mb][0];
+        float l;
+        if constexpr (kAsmS) {
+          l = l_part[mb];
+          l += __shfl_xor(l, 16, 64);
+          l += __shfl_xor(l, 32, 64);
+        } else {
+          l = l_acc[mb][0];
+        }
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const int rr = mb * 16 + c16;  // row within the wave
 #pragma unroll

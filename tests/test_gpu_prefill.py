@@ -71,6 +71,26 @@ def test_prefill_small_ragged(d, dtype, mode):
         assert_close(got, want, dtype, "d=%d %s mode=%d W=%d" % (d, dtype, mode, W))
 
 
+@pytest.mark.parametrize("d", [128, 256, 512])
+@pytest.mark.parametrize("mode", [CAUSAL, BLOCKWISE])
+def test_prefill_odd_group(d, mode):
+    """Three query heads per kv head: work-groups that hold one query head
+    (the GQA pairing of heads needs an even group)."""
+    require_gpu()
+    rng = si.rng_for(900 + d + mode)
+    T, hkv, g = 301, 1, 3
+    cu = np.array([0, 150, 151, T], np.int32)
+    q = si.normal(rng, (T, hkv * g, d), "bf16")
+    k = si.normal(rng, (T, hkv, d), "bf16")
+    v = si.normal(rng, (T, hkv, d), "bf16")
+    ids = _ids_for(T, cu, 950 + d) if mode == BLOCKWISE else None
+    for W in (0, 45):
+        log("prefill odd group d=%d mode=%d W=%d" % (d, mode, W))
+        got = _run(q, k, v, cu, ids, W, mode, "bf16")
+        want = orc.prefill(q, k, v, cu, ids, W, mode)
+        assert_close(got, want, "bf16", "odd group d=%d mode=%d W=%d" % (d, mode, W))
+
+
 @pytest.mark.parametrize("d", [64, 128, 256, 512])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_window_one_is_exact(d, dtype):
@@ -88,11 +108,17 @@ def test_prefill_window_one_is_exact(d, dtype):
     np.testing.assert_array_equal(got, want)
 
 
-def test_prefill_needle_marks_window_edge():
+@pytest.mark.parametrize("d", [128, 256, 512])
+@pytest.mark.parametrize("strength", [40.0, 400.0])
+def test_prefill_needle_marks_window_edge(d, strength):
     """bf16 sharpness check: key j carries a strong needle; query rows that
-    may see it output ~v[j], rows just outside the window do not."""
+    may see it output ~v[j], rows just outside the window do not.  The
+    strong needle lifts a row's scores far above those of its first key
+    tile (by about 200 log2 units), which moves the reference maximum of the
+    D = 128 loop and makes the D >= 256 loop run its key loop a second time
+    with the true row maxima."""
     require_gpu()
-    d, hkv, g, W = 128, 1, 2, 64
+    hkv, g, W = 1, 2, 64
     T = 512
     rng = si.rng_for(5)
     qf = rng.standard_normal((T, hkv * g, d), dtype=np.float32) * 0.1
@@ -101,10 +127,12 @@ def test_prefill_needle_marks_window_edge():
     j = 200
     direction = np.ones(d, np.float32) / np.sqrt(d)
     qf[:, :, :] += 4.0 * direction
-    kf[j, 0, :] = 40.0 * direction
+    # the score scale is 1/sqrt(d): grow the needle with sqrt(d) so that it
+    # dominates its rows equally at every head size
+    kf[j, 0, :] = strength * np.sqrt(d / 128.0) * direction
     q, k, v = (si.f32_to_bf16_bits(x) for x in (qf, kf, vf))
     cu = np.array([0, T], np.int32)
-    log("prefill needle")
+    log("prefill needle d=%d strength=%g" % (d, strength))
     got_bits = _run(q, k, v, cu, None, W, CAUSAL, "bf16")
     want = orc.prefill(q, k, v, cu, None, W, CAUSAL)
     assert_close(got_bits, want, "bf16", "needle")
