@@ -230,17 +230,18 @@ struct PfTraits<float> {
   static constexpr int KW = 16;  // one 16-byte LDS read feeds 4 MFMAs of K=4
 };
 
-// Pipelined loop: LDS fragment lookahead (K fragment pairs, V^T fragment
-// groups) per head dimension.
+// Pipelined loop schedule per head dimension: LDS fragment lookahead (K
+// fragment pairs, V^T fragment groups requested ahead of their use) and the
+// tile loads issued per K fragment pair (DPP; 0 = all at the start of a
+// step).  A direct-to-LDS load costs the issuing wave about 40 cycles, so a
+// burst of 16 of them idles the matrix cores of a single-wave SIMD; spread
+// out, they issue while earlier products run.  D = 128 runs two waves per
+// SIMD, which hide the burst.  (Chosen by measurement on MI355X.)
 template <int D>
 struct PfLookahead {
-#ifndef SWA_PF_KLA
-  static constexpr int K = D == 128 ? 2 : 3;
-  static constexpr int V = D == 128 ? 1 : 2;
-#else
-  static constexpr int K = D == 128 ? 2 : SWA_PF_KLA;
-  static constexpr int V = D == 128 ? 1 : SWA_PF_VLA;
-#endif
+  static constexpr int K = 2;
+  static constexpr int V = 1;
+  static constexpr int DPP = D == 128 ? 0 : 2;
 };
 
 // Workgroup geometry.
@@ -486,11 +487,16 @@ void prefill_fwd_kernel(
   for (int i = 0; i < G::UPT; ++i) voff[i] = unit_off[i] * (int)sizeof(T);
   // one K or V tile (keys k0 .. k0+BN-1 of this kv head) into an LDS stage;
   // rows at or past Ttot fall outside the buffer and arrive as zeros
-  auto dma_pl = [&](const T* tb, int k0, uint32_t lds_stage) {
+  // descriptor of one K or V tile; `want` false gives an empty buffer, whose
+  // loads fetch nothing and fill their LDS slots with zeros
+  auto tile_rsrc = [&](const T* tb, int k0, bool want = true) {
     const T* p0 = tb + (size_t)k0 * kv_row_stride;
     const long long rem = (long long)(Ttot - k0) * (long long)kv_row_stride * (long long)sizeof(T);
-    const uint32_t nrec = rem <= 0 ? 0u : (rem > 0xffffffffLL ? 0xffffffffu : (uint32_t)rem);
-    const i32x4 rsrc = make_buffer_rsrc(p0, nrec);
+    const uint32_t nrec = (rem <= 0 || !want) ? 0u : (rem > 0xffffffffLL ? 0xffffffffu : (uint32_t)rem);
+    return make_buffer_rsrc(p0, nrec);
+  };
+  auto dma_pl = [&](const T* tb, int k0, uint32_t lds_stage) {
+    const i32x4 rsrc = tile_rsrc(tb, k0);
     const uint32_t lw = lds_stage + wave_u * G::UPT * 1024;
 #pragma unroll
     for (int i = 0; i < G::UPT; ++i) dma16_buf(rsrc, voff[i], lw + i * 1024);
@@ -689,6 +695,9 @@ void prefill_fwd_kernel(
     constexpr int NJ = NKS * (NDT / 2); // V^T fragment groups per tile (4 MFMAs each)
     // LDS fragment lookahead: K pairs and V groups requested ahead of use
     constexpr int KLA = PfLookahead<D>::K, VLA = PfLookahead<D>::V;
+    // tile loads issued per K fragment pair (0: all at the start of the step)
+    constexpr int DPP = PfLookahead<D>::DPP;
+    static_assert(DPP == 0 || DPP * NP >= 2 * G::UPT, "every load is issued in the step");
     static_assert(2 * KLA <= 15 && 4 * VLA <= 15, "lgkmcnt range");
     // D >= 256: score products by hand (VGPR accumulators, see mfma_bf16_vacc)
     // and row sums on the VALU, so that the AGPRs hold O^T alone
@@ -859,10 +868,31 @@ void prefill_fwd_kernel(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      // every wave is done with K_t and V_(t-1): refill their stages
-      if (t + 2 < n) dma_pl(kbase, kt0 + (t + 2) * BN, kring + par * TB);
-      if (t + 1 < n) dma_pl(vbase, kt0 + (t + 1) * BN, vring + ((par + 1) % 2) * TB);
-      if (!(t + 1 >= ta && t <= tb)) return;
+      // every wave is done with K_t and V_(t-1): refill their stages.  This
+      // wave's 2*UPT loads (V_(t+1) units, then K_(t+2) units) go out DPP
+      // per K fragment pair, so the vector memory queue never stalls the
+      // wave behind a burst (DPP = 0: all of them here)
+      // (a load that is not wanted gets an empty buffer instead of a branch:
+      // its stage is free, and branches here cost the accumulators their
+      // register assignment)
+      const bool kld = t + 2 < n, vld = t + 1 < n;
+      const i32x4 rs_k = tile_rsrc(kbase, kt0 + (t + 2) * BN, kld);
+      const i32x4 rs_v = tile_rsrc(vbase, kt0 + (t + 1) * BN, vld);
+      const uint32_t lw_k = kring + par * TB + wave_u * G::UPT * 1024;
+      const uint32_t lw_v = vring + ((par + 1) % 2) * TB + wave_u * G::UPT * 1024;
+      auto dma_unit = [&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (u < G::UPT) dma16_buf(rs_v, voff[u], lw_v + u * 1024);
+        else dma16_buf(rs_k, voff[u - G::UPT], lw_k + (u - G::UPT) * 1024);
+      };
+      if constexpr (DPP == 0) {
+        static_for<2 * G::UPT>(dma_unit);
+        if (!(t + 1 >= ta && t <= tb)) return;
+      }
+      // DPP > 0: a wave with no rows in tiles t and t+1 still runs the step
+      // (its loads are spread through it; a branch around them would cost
+      // the accumulators their registers): every score of such a tile is
+      // masked, so its weights are 0 against finite V rows
       const bool a_cur = t >= ta && t <= tb;
       mask(t, a_cur, sc);
 
@@ -938,6 +968,12 @@ void prefill_fwd_kernel(
       constexpr int NE = MB * NKB * 2;  // exp pairs per tile
       static_for<NP>([&](auto qc) {
         constexpr int qq = decltype(qc)::value;
+        if constexpr (DPP > 0) {
+          static_for<DPP>([&](auto ic) {
+            constexpr int u = qq * DPP + decltype(ic)::value;
+            if constexpr (u < 2 * G::UPT) dma_unit(std::integral_constant<int, u>{});
+          });
+        }
         if constexpr (qq + KLA < NP)
           issue_k(std::integral_constant<int, (qq + KLA) / (NKB / 2)>{},
                   std::integral_constant<int, (qq + KLA) % (NKB / 2)>{}, KST, kf[(qq + KLA) % (KLA + 1)]);
