@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/swa.h"
 #include "swa_internal.h"
 
@@ -39,6 +41,23 @@ int check_ring(int32_t window, int32_t batch, int32_t ring_rows, int32_t hkv,
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
 
 }  // namespace
+
+namespace swa {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace swa
 
 extern "C" {
 

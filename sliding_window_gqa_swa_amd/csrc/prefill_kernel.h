@@ -241,7 +241,7 @@ template <int D>
 struct PfLookahead {
   static constexpr int K = 2;
   static constexpr int V = 1;
-  static constexpr int DPP = D == 128 ? 0 : 2;
+  static constexpr int DPP = D == 128 ? 1 : 2;
 };
 
 // Workgroup geometry.
@@ -298,18 +298,33 @@ __device__ __forceinline__ int tile_cost_bucket(const int* cu_s, int ndocs, int 
   return min(r1 / BN - lo / BN + 1, kPlanBuckets - 1);
 }
 
-// Longest-first order of one XCD's slice of work [w0, w0 + P): returns the
-// offset in the slice of the item at sorted position `pos` (descending cost
-// bucket, ties by ascending offset).  Blocks of one XCD are dispatched in
-// ascending `pos` as CUs free up, so this is list scheduling with the
-// longest items first, which keeps the tail of the grid short when item
-// costs vary (causal tiles of many documents).  A counting sort: bucket of
-// every item (kept in `bk`, P bytes), histogram, the bucket holding `pos`,
-// then the rank inside that bucket by a block-wide scan.  Deterministic.
-// Called by all NT threads; ends with a barrier.
+// Inclusive prefix sum over the 64 lanes of a wave, by DPP row shifts and
+// row broadcasts (no LDS traffic: the plan runs next to another
+// work-group's key loop, which keeps the LDS busy).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Longest-first order of one XCD's slice of work [w0, w0 + P): the offsets
+// in the slice of the items at sorted positions pos[0] and pos[1] (sorted
+// by descending cost bucket, ties by ascending offset; a position >= P
+// gives -1).  Blocks take their items in ascending position, so this is
+// list scheduling with the longest items first, which keeps the tail of
+// the grid short when item costs vary (causal tiles of many documents).  A
+// counting sort: bucket of every item (kept in `bk`, P bytes), histogram,
+// the bucket holding each position, then the rank inside that bucket by a
+// block-wide scan.  Deterministic.  Called by all NT threads; ends with a
+// barrier.  sel_s: 6 ints, wsum_s: 2 * NT / 64 ints.
 template <int NT, int BM, int BN>
-__device__ int lpt_slot(const int* cu_s, int ndocs, int Ttot, int W, int ntiles, int w0, int P,
-                        int pos, unsigned char* bk, int* hist_s, int* wsum_s, int* sel_s) {
+__device__ void lpt_select(const int* cu_s, int ndocs, int Ttot, int W, int ntiles, int w0, int P,
+                           const int (&pos)[2], unsigned char* bk, int* hist_s, int* wsum_s,
+                           int* sel_s, int (&out)[2]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NWV = NT / 64;
   for (int i = tid; i < P; i += NT) {
@@ -318,8 +333,9 @@ __device__ int lpt_slot(const int* cu_s, int ndocs, int Ttot, int W, int ntiles,
     bk[i] = (unsigned char)c;
     atomicAdd(&hist_s[c], 1);
   }
+  if (tid < 6) sel_s[tid] = -1;
   __syncthreads();
-  if (wave == 0) {  // bucket holding position pos, scanning buckets high to low
+  if (wave == 0) {  // bucket holding each position, scanning buckets high to low
     static_assert(kPlanBuckets == 4 * 64, "four buckets per lane");
     int n[4], sum = 0;
 #pragma unroll
@@ -327,48 +343,56 @@ __device__ int lpt_slot(const int* cu_s, int ndocs, int Ttot, int W, int ntiles,
       n[j] = hist_s[kPlanBuckets - 1 - 4 * lane - j];
       sum += n[j];
     }
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    int start = incl - sum;
+    int start = wave_incl_scan(sum) - sum;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (pos >= start && pos < start + n[j]) {
-        sel_s[0] = kPlanBuckets - 1 - 4 * lane - j;
-        sel_s[1] = pos - start;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        if (pos[x] >= start && pos[x] < start + n[j]) {
+          sel_s[2 * x] = kPlanBuckets - 1 - 4 * lane - j;
+          sel_s[2 * x + 1] = pos[x] - start;
+        }
       }
       start += n[j];
     }
   }
   __syncthreads();
-  const int tb = sel_s[0], tr = sel_s[1];
   const int chunk = (P + NT - 1) / NT;
   const int i0 = min(tid * chunk, P), i1 = min(i0 + chunk, P);
-  int cnt = 0;
-  for (int i = i0; i < i1; ++i) cnt += bk[i] == tb;
-  int incl = cnt;
+  int tb[2], tr[2], cnt[2], incl[2];
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
+  for (int x = 0; x < 2; ++x) {
+    tb[x] = sel_s[2 * x];
+    tr[x] = sel_s[2 * x + 1];
+    cnt[x] = 0;
   }
-  if (lane == 63) wsum_s[wave] = incl;
-  __syncthreads();
-  int before = incl - cnt;
-  for (int w = 0; w < NWV; ++w) before += w < wave ? wsum_s[w] : 0;
-  if (tr >= before && tr < before + cnt) {
-    int r = tr - before;
-    for (int i = i0; i < i1; ++i)
-      if (bk[i] == tb) {
-        if (r == 0) sel_s[2] = i;
-        --r;
-      }
+  for (int i = i0; i < i1; ++i) {
+    const int c = bk[i];
+    cnt[0] += c == tb[0];
+    cnt[1] += c == tb[1];
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    incl[x] = wave_incl_scan(cnt[x]);
+    if (lane == 63) wsum_s[x * NWV + wave] = incl[x];
   }
   __syncthreads();
-  return min(max(sel_s[2], 0), P - 1);
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    int before = incl[x] - cnt[x];
+    for (int w = 0; w < NWV; ++w) before += w < wave ? wsum_s[x * NWV + w] : 0;
+    if (tb[x] >= 0 && tr[x] >= before && tr[x] < before + cnt[x]) {
+      int r = tr[x] - before;
+      for (int i = i0; i < i1; ++i)
+        if (bk[i] == tb[x]) {
+          if (r == 0) sel_s[4 + x] = i;
+          --r;
+        }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 2; ++x) out[x] = pos[x] < P ? min(max(sel_s[4 + x], 0), P - 1) : -1;
 }
 
 template <int D, typename T, int MB, int BN, int NW, int GH, bool PL>
@@ -377,7 +401,7 @@ void prefill_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ cu, int ndocs, const int32_t* __restrict__ ids,
     int W, int mode, T* __restrict__ out, int Ttot, int hq, int hkv,
-    float qk_scale_log2, int ntiles, int nwork, int work_per_xcd) {
+    float qk_scale_log2, int ntiles, int nwork, int work_per_xcd, int slots_per_xcd) {
   using G = PfGeom<D, T, MB, BN, NW, GH, PL>;
   using TR = typename G::TR;
   constexpr bool kF32 = std::is_same<T, float>::value;
@@ -389,7 +413,7 @@ void prefill_fwd_kernel(
   __shared__ int ext_end_s, de_last_s;
   __shared__ int cu_s[kCuCache];
   __shared__ int hist_s[kPlanBuckets];
-  __shared__ int plan_s[3 + NW];
+  __shared__ int plan_s[6 + 2 * NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -404,6 +428,7 @@ void prefill_fwd_kernel(
   const int b = (int)blockIdx.x;
   const int w0 = (b & 7) * work_per_xcd;
   const int P = min(work_per_xcd, nwork - w0);
+  constexpr bool kTwoItems = PL;
   const int pos = b >> 3;
   if (pos >= P) return;  // uniform per block
   // cu_seqlens -> LDS with one cooperative load (one memory latency instead
@@ -412,13 +437,37 @@ void prefill_fwd_kernel(
   if (cu_in_lds)
     for (int d = tid; d <= ndocs; d += G::NT) cu_s[d] = cu[d];
   const bool plan = cu_in_lds && P > 1 && P <= kPlanMaxItems;
+  // Pipelined path: S = slots_per_xcd work-groups per XCD with at most two
+  // items each: the sorted positions pos and 2S-1-pos, so the longest items
+  // are paired with the shortest and run back to back (one launch ramp, one
+  // cu_seqlens load and one plan for both).
+  const int S = kTwoItems ? min(slots_per_xcd, P) : P;
+  const int pos2 = kTwoItems ? 2 * S - 1 - pos : P;
+  int items[2] = {pos, pos2 < P ? pos2 : -1};
   if (plan)
     for (int c = tid; c < kPlanBuckets; c += G::NT) hist_s[c] = 0;
-  __syncthreads();
-  const int work = w0 + (plan ? lpt_slot<G::NT, G::BM, BN>(cu_s, ndocs, Ttot, W, ntiles, w0, P,
-                                                           pos, &ring[0][0], hist_s, plan_s + 3,
-                                                           plan_s)
-                              : pos);
+  __syncthreads();  // cu_s and the histogram are ready
+  if (plan) {
+    const int posv[2] = {pos, pos2};
+    lpt_select<G::NT, G::BM, BN>(cu_s, ndocs, Ttot, W, ntiles, w0, P, posv, &ring[0][0], hist_s,
+                                 plan_s + 6, plan_s, items);
+  }
+#pragma nounroll
+  for (int kq = 0; kq < 2; ++kq) {
+  if (items[kq] < 0) break;
+  if (kq > 0) __syncthreads();  // the first item is done with every LDS buffer
+  const int work = w0 + items[kq];
+  [&]() __attribute__((always_inline)) {
+  // lane-derived values are recomputed per item from an opaque copy of the
+  // thread index: hoisted out of the item loop they would stay live across
+  // it and spill the key loop's registers
+  int tid_o = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid_o));
+  const int tid = tid_o;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c16 = lane & 15;
+  const int grp = lane >> 4;
   const int hg_index = work / ntiles;
   const int tile = ntiles - 1 - (work - hg_index * ntiles);  // heavy tiles first
   const int q0 = tile * G::BM;
@@ -531,6 +580,8 @@ void prefill_fwd_kernel(
       qf[mb][kk] = x;
     }
   }
+  // pipelined D = 128: fixed per-row softmax reference, Q scaled once
+  constexpr bool kDiagRef = PL && D == 128;
 
   // ---- prologue: per-row key interval [lo_i, hi_i] ------------------------
   int my_de = 0;
@@ -769,6 +820,10 @@ void prefill_fwd_kernel(
     }
 
     floatx4 o_acc[MB][NDT], l_acc[MB];
+    // kDiagRef: every S^T product chain starts from minus the row's
+    // reference, so the accumulator already holds the exp2 argument
+    floatx4 s_init[MB];
+    bool ref_ok[MB];  // kDiagRef: the row has its reference (rows past the end need none)
     float m_ref[MB], l_part[MB];  // l_part: this lane's share of the row sum (kAsmS)
     float dmax[MB];               // kAsmS: rise of later tile maxima above m_ref
 #pragma unroll
@@ -777,6 +832,7 @@ void prefill_fwd_kernel(
       dmax[mb] = -INFINITY;
       l_part[mb] = 0.f;
       l_acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      s_init[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
@@ -823,8 +879,7 @@ void prefill_fwd_kernel(
             else mfma_bf16_vacc(sn[mb][kb], kf[decltype(ic)::value], qf[mb][kk]);
           } else {
             sn[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                kf[decltype(ic)::value], qf[mb][kk], kk == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : sn[mb][kb],
-                0, 0, 0);
+                kf[decltype(ic)::value], qf[mb][kk], kk == 0 ? s_init[mb] : sn[mb][kb], 0, 0, 0);
           }
         });
       });
@@ -859,7 +914,7 @@ void prefill_fwd_kernel(
     floatx4 sA[MB][NKB], sB[MB][NKB];
 
     // one iteration (t of parity par): scores of tile t in sc, of t+1 into sn
-    auto step = [&](auto parc, int t, floatx4 (&sc)[MB][NKB], floatx4 (&sn)[MB][NKB]) {
+    auto step = [&](auto parc, int t, floatx4 (&sc)[MB][NKB], floatx4 (&sn)[MB][NKB]) __attribute__((always_inline)) {
       constexpr int par = decltype(parc)::value;
       constexpr std::integral_constant<int, ((par + 1) % 2) * TB> KST{};  // K stage of tile t+1
       constexpr std::integral_constant<int, par * TB> VST{};              // V stage of tile t
@@ -895,12 +950,39 @@ void prefill_fwd_kernel(
       // masked, so its weights are 0 against finite V rows
       const bool a_cur = t >= ta && t <= tb;
       mask(t, a_cur, sc);
+      if constexpr (kDiagRef) {
+        // rows without a reference: their tile-t scores started from 0; the
+        // maximum of their allowed scores here becomes the reference, the
+        // scores are shifted by it, and the products issued from now on start
+        // from minus it (wave-uniform branch, taken in a row's first tiles)
+        bool need = false;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) need |= !ref_ok[mb];
+        if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sc[mb][kb][r]);
+            tmax = max_over_lane_groups(tmax);
+            if (!ref_ok[mb] && tmax != -INFINITY) {
+              ref_ok[mb] = true;
+              s_init[mb] = floatx4{-tmax, -tmax, -tmax, -tmax};
+#pragma unroll
+              for (int kb = 0; kb < NKB; ++kb) sc[mb][kb] -= tmax;
+            }
+          }
+        }
+      }
 
       // -- phase 1: S^T of tile t+1 with the softmax of tile t --------------------
       float alpha[MB], mc[MB];
       bool any_move = false;
       auto row_stats = [&](auto mbc) {
         constexpr int mb = decltype(mbc)::value;
+        if constexpr (kDiagRef) return;  // fixed reference, no row statistics
         float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -926,8 +1008,14 @@ void prefill_fwd_kernel(
       // weights of keys kb*16 + 4 grp + (2 rp, 2 rp + 1) of q-block mb
       auto exp_pair = [&](auto mbc, auto kbc, auto rpc) {
         constexpr int mb = decltype(mbc)::value, kb = decltype(kbc)::value, rp = decltype(rpc)::value;
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp], c_scale, -mc[mb]));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp + 1], c_scale, -mc[mb]));
+        float e0, e1;
+        if constexpr (kDiagRef) {  // the accumulator holds s*c - reference
+          e0 = __builtin_amdgcn_exp2f(sc[mb][kb][2 * rp]);
+          e1 = __builtin_amdgcn_exp2f(sc[mb][kb][2 * rp + 1]);
+        } else {
+          e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp], c_scale, -mc[mb]));
+          e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp + 1], c_scale, -mc[mb]));
+        }
         const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
         pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp] = b0;
         pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp + 1] = b1;
@@ -1006,7 +1094,7 @@ void prefill_fwd_kernel(
         constexpr int j0 = decltype(jc0)::value;
         issue_v(std::integral_constant<int, j0>{}, VST, vf[j0]);
       });
-      if constexpr (!kAsmS) {
+      if constexpr (!kAsmS && !kDiagRef) {
         if (__builtin_amdgcn_ballot_w64(any_move)) {  // rare after the first tiles
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
@@ -1043,6 +1131,31 @@ void prefill_fwd_kernel(
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int kk = 0; kk < G::QREG; ++kk) asm volatile("" : : "v"(qf[mb][kk]));
+    // kDiagRef: Q is scaled by c = scale * log2(e) once (rounded to bf16,
+    // the operand the products use), so scores are in log2 units.  A row's
+    // softmax reference is the maximum of its scores in the first key tile
+    // that holds an allowed key for it, and never moves afterwards: the loop
+    // needs no row maximum, no exp2 argument arithmetic (every product
+    // chain of a row starts from minus its reference) and no rescale of
+    // O^T.  The largest weight of a row is at least 1, so its sum never
+    // underflows; weights above 1 are kept as they are.  A row whose later
+    // scores rise so far above the reference that its sum or output leaves
+    // the safe range is caught after the loop, and the work-group then
+    // computes the true row maxima and runs the key loop again with those.
+    if constexpr (kDiagRef) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int kk = 0; kk < G::QREG; ++kk) {
+          bf16x8 x = qf[mb][kk];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = (__bf16)((float)x[e] * c_scale);
+          qf[mb][kk] = x;
+        }
+        ref_ok[mb] = !(row_i[mb] < Ttot && row_lo[mb] != 0x3fffffff);
+      }
+      if (tid == 0) plan_s[0] = 0;  // redo flag (the plan is done with it)
+    }
     // kAsmS: weights are exp2 of (score - reference) with a reference that
     // never moves, so O^T is never rescaled (an in-loop rescale would give
     // the AGPR accumulators VALU definitions, which the compiler resolves by
@@ -1053,59 +1166,129 @@ void prefill_fwd_kernel(
     if constexpr (kAsmS) {
       if (tid == 0) plan_s[0] = 0;  // redo flag (the plan is done with it)
     }
-#pragma nounroll
-    for (int pass = 0;; ++pass) {
-    if (pass > 0) {  // second pass: state reset, first load groups again
+    // group 0 (K_0) landed in every wave; the key loop of the work-group
+    auto key_loop = [&]() __attribute__((always_inline)) {
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (ta == 0) {
+        static_for<QR>([&](auto kkc) {
+          static_for<NKB / 2>([&](auto kpc) {
+            bf16x8 kf[2];
+            issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
+            lgkm_wait<0>(kf[0], kf[1]);
+            s_mfmas(kkc, kpc, kf, sA);
+          });
+        });
+        if constexpr (kAsmS) mfma_drain();  // the first step's VALU reads sA
+      }
+      constexpr std::integral_constant<int, 0> EVEN{};
+      constexpr std::integral_constant<int, 1> ODD{};
+      int t = 0;
+      for (; t + 1 < n; t += 2) {
+        step(EVEN, t, sA, sB);
+        step(ODD, t + 1, sB, sA);
+      }
+      if (t < n) step(EVEN, t, sA, sB);
+      wait_vmcnt<0>();  // nothing may still be writing LDS below
+    };
+    // second pass: accumulators cleared, first load groups again
+    auto restart = [&]() {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         m_ref[mb] = m_ref[mb] == -INFINITY ? m_ref[mb] : m_ref[mb] + fmaxf(dmax[mb], 0.f);
         dmax[mb] = -INFINITY;
         l_part[mb] = 0.f;
+        l_acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
       dma_pl(kbase, kt0, kring);
       dma_pl(kbase, kt0 + BN, kring + G::TILE_BYTES);
       dma_pl(vbase, kt0, vring);
-    }
-    // group 0 (K_0) landed in every wave
-    wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (ta == 0) {
-      static_for<QR>([&](auto kkc) {
-        static_for<NKB / 2>([&](auto kpc) {
-          bf16x8 kf[2];
-          issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
-          lgkm_wait<0>(kf[0], kf[1]);
-          s_mfmas(kkc, kpc, kf, sA);
-        });
-      });
-      if constexpr (kAsmS) mfma_drain();  // the first step's VALU reads sA
-    }
-
-    constexpr std::integral_constant<int, 0> EVEN{};
-    constexpr std::integral_constant<int, 1> ODD{};
-    int t = 0;
-    for (; t + 1 < n; t += 2) {
-      step(EVEN, t, sA, sB);
-      step(ODD, t + 1, sB, sA);
-    }
-    if (t < n) step(EVEN, t, sA, sB);
-    wait_vmcnt<0>();  // nothing may still be writing LDS below
-    if constexpr (!kAsmS) {
-      break;
-    } else {
-      if (pass > 0) break;
-      bool rose = false;
+    };
+    if constexpr (kDiagRef) {
+      // (two inlined copies of the key loop rather than a loop over passes:
+      // a loop would keep the first pass's registers live across its back
+      // edge and spill)
+      key_loop();
+      // safe range: row sums below 2^64 and finite outputs (any inf or NaN
+      // in O^T makes the sum of its entries non-finite)
+      bool bad = false;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) rose |= dmax[mb] * c_scale > kFixedRefLimit;
-      if (__builtin_amdgcn_ballot_w64(rose) && lane == 0) plan_s[0] = 1;
+      for (int mb = 0; mb < MB; ++mb) {
+        float osum = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          osum += (o_acc[mb][dt][0] + o_acc[mb][dt][1]) + (o_acc[mb][dt][2] + o_acc[mb][dt][3]);
+        bad |= !(l_acc[mb][0] < 0x1p64f) || !(__builtin_fabsf(osum) < INFINITY);
+      }
+      if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) plan_s[0] = 1;
       lds_barrier();
-      if (plan_s[0] == 0) break;
+      if (plan_s[0] != 0) {
+        // true row maxima of the scaled scores, one K tile at a time
+        float mtrue[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          mtrue[mb] = -INFINITY;
+          s_init[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int tt = 0; tt < n; ++tt) {
+          dma_pl(kbase, kt0 + tt * BN, kring);
+          wait_vmcnt<0>();
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if (tt >= ta && tt <= tb) {
+            static_for<QR>([&](auto kkc) {
+              static_for<NKB / 2>([&](auto kpc) {
+                bf16x8 kf[2];
+                issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
+                lgkm_wait<0>(kf[0], kf[1]);
+                s_mfmas(kkc, kpc, kf, sA);
+              });
+            });
+            mask(tt, true, sA);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+              float tmax = -INFINITY;
+#pragma unroll
+              for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sA[mb][kb][r]);
+              mtrue[mb] = fmaxf(mtrue[mb], max_over_lane_groups(tmax));
+            }
+          }
+          lds_barrier();  // every wave is done with the stage before it is refilled
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const float m = mtrue[mb] == -INFINITY ? 0.f : mtrue[mb];
+          s_init[mb] = floatx4{-m, -m, -m, -m};
+          ref_ok[mb] = true;
+        }
+        restart();
+        key_loop();
+      }
+    } else {
+#pragma nounroll
+      for (int pass = 0;; ++pass) {
+        if (pass > 0) restart();
+        key_loop();
+        if constexpr (!kAsmS) {
+          break;
+        } else {
+          if (pass > 0) break;
+          bool rose = false;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) rose |= dmax[mb] * c_scale > kFixedRefLimit;
+          if (__builtin_amdgcn_ballot_w64(rose) && lane == 0) plan_s[0] = 1;
+          lds_barrier();
+          if (plan_s[0] == 0) break;
+        }
+      }
     }
-    }  // pass
 
     // ---- epilogue: normalise, transpose through LDS, store whole rows --------
     // O^T fragments give each lane 4 head-dim values of one row, i.e. 8-byte
@@ -1372,6 +1555,9 @@ void prefill_fwd_kernel(
       }
     }
   }
+  }();  // one work item
+  if constexpr (!kTwoItems) break;
+  }  // items of this work-group
 }
 
 }  // namespace swa

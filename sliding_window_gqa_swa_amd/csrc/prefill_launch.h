@@ -4,6 +4,8 @@
 #include "prefill_kernel.h"
 #include "swa_internal.h"
 
+#include <algorithm>
+
 namespace swa {
 
 template <int D, typename T, int MB, int BN, int NW, int GH, bool PL = false>
@@ -17,10 +19,20 @@ int launch_prefill_cfg(const void* q, const void* k, const void* v,
   const long long nwork = (long long)ntiles * hkv * (g / GH);
   const long long per_xcd = (nwork + 7) / 8;  // 8 XCDs, blocks round-robin over them
   if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL>), dim3((unsigned)(8 * per_xcd)),
+  // the pipelined kernel runs up to two items per work-group: as many
+  // work-groups per XCD as its CUs hold at once (the kernel's occupancy), or
+  // half the items when there are more
+  int slots = (int)per_xcd;
+  if (PL) {
+    constexpr int kWgPerCu = (NW == 4 && D <= 128 && !std::is_same<T, float>::value) ? 2 : 1;
+    const long long fill = (long long)kWgPerCu * (device_cu_count() / 8);
+    slots = (int)std::min<long long>(per_xcd, std::max<long long>(fill, (per_xcd + 1) / 2));
+    slots = std::max(slots, 1);
+  }
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL>), dim3((unsigned)(8 * slots)),
                      dim3(G::NT), 0, stream, (const T*)q, (const T*)k, (const T*)v, cu,
                      num_docs, ids, window, mode, (T*)out, total_tokens, hq, hkv,
-                     scale * kPrefillLog2e, ntiles, (int)nwork, (int)per_xcd);
+                     scale * kPrefillLog2e, ntiles, (int)nwork, (int)per_xcd, slots);
   return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
 }
 

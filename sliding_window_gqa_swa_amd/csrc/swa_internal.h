@@ -37,6 +37,9 @@ int launch_decode(const void* q, const void* k_ring, const void* v_ring,
                   float scale, void* workspace, const DecodePlan& plan,
                   hipStream_t stream);
 
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 // Prefill.
 int launch_prefill(const void* q, const void* k, const void* v,
                    const int32_t* cu, const int32_t* ids, int window,
