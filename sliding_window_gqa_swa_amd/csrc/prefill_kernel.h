@@ -401,7 +401,8 @@ void prefill_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ cu, int ndocs, const int32_t* __restrict__ ids,
     int W, int mode, T* __restrict__ out, int Ttot, int hq, int hkv,
-    float qk_scale_log2, int ntiles, int nwork, int work_per_xcd, int slots_per_xcd) {
+    float qk_scale_log2, int ntiles, int nwork, int work_per_xcd, int slots_per_xcd,
+    int colocated) {
   using G = PfGeom<D, T, MB, BN, NW, GH, PL>;
   using TR = typename G::TR;
   constexpr bool kF32 = std::is_same<T, float>::value;
@@ -442,7 +443,16 @@ void prefill_fwd_kernel(
   // are paired with the shortest and run back to back (one launch ramp, one
   // cu_seqlens load and one plan for both).
   const int S = kTwoItems ? min(slots_per_xcd, P) : P;
-  const int pos2 = kTwoItems ? 2 * S - 1 - pos : P;
+  int pos2 = kTwoItems ? 2 * S - 1 - pos : P;
+  if (kTwoItems && colocated && S == slots_per_xcd && (S & 1) == 0) {
+    // Every CU of the XCD holds two of its work-groups, w and w + S/2 (the
+    // dispatcher fills each CU's first slot, then its second), and the
+    // earlier one's waves win issue while both run (about 1.5x its
+    // partner's rate, measured): the earlier work-group takes the heavier
+    // second items, so that both finish together.
+    const int hs = S >> 1;
+    pos2 = pos < hs ? 3 * hs - 1 - pos : 4 * hs - 1 - (pos - hs);
+  }
   int items[2] = {pos, pos2 < P ? pos2 : -1};
   if (plan)
     for (int c = tid; c < kPlanBuckets; c += G::NT) hist_s[c] = 0;

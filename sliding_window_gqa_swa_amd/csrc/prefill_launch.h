@@ -22,17 +22,18 @@ int launch_prefill_cfg(const void* q, const void* k, const void* v,
   // the pipelined kernel runs up to two items per work-group: as many
   // work-groups per XCD as its CUs hold at once (the kernel's occupancy), or
   // half the items when there are more
-  int slots = (int)per_xcd;
+  int slots = (int)per_xcd, colocated = 0;
   if (PL) {
     constexpr int kWgPerCu = (NW == 4 && D <= 128 && !std::is_same<T, float>::value) ? 2 : 1;
     const long long fill = (long long)kWgPerCu * (device_cu_count() / 8);
     slots = (int)std::min<long long>(per_xcd, std::max<long long>(fill, (per_xcd + 1) / 2));
     slots = std::max(slots, 1);
+    colocated = kWgPerCu == 2 && slots == fill;  // two work-groups on every CU
   }
   hipLaunchKernelGGL((prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL>), dim3((unsigned)(8 * slots)),
                      dim3(G::NT), 0, stream, (const T*)q, (const T*)k, (const T*)v, cu,
                      num_docs, ids, window, mode, (T*)out, total_tokens, hq, hkv,
-                     scale * kPrefillLog2e, ntiles, (int)nwork, (int)per_xcd, slots);
+                     scale * kPrefillLog2e, ntiles, (int)nwork, (int)per_xcd, slots, colocated);
   return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
 }
 
