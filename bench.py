@@ -143,12 +143,15 @@ def bench_prefill(name, steps, warmup, torch, api, nsets=None):
         api.prefill(sets[s][0], sets[s][1], sets[s][2], cu, ids, c.window, c.mode, out=outs[s])
 
     ms = time_loop(step, steps, warmup, torch)
+    # warm: one input set every call (K/V and Q stay in the Infinity Cache)
+    warm_ms = time_loop(lambda i: step(0), steps, warmup, torch)
     fl = useful_flops(c)
     return {
         "workload": name, "T": c.T, "docs": int(c.cu_seqlens.size - 1), "hq": c.hq,
         "hkv": c.hkv, "d": c.d, "window": c.window,
         "mask": "blockwise" if c.mode == si.BLOCKWISE else "causal",
         "useful_flop": fl, "ms_per_call": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+        "ms_per_call_warm": warm_ms, "tflops_warm": fl / (warm_ms * 1e-3) / 1e12,
         "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "input_sets": nsets,
     }
@@ -257,6 +260,101 @@ def cpu_baseline(budget_s=15.0):
     }
 
 
+def record_traffic(fetch_dir, write_dir, kernel="prefill_fwd_kernel", workload=HEADLINE):
+    """Write profiles/traffic.json from two rocprofv3 --pmc runs of
+    `bench.py --only-headline --copy-calibration` (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch).  Each counter is scaled by what it reads
+    for the 512 MiB device copy of the same run (known bytes)."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        vals, calib = {}, {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Dispatch_Id"], r["Kernel_Name"])
+                tgt = vals if kernel in r["Kernel_Name"] else (
+                    calib if "copyBuffer" in r["Kernel_Name"] else None)
+                if tgt is not None:
+                    tgt[key] = tgt.get(key, 0.0) + float(r["Counter_Value"])
+        return list(vals.values()), max(calib.values()) if calib else None
+
+    fetch, fcal = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write, wcal = per_dispatch(write_dir, "WRITE_SIZE")
+    if not fetch or not write or not fcal or not wcal:
+        raise SystemExit("counter files lack the kernel or the copy calibration")
+    copy_kib = 512 * 1024.0
+    fs, ws = copy_kib / fcal, copy_kib / wcal
+    c = si.PREFILL_WORKLOADS[workload]()
+    q, k, v = c.tensors("bf16")
+    alg = q.nbytes + k.nbytes + v.nbytes + q.nbytes  # q, k, v read once; out (q-sized) written once
+    fb = float(np.mean(fetch)) * 1024 * fs
+    wb = float(np.mean(write)) * 1024 * ws
+    rec = {
+        "workload": workload, "kernel": kernel,
+        "fetch_kib_raw": float(np.mean(fetch)), "write_kib_raw": float(np.mean(write)),
+        "fetch_kib_min_max": [float(np.min(fetch)), float(np.max(fetch))],
+        "dispatches": [len(fetch), len(write)],
+        "copy_fetch_kib": fcal, "copy_write_kib": wcal,
+        "fetch_scale": fs, "write_scale": ws,
+        "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
+        "bytes_per_launch": int(fb + wb), "algorithmic_bytes_per_launch": int(alg),
+        "sources_sha256": sources_hash(kernel),
+    }
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            allrec = json.load(fh)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[kernel] = rec
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allrec, fh, indent=2)
+        fh.write("\n")
+    print(json.dumps(rec, indent=2))
+
+
+def summarize_trace(trace_dir):
+    """Per-kernel table (markdown) from a `rocprofv3 --kernel-trace` database
+    under trace_dir: calls, total / average / min / max duration, grouped by
+    kernel and grid size."""
+    import glob
+    import re
+    import sqlite3
+    dbs = glob.glob(os.path.join(trace_dir, "**", "*.db"), recursive=True)
+    if not dbs:
+        raise SystemExit("no rocprofv3 database under %s" % trace_dir)
+    cur = sqlite3.connect(dbs[0]).cursor()
+    rows = cur.execute(
+        "select name, grid_x, workgroup_x, count(*), sum(duration), avg(duration), "
+        "min(duration), max(duration) from kernels group by name, grid_x "
+        "order by sum(duration) desc").fetchall()
+    tot = sum(r[4] for r in rows) or 1
+
+    def short(nm):
+        m = re.search(r"prefill_fwd_kernelILi(\d+)E(DF16b|f)Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)", nm)
+        if m:
+            return "prefill_fwd_kernel<D=%s,%s,MB=%s,BN=%s,NW=%s,GH=%s%s>" % (
+                m.group(1), "bf16" if m.group(2) == "DF16b" else "f32", m.group(3), m.group(4),
+                m.group(5), m.group(6), ",pipelined" if m.group(7) == "1" else "")
+        m = re.search(r"decode_split_kernelILi(\d+)E(DF16b|f)Li(\d+)E", nm)
+        if m:
+            return "decode_split_kernel<D=%s,%s,GB=%s>" % (
+                m.group(1), "bf16" if m.group(2) == "DF16b" else "f32", m.group(3))
+        m = re.search(r"(ring_\w+_kernel)", nm)
+        if m:
+            return m.group(1)
+        return nm.split("(")[0].replace("void ", "")[:48]
+
+    print("| kernel | grid (threads) | calls | total us | avg us | min us | max us | % |")
+    print("|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print("| %s | %d | %d | %.1f | %.2f | %.2f | %.2f | %.1f |" % (
+            short(r[0]), r[1], r[3], r[4] / 1e3, r[5] / 1e3, r[6] / 1e3, r[7] / 1e3,
+            100.0 * r[4] / tot))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,7 +365,19 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy 4 times (known bytes, for "
                          "scaling HBM counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc output "
+                         "directories (FETCH_SIZE, WRITE_SIZE) and exit (no GPU needed)")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print a per-kernel table from a rocprofv3 --kernel-trace database "
+                         "and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this implementation has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
