@@ -163,7 +163,9 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
     after compaction (A = ring_rows - window = 64): for a batch compacted
     together that is exactly when the rings are full.  The kernel itself
     decides per sequence on the device, so this cadence is only a saving of
-    launches, never a correctness assumption."""
+    launches, never a correctness assumption.  The same steps are then timed
+    as one swa_decode_step launch per layer (metadata roll + append +
+    decode), eagerly and as one captured HIP graph of the whole run."""
     c = si.DECODE_WORKLOADS[name]()
     ks, vs = c.prompt_tail("bf16")
     B, hq, hkv, d, R, W = c.batch, c.hq, c.hkv, c.d, c.ring_rows, c.window
@@ -175,8 +177,12 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
         api.cache_compact(to_dev(ks, torch), to_dev(vs, torch), to_dev(c.cu_tail, torch), kr, vr,
                           meta, W, to_dev(c.prompt_lens, torch), to_dev(c.left_pad, torch))
         rings.append((kr, vr, meta))
+    # timed steps: the workload's own, or 32 consecutive ones when it has
+    # fewer (the single-sequence step at position 3000 is then timed over
+    # positions 3000..3031, which include the roll at 3008)
+    nsteps = max(c.steps, 32)
     steps_in = []
-    for s in range(-c.pre_appends, c.steps):
+    for s in range(-c.pre_appends, nsteps):
         q, kn, vn = c.step_inputs(s, "bf16")
         steps_in.append((to_dev(q, torch), to_dev(kn, torch), to_dev(vn, torch)))
     ws = api.decode_workspace(steps_in[0][0], rings[0][0])
@@ -215,7 +221,43 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
     # warm: the same ring set every call
     warm_ms = time_loop(lambda i: api.decode(q, rings[0][0], rings[0][1], rings[0][2], W,
                                              out=outs[0], workspace=ws), reps, warmup, torch)
-    pos = c.prompt_lens.astype(np.int64) - 1 + c.pre_appends + c.steps
+
+    # the same steps as one swa_decode_step launch per layer (roll by
+    # metadata + append + decode), on freshly compacted ring sets
+    def fresh_rings():
+        for kr, vr, meta in rings:
+            api.cache_compact(to_dev(ks, torch), to_dev(vs, torch), to_dev(c.cu_tail, torch), kr, vr,
+                              meta, W, to_dev(c.prompt_lens, torch), to_dev(c.left_pad, torch))
+        for s in range(c.pre_appends):
+            q0, kn0, vn0 = steps_in[s]
+            for li, (kr, vr, meta) in enumerate(rings):
+                api.decode_step(q0, kn0, vn0, kr, vr, meta, W, out=outs[li], workspace=ws)
+        torch.cuda.synchronize()
+
+    fresh_rings()
+    e0.record()
+    for t, (qq, kn, vn) in enumerate(timed):
+        for li, (kr, vr, meta) in enumerate(rings):
+            api.decode_step(qq, kn, vn, kr, vr, meta, W, out=outs[li], workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    fused_us = e0.elapsed_time(e1) * 1e3 / (len(timed) * layers)
+    # and the whole run (every step of every layer) captured in one HIP graph
+    # and replayed: no host launch cost per kernel
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t, (qq, kn, vn) in enumerate(timed):
+            for li, (kr, vr, meta) in enumerate(rings):
+                api.decode_step(qq, kn, vn, kr, vr, meta, W, out=outs[li], workspace=ws)
+    fresh_rings()
+    graph.replay()  # warm-up
+    fresh_rings()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / (len(timed) * layers)
+    pos = c.prompt_lens.astype(np.int64) - 1 + c.pre_appends + nsteps
     valid = decode_valid_rows(pos, c.left_pad.astype(np.int64), W)
     es = 2
     alg_bytes = int(valid.sum()) * hkv * d * es * 2 + 2 * B * hq * d * es + B * 16
@@ -226,6 +268,7 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
         "us_per_step_append_decode_roll": step_us, "rolls_in_run": sum(
             1 for t in range(len(timed)) if (c.pre_appends + t) > 0 and (c.pre_appends + t) % A == 0),
         "decode_us": dec_ms * 1e3, "decode_warm_us": warm_ms * 1e3,
+        "us_per_step_fused": fused_us, "us_per_step_fused_graph": graph_us,
         "algorithmic_bytes": alg_bytes, "full_ring_bytes": scanned,
         "decode_gbs": alg_bytes / (dec_ms * 1e-3) / 1e9,
         "frac_of_hbm_peak": alg_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -412,8 +455,9 @@ def main():
                   flush=True)
         for name in ("decode_b64_d256", "decode_single_d256"):
             workloads[name] = bench_decode(name, torch, api)
-            print("%s: %.2f us/step, decode %.2f us, %.0f GB/s" % (
+            print("%s: %.2f us/step, fused %.2f us/step (graph %.2f), decode %.2f us, %.0f GB/s" % (
                 name, workloads[name]["us_per_step_append_decode_roll"],
+                workloads[name]["us_per_step_fused"], workloads[name]["us_per_step_fused_graph"],
                 workloads[name]["decode_us"], workloads[name]["decode_gbs"]), file=sys.stderr,
                 flush=True)
 

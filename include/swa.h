@@ -149,6 +149,41 @@ SWA_API int swa_decode(const void* q, const void* k_ring, const void* v_ring,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * swa_decode_step -- one whole decode step of every sequence in one launch:
+ * the periodic roll (by metadata), the append of the new token and the
+ * decode of its query.
+ *
+ * [SPYRE] Summary: the compact cache holds window + slack anchored rows,
+ * receives each new token through the compact cache index and is rolled
+ * every slack-count tokens; Compilation behavior: every position-dependent
+ * value is tensor data, one fixed-shape launch per step.  [BONSAI] Steps
+ * 2-3: writes wrap with a modulo and the mask follows the wrap.  For each
+ * sequence b, from ring_meta[b] = {pos, anchor, start, lo}: p = pos + 1;
+ * if p - anchor >= ring_rows, anchor += A and start = (start + A) mod
+ * ring_rows with A = ring_rows - window (every position keeps its physical
+ * row; the A oldest rows, all outside the window, become free: the same
+ * state as swa_cache_roll reaches by copying, without moving bytes).  Then,
+ * as swa_cache_append, row slot(p) of every kv head receives k_new[b] /
+ * v_new[b] and pos = p (if the ring is still full, nothing is written, pos
+ * is kept and SWA_META_ERR is set).  Then, as swa_decode, out[b] is the
+ * attention of q[b] over the rows of positions max(lo, pos - window + 1, 0)
+ * .. pos.  ring_meta is updated in place.
+ *
+ *   q [batch, hq, d]; k_new, v_new [batch, hkv, d];
+ *   k_ring, v_ring [batch, hkv, ring_rows, d]; ring_meta int32 [batch, 4];
+ *   out [batch, hq, d]; window >= 1, ring_rows > window; scale <= 0 means
+ *   1 / sqrt(d); workspace as for swa_decode (same size, same reuse rule).
+ * Rings advanced only by this call never need swa_cache_roll.  A ring rolled
+ * by copy (swa_cache_roll) and one rolled here hold the same positions in
+ * different physical rows; both are valid states for every entry point.
+ */
+SWA_API int swa_decode_step(const void* q, const void* k_new, const void* v_new,
+                            void* k_ring, void* v_ring, int32_t* ring_meta, int32_t window,
+                            void* out, int32_t batch, int32_t ring_rows, int32_t hq,
+                            int32_t hkv, int32_t d, int32_t dtype, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * swa_cache_append -- write one new token per sequence into its ring.
  *
  * [SPYRE] Summary: decode writes go through the compact cache index;

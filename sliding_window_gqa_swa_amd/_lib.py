@@ -30,6 +30,8 @@ SIGNATURES = {
     "swa_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "swa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "swa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
+    "swa_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P,
+                                       _S, _P]),
     "swa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "swa_cache_compact": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "swa_cache_roll": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),

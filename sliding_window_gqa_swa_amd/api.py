@@ -96,6 +96,30 @@ def decode(q, k_ring, v_ring, ring_meta, window, out=None, workspace=None, scale
     return out
 
 
+def decode_step(q, k_new, v_new, k_ring, v_ring, ring_meta, window, out=None, workspace=None,
+                scale=0.0):
+    """Roll (by metadata, when a ring is full), append and decode in one
+    launch; see swa_decode_step in swa.h.
+
+    q [B, Hq, D]; k_new/v_new [B, Hkv, D]; k_ring/v_ring [B, Hkv, R, D];
+    ring_meta int32 [B, 4] (updated in place).  Returns out [B, Hq, D]."""
+    B, hq, d = q.shape
+    _, hkv, R, _ = k_ring.shape
+    if k_new.shape != (B, hkv, d) or v_new.shape != (B, hkv, d):
+        raise ValueError("k_new and v_new must be [B, Hkv, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = decode_workspace(q, k_ring)
+    rc = _lib.lib().swa_decode_step(
+        _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_ring, "k_ring"),
+        _dev(v_ring, "v_ring"), _dev(ring_meta, "ring_meta", torch.int32), int(window),
+        _dev(out, "out"), B, R, hq, hkv, d, _dtype_code(q), float(scale),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(q))
+    _lib.check("swa_decode_step", rc)
+    return out
+
+
 def cache_append(k_new, v_new, k_ring, v_ring, ring_meta):
     """Write one token per sequence at position pos + 1; see swa_cache_append."""
     B, hkv, R, d = k_ring.shape

@@ -129,8 +129,33 @@ SWA_API int swa_decode(const void* q, const void* k_ring, const void* v_ring,
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < plan.workspace_bytes)
     return SWA_EWORKSPACE;
   if (!(scale > 0.f)) scale = 1.0f / __builtin_sqrtf((float)d);
-  return swa::launch_decode(q, k_ring, v_ring, ring_meta, window, out, batch, ring_rows, hq,
-                            hkv, d, dtype, scale, workspace, plan, (hipStream_t)stream);
+  // (decode only: the kernel reads the rings and ring_meta and writes neither)
+  return swa::launch_decode(q, nullptr, nullptr, const_cast<void*>(k_ring),
+                            const_cast<void*>(v_ring), const_cast<int32_t*>(ring_meta), window,
+                            out, batch, ring_rows, hq, hkv, d, dtype, scale, workspace, plan,
+                            (hipStream_t)stream);
+}
+
+SWA_API int swa_decode_step(const void* q, const void* k_new, const void* v_new,
+                            void* k_ring, void* v_ring, int32_t* ring_meta, int32_t window,
+                            void* out, int32_t batch, int32_t ring_rows, int32_t hq,
+                            int32_t hkv, int32_t d, int32_t dtype, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_heads(hq, hkv, d, dtype);
+  if (rc) return rc;
+  rc = check_ring(window, batch, ring_rows, hkv, d, dtype);
+  if (rc) return rc;
+  if (batch == 0) return SWA_OK;
+  if (!ptr_ok(q) || !ptr_ok(k_new) || !ptr_ok(v_new) || !ptr_ok(k_ring) || !ptr_ok(v_ring) ||
+      !ptr_ok(ring_meta) || !ptr_ok(out))
+    return SWA_EINVAL;
+  const swa::DecodePlan plan = swa::plan_decode(batch, hq, hkv, d, ring_rows);
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < plan.workspace_bytes)
+    return SWA_EWORKSPACE;
+  if (!(scale > 0.f)) scale = 1.0f / __builtin_sqrtf((float)d);
+  return swa::launch_decode(q, k_new, v_new, k_ring, v_ring, ring_meta, window, out, batch,
+                            ring_rows, hq, hkv, d, dtype, scale, workspace, plan,
+                            (hipStream_t)stream);
 }
 
 SWA_API int swa_cache_append(const void* k_new, const void* v_new,

@@ -24,6 +24,20 @@
 //   (m, l, o) go to the workspace; the last split block of each sequence and
 //   head block (a device-scope counter in the workspace) combines the splits
 //   in a fixed order (deterministic), so one launch does the whole decode.
+//
+// Decode step (STEP = true): the same kernel also performs the per-token
+// cache work of the sequence first, so one launch serves a whole decode
+// step.  Every block derives the same new state from ring_meta: position
+// p = pos + 1; if the ring is full (p - anchor >= R) it is rolled by
+// metadata alone (anchor += A, start += A mod R, A = R - W: each position
+// keeps its physical row, the A oldest rows become free); the token is
+// appended at slot(p) unless the ring is still full (then nothing is
+// written and the sticky flag is set, as for swa_cache_append).  Blocks
+// whose rows include slot(p) take that row from k_new / v_new instead of
+// the ring, and exactly one of them writes it to the ring, so no block
+// reads a row while it is written.  The last block of a sequence (a second
+// device-scope counter) stores the new ring_meta after every block of the
+// sequence has read the old one.
 #include <type_traits>
 
 #include "swa_common.h"
@@ -89,13 +103,13 @@ struct DecGeom {
   static constexpr int ELT = CPL * VEC;             // elements per lane
 };
 
-template <int D, typename T, int GB>
+template <int D, typename T, int GB, bool STEP>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_ring,
-    const T* __restrict__ v_ring, const int32_t* __restrict__ meta, int W,
-    int R, int hq, int hkv, int head_blocks, int rows_per_split,
-    float qk_scale_log2, float* ws_o, float* ws_ml, int splits, uint32_t* counters,
-    T* __restrict__ out) {
+    const T* __restrict__ q, T* __restrict__ k_ring, T* __restrict__ v_ring,
+    int32_t* __restrict__ meta, int W, int R, int hq, int hkv, int head_blocks,
+    int rows_per_split, float qk_scale_log2, float* ws_o, float* ws_ml, int splits,
+    uint32_t* counters, T* __restrict__ out, const T* __restrict__ k_new,
+    const T* __restrict__ v_new) {
   using G = DecGeom<D, T>;
   __shared__ float red_o[kDecWaves][GB][D];
   __shared__ float red_m[kDecWaves][GB], red_l[kDecWaves][GB];
@@ -118,9 +132,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   // ring state; the physical -> position map needs no division per row:
   // j = r - start (+R if negative), a = anchor + j
   const int32_t* m = meta + 4 * (size_t)b;
-  const int64_t pos = m[0], anchor = m[1];
-  const int start = (int)pos_mod(m[2], R);
-  const int64_t lo = m[3] & 0x7fffffff;
+  int64_t pos = m[0], anchor = m[1];
+  int start = (int)pos_mod(m[2], R);
+  const int32_t lo_raw = m[3];
+  const int64_t lo = lo_raw & 0x7fffffff;
+  // decode step: metadata roll, then the append slot (-1: refused)
+  int slot_p = -1;
+  if constexpr (STEP) {
+    const int64_t p = pos + 1;
+    const int A = R - W;  // > 0 (checked on the host)
+    if (p - anchor >= R) {
+      anchor += A;
+      start = (int)pos_mod((int64_t)start + A, R);
+    }
+    if (p - anchor < R && p >= anchor) {
+      slot_p = (int)pos_mod((int64_t)start + (p - anchor), R);
+      pos = p;
+    }
+  }
   int64_t low = max(lo, (int64_t)0);
   if (W > 0) low = max(low, pos - W + 1);
   const int64_t high = pos;
@@ -145,6 +174,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const uint32_t ring_bytes = (uint32_t)((size_t)R * D * sizeof(T));
   const i32x4 krs = make_buffer_rsrc(k_ring + ring_off, ring_bytes);
   const i32x4 vrs = make_buffer_rsrc(v_ring + ring_off, ring_bytes);
+  const size_t new_off = ((size_t)b * hkv + kvh) * D;  // row of k_new / v_new
+  if constexpr (STEP) {
+    // one writer of the appended row: head block 0 of the split holding it
+    if (hb == 0 && slot_p >= r0 && slot_p < r1) {
+      for (int c = threadIdx.x; c < D / G::VEC; c += kDecThreads) {
+        const size_t dst = ring_off + (size_t)slot_p * D + (size_t)c * G::VEC;
+        *reinterpret_cast<u32x4*>(k_ring + dst) =
+            *reinterpret_cast<const u32x4*>(k_new + new_off + (size_t)c * G::VEC);
+        *reinterpret_cast<u32x4*>(v_ring + dst) =
+            *reinterpret_cast<const u32x4*>(v_new + new_off + (size_t)c * G::VEC);
+      }
+    }
+  }
 
   float mrun[GB], lrun[GB], acc[GB][G::ELT];
 #pragma unroll
@@ -170,8 +212,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
       for (int c = 0; c < G::CPL; ++c) {
         const int32_t off = ok[u] ? row_byte + (li + c * G::LPR) * 16 : kBufferOob;
-        kw[u][c] = buffer_load16(krs, off);
-        vw[u][c] = buffer_load16(vrs, off);
+        if (STEP && r == slot_p) {  // the appended row, from the step's input
+          const size_t e0 = new_off + (size_t)(li + c * G::LPR) * G::VEC;
+          kw[u][c] = *reinterpret_cast<const u32x4*>(k_new + e0);
+          vw[u][c] = *reinterpret_cast<const u32x4*>(v_new + e0);
+        } else {
+          kw[u][c] = buffer_load16(krs, off);
+          vw[u][c] = buffer_load16(vrs, off);
+        }
       }
     }
     // scores (identical in every lane of a row group)
@@ -288,9 +336,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   __shared__ int is_last;
   __syncthreads();
   uint32_t* cnt = counters + (size_t)b * gridDim.y + blockIdx.y;
-  if (threadIdx.x == 0)
+  if (threadIdx.x == 0) {
     is_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
               (uint32_t)(splits - 1);
+    if constexpr (STEP) {
+      // every block of the sequence has read ring_meta: the last one to get
+      // here stores the new state (the ring row was written by its block
+      // before that block's barrier above)
+      uint32_t* scnt = counters + (size_t)gridDim.z * gridDim.y + b;
+      const uint32_t nblk = (uint32_t)splits * gridDim.y;
+      if (__hip_atomic_fetch_add(scnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nblk - 1) {
+        int32_t* mw = meta + 4 * (size_t)b;
+        mw[0] = (int32_t)pos;
+        mw[1] = (int32_t)anchor;
+        mw[2] = start;
+        mw[3] = slot_p >= 0 ? lo_raw : (int32_t)((uint32_t)lo_raw | 0x80000000u);
+        __hip_atomic_store(scnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
   __syncthreads();
   if (!is_last) return;
   // (m, l) of every split -> LDS in one batch of independent loads
@@ -326,18 +390,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 }
 
 template <int D, typename T, int GB>
-int launch_decode_t(const void* q, const void* k_ring, const void* v_ring,
-                    const int32_t* meta, int window, void* out, int batch,
+int launch_decode_t(const void* q, const void* k_new, const void* v_new, void* k_ring,
+                    void* v_ring, int32_t* meta, int window, void* out, int batch,
                     int ring_rows, int hq, int hkv, float scale,
                     void* workspace, const DecodePlan& p, hipStream_t stream) {
   uint32_t* counters = (uint32_t*)workspace;
   float* ws_ml = (float*)((char*)workspace + p.counter_bytes);
   float* ws_o = ws_ml + (size_t)batch * hq * p.splits * 2;
   dim3 grid(p.splits, hkv * p.head_blocks, batch);
-  hipLaunchKernelGGL((decode_split_kernel<D, T, GB>), grid, dim3(kDecThreads), 0, stream,
-                     (const T*)q, (const T*)k_ring, (const T*)v_ring, meta, window,
-                     ring_rows, hq, hkv, p.head_blocks, p.rows_per_split,
-                     scale * kLog2e, ws_o, ws_ml, p.splits, counters, (T*)out);
+  if (k_new == nullptr) {
+    hipLaunchKernelGGL((decode_split_kernel<D, T, GB, false>), grid, dim3(kDecThreads), 0, stream,
+                       (const T*)q, (T*)k_ring, (T*)v_ring, meta, window,
+                       ring_rows, hq, hkv, p.head_blocks, p.rows_per_split,
+                       scale * kLog2e, ws_o, ws_ml, p.splits, counters, (T*)out,
+                       (const T*)nullptr, (const T*)nullptr);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<D, T, GB, true>), grid, dim3(kDecThreads), 0, stream,
+                       (const T*)q, (T*)k_ring, (T*)v_ring, meta, window,
+                       ring_rows, hq, hkv, p.head_blocks, p.rows_per_split,
+                       scale * kLog2e, ws_o, ws_ml, p.splits, counters, (T*)out,
+                       (const T*)k_new, (const T*)v_new);
+  }
   return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
 }
 
@@ -372,23 +445,26 @@ DecodePlan plan_decode(int batch, int hq, int hkv, int d, int ring_rows) {
   if (rps < rps_min) rps = rps_min;
   p.rows_per_split = rps;
   p.splits = (ring_rows + rps - 1) / rps;
-  // [counters: one uint32 per (sequence, kv head, head block), 256-byte
-  //  padded][(m, l) per (sequence, query head, split)][o per ... and d]
-  p.counter_bytes = ((size_t)batch * hkv * p.head_blocks * sizeof(uint32_t) + 255) / 256 * 256;
+  // [counters: one uint32 per (sequence, kv head, head block), then one per
+  //  sequence (decode step), 256-byte padded][(m, l) per (sequence, query
+  //  head, split)][o per ... and d]
+  p.counter_bytes =
+      ((size_t)batch * (hkv * p.head_blocks + 1) * sizeof(uint32_t) + 255) / 256 * 256;
   p.workspace_bytes =
       p.counter_bytes + (size_t)batch * hq * p.splits * ((size_t)d + 2) * sizeof(float);
   return p;
 }
 
-int launch_decode(const void* q, const void* k_ring, const void* v_ring,
-                  const int32_t* meta, int window, void* out, int batch,
+int launch_decode(const void* q, const void* k_new, const void* v_new, void* k_ring,
+                  void* v_ring, int32_t* meta, int window, void* out, int batch,
                   int ring_rows, int hq, int hkv, int d, int dtype,
                   float scale, void* workspace, const DecodePlan& p,
                   hipStream_t stream) {
-#define SWA_DEC_CASE(DD, TT, GBV)                                                    \
-  if (d == DD && p.heads_per_block == GBV)                                           \
-    return launch_decode_t<DD, TT, GBV>(q, k_ring, v_ring, meta, window, out, batch, \
-                                        ring_rows, hq, hkv, scale, workspace, p, stream);
+#define SWA_DEC_CASE(DD, TT, GBV)                                                     \
+  if (d == DD && p.heads_per_block == GBV)                                            \
+    return launch_decode_t<DD, TT, GBV>(q, k_new, v_new, k_ring, v_ring, meta, window, \
+                                        out, batch, ring_rows, hq, hkv, scale, workspace, \
+                                        p, stream);
 #define SWA_DEC_D(DD, TT) \
   SWA_DEC_CASE(DD, TT, 1) SWA_DEC_CASE(DD, TT, 2) SWA_DEC_CASE(DD, TT, 4) SWA_DEC_CASE(DD, TT, 8)
   if (dtype == SWA_BF16) {

@@ -31,8 +31,10 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 DecodePlan plan_decode(int batch, int hq, int hkv, int d, int ring_rows);
-int launch_decode(const void* q, const void* k_ring, const void* v_ring,
-                  const int32_t* meta, int window, void* out, int batch,
+// k_new == NULL: decode only (the rings and ring_meta are read, not
+// written); otherwise a decode step (metadata roll + append + decode).
+int launch_decode(const void* q, const void* k_new, const void* v_new, void* k_ring,
+                  void* v_ring, int32_t* meta, int window, void* out, int batch,
                   int ring_rows, int hq, int hkv, int d, int dtype,
                   float scale, void* workspace, const DecodePlan& plan,
                   hipStream_t stream);

@@ -97,6 +97,37 @@ def test_decode_rejects(kw, code):
     assert _decode(**kw) == code
 
 
+def _decode_step(**kw):
+    a = dict(q=A, kn=A, vn=A, k=A, v=A, meta=B, window=1024, out=A, b=2, R=1088, hq=8, hkv=4,
+             d=256, dtype=0, ws=A, wsb=1 << 30)
+    a.update(kw)
+    return _lib.lib().swa_decode_step(a["q"], a["kn"], a["vn"], a["k"], a["v"], a["meta"],
+                                      a["window"], a["out"], a["b"], a["R"], a["hq"], a["hkv"],
+                                      a["d"], a["dtype"], 0.0, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=0), _lib.SWA_EINVAL),
+    (dict(R=1024), _lib.SWA_EINVAL),
+    (dict(R=70000, window=1024), _lib.SWA_EUNSUPPORTED),
+    (dict(d=96), _lib.SWA_EUNSUPPORTED),
+    (dict(dtype=3), _lib.SWA_EUNSUPPORTED),
+    (dict(kn=None), _lib.SWA_EINVAL),
+    (dict(vn=A + 4), _lib.SWA_EINVAL),
+    (dict(meta=None), _lib.SWA_EINVAL),
+    (dict(ws=None), _lib.SWA_EWORKSPACE),
+    (dict(wsb=16), _lib.SWA_EWORKSPACE),
+    (dict(hq=6, hkv=4), _lib.SWA_EINVAL),
+])
+def test_decode_step_rejects(kw, code):
+    assert _decode_step(**kw) == code
+
+
+def test_decode_step_empty_batch_is_a_no_op():
+    assert _decode_step(b=0, q=None, kn=None, vn=None, k=None, v=None, meta=None, out=None,
+                        ws=None, wsb=0) == _lib.SWA_OK
+
+
 def test_decode_workspace_depends_only_on_sizes():
     L = _lib.lib()
     a = L.swa_decode_workspace_bytes(64, 8, 4, 256, 1088)
