@@ -197,10 +197,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     for (int e = 0; e < G::ELT; ++e) acc[j][e] = 0.f;
   }
 
-  constexpr int U = 4;  // row steps in flight per lane (K and V loads)
-  for (int base = r0; base < r1; base += G::RPI * U) {
-    u32x4 kw[U][G::CPL], vw[U][G::CPL];
-    bool ok[U];
+  constexpr int U = 4;  // row steps per batch of K and V loads
+  constexpr int STEPR = G::RPI * U;  // rows per batch
+  // One batch of row loads: every lane issues U rows x CPL chunks of K and
+  // V.  Batches past r1 issue only out-of-range offsets (zeros, no memory
+  // access), so the pipeline below needs no branch around a load.
+  auto issue = [&](int base, u32x4 (&kw)[U][G::CPL], u32x4 (&vw)[U][G::CPL], bool (&ok)[U])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = base + u * G::RPI + wave * G::RPW + rg;
@@ -222,6 +225,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         }
       }
     }
+  };
+  // scores, online softmax over the batch, then the weighted V rows
+  auto consume = [&](const u32x4 (&kw)[U][G::CPL], const u32x4 (&vw)[U][G::CPL],
+                     const bool (&ok)[U]) __attribute__((always_inline)) {
     // scores (identical in every lane of a row group)
     float sc[U][GB];
 #pragma unroll
@@ -238,7 +245,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         sc[u][j] = ok[u] ? x : -INFINITY;
       }
     }
-    // online softmax over the batch, then the weighted V rows
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
       float bm = sc[0][j];
@@ -266,6 +272,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
         for (int e = 0; e < G::ELT; ++e) acc[j][e] = fmaf(p[u], vf[e], acc[j][e]);
       }
+    }
+  };
+  // two batches in flight: the next batch's loads go out before the current
+  // batch is consumed, so a wave waits for memory once per split, not once
+  // per batch
+  {
+    u32x4 kA[U][G::CPL], vA[U][G::CPL], kB[U][G::CPL], vB[U][G::CPL];
+    bool okA[U], okB[U];
+    int base = r0;
+    issue(base, kA, vA, okA);
+    while (base < r1) {
+      issue(base + STEPR, kB, vB, okB);
+      consume(kA, vA, okA);
+      base += STEPR;
+      if (base >= r1) break;
+      issue(base + STEPR, kA, vA, okA);
+      consume(kB, vB, okB);
+      base += STEPR;
     }
   }
 
