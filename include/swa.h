@@ -111,6 +111,38 @@ SWA_API int swa_prefill(const void* q, const void* k, const void* v,
                         int32_t dtype, float scale, void* stream);
 
 /*
+ * swa_prefill_chunk -- prefill of one chunk of each document against the
+ * document's cache so far.
+ *
+ * [SPYRE] Summary: chunked prefill is preserved: a prompt is prefilled in
+ * chunks, each attending to the keys already cached plus its own.  For
+ * document b the keys are its first len_k = cu_seqlens_k[b+1] -
+ * cu_seqlens_k[b] positions and the queries are the LAST len_q =
+ * cu_seqlens_q[b+1] - cu_seqlens_q[b] of them (0 <= len_q <= len_k), so
+ * query row i of b sits at position len_k - len_q + i.  The mask is
+ * swa_prefill's over positions 0 .. len_k - 1 of the document: a chunk's
+ * rows equal those rows of swa_prefill over the document cut at len_k
+ * (for SWA_CAUSAL, the rows of the whole document: later keys are never
+ * allowed); an image block is cut at len_k too (its later tokens are not
+ * cached yet).  swa_prefill is the case cu_seqlens_q == cu_seqlens_k.
+ *
+ *   q [total_q, hq, d], out like q; k and v [total_k, hkv, d];
+ *   cu_seqlens_q, cu_seqlens_k int32 [num_docs + 1] (device), each
+ *   non-decreasing from 0 to total_q / total_k, with len_q <= len_k per
+ *   document (malformed offsets give unspecified values, never an
+ *   out-of-bounds access);
+ *   doc_or_block_ids int32 [total_k] (device), indexed by key row:
+ *   required for SWA_BLOCKWISE, ignored for SWA_CAUSAL.
+ *   window, causal_mode, scale, dtype, stream as for swa_prefill.
+ */
+SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              const int32_t* doc_or_block_ids, int32_t window,
+                              int32_t causal_mode, void* out, int32_t total_q,
+                              int32_t total_k, int32_t num_docs, int32_t hq, int32_t hkv,
+                              int32_t d, int32_t dtype, float scale, void* stream);
+
+/*
  * Bytes of workspace swa_decode needs for these sizes: split counters plus
  * fp32 split-K partials.  Depends only on the sizes, never on positions.
  */

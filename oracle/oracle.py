@@ -91,6 +91,39 @@ def prefill(q, k, v, cu_seqlens, ids=None, window=0, mode=CAUSAL, scale=None,
     return out
 
 
+def prefill_chunk(q, k, v, cu_q, cu_k, ids=None, window=0, mode=CAUSAL, scale=None,
+                  rows=None, nthreads=0):
+    """Prefill of a chunk of each document against its cache so far, fp64.
+
+    [SPYRE] Summary: chunked prefill is preserved.  Document b's keys are
+    its first len_k = cu_k[b+1] - cu_k[b] positions and its queries the last
+    len_q = cu_q[b+1] - cu_q[b] of them; the mask is the prefill mask over
+    positions 0 .. len_k - 1 of the document.  That is, by definition, the
+    prefill of the documents cut at len_k, read at the chunk's rows: the
+    chunk rows are placed at their key positions of a key-length query array
+    (other rows unused) and only they are computed.  ids are key-indexed.
+    ``rows`` selects packed chunk rows (default: all).
+    Returns float64 [len(rows), Hq, D]."""
+    q = np.ascontiguousarray(q)
+    cq = np.asarray(cu_q, dtype=np.int64)
+    ck = np.asarray(cu_k, dtype=np.int64)
+    Tk = int(ck[-1])
+    _, hq, d = q.shape
+    full = np.zeros((Tk, hq, d), dtype=q.dtype)
+    keyrow = np.empty(q.shape[0], np.int64)  # key row of every chunk row
+    for b in range(cq.size - 1):
+        nq, ke = int(cq[b + 1] - cq[b]), int(ck[b + 1])
+        if nq > ke - int(ck[b]):
+            raise ValueError("document %d: more queries than keys" % b)
+        full[ke - nq:ke] = q[cq[b]:cq[b + 1]]
+        keyrow[cq[b]:cq[b + 1]] = np.arange(ke - nq, ke)
+    sel = keyrow if rows is None else keyrow[np.asarray(rows, dtype=np.int64)]
+    if sel.size == 0:
+        return np.zeros((0, hq, d), dtype=np.float64)
+    return prefill(full, k, v, ck.astype(np.int32), ids, window, mode, scale,
+                   rows=sel.astype(np.int32), nthreads=nthreads)
+
+
 def decode_linear(q, k_hist, v_hist, hist_off, first_pos, hist_len, pos, lo,
                   window, scale=None, nthreads=0):
     """One-token decode per sequence on linear histories, fp64.

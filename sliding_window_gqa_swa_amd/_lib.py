@@ -28,6 +28,8 @@ _F = ctypes.c_float
 _S = ctypes.c_size_t
 SIGNATURES = {
     "swa_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "swa_prefill_chunk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _I,
+                                         _I, _F, _P]),
     "swa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "swa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "swa_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P,

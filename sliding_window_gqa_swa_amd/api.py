@@ -65,6 +65,36 @@ def prefill(q, k, v, cu_seqlens, doc_or_block_ids=None, window=0, causal_mode=CA
     return out
 
 
+def prefill_chunk(q, k, v, cu_seqlens_q, cu_seqlens_k, doc_or_block_ids=None, window=0,
+                  causal_mode=CAUSAL, out=None, scale=0.0):
+    """Prefill of one chunk of each document against its cache so far; see
+    swa_prefill_chunk in swa.h.
+
+    q [Tq, Hq, D] (document b's rows are the last cu_q[b+1]-cu_q[b] of its
+    cu_k[b+1]-cu_k[b] key positions); k/v [Tk, Hkv, D]; doc_or_block_ids
+    int32 [Tk] (BLOCKWISE only).  Returns out [Tq, Hq, D]."""
+    Tq, hq, d = q.shape
+    Tk, hkv = k.shape[0], k.shape[1]
+    if k.shape != (Tk, hkv, d) or v.shape != (Tk, hkv, d):
+        raise ValueError("k and v must be [Tk, Hkv, D] with q's D")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have one entry per document + 1")
+    if out is None:
+        out = torch.empty_like(q)
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s dtype differs from q" % name)
+    rc = _lib.lib().swa_prefill_chunk(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32),
+        _dev(doc_or_block_ids, "doc_or_block_ids", torch.int32), int(window), int(causal_mode),
+        _dev(out, "out"), Tq, Tk, cu_seqlens_q.numel() - 1, hq, hkv, d, dt, float(scale),
+        _stream(q))
+    _lib.check("swa_prefill_chunk", rc)
+    return out
+
+
 def decode_workspace_bytes(batch, hq, hkv, d, ring_rows) -> int:
     return int(_lib.lib().swa_decode_workspace_bytes(batch, hq, hkv, d, ring_rows))
 

@@ -84,24 +84,55 @@ SWA_API int swa_prefill(const void* q, const void* k, const void* v,
                         int32_t causal_mode, void* out, int32_t total_tokens,
                         int32_t num_docs, int32_t hq, int32_t hkv, int32_t d,
                         int32_t dtype, float scale, void* stream) {
+  // a whole prompt is the chunk that covers every key of its document
+  return swa_prefill_chunk(q, k, v, cu_seqlens, cu_seqlens, doc_or_block_ids, window,
+                           causal_mode, out, total_tokens, total_tokens, num_docs, hq, hkv, d,
+                           dtype, scale, stream);
+}
+
+SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              const int32_t* doc_or_block_ids, int32_t window,
+                              int32_t causal_mode, void* out, int32_t total_q,
+                              int32_t total_k, int32_t num_docs, int32_t hq, int32_t hkv,
+                              int32_t d, int32_t dtype, float scale, void* stream) {
   int rc = check_heads(hq, hkv, d, dtype);
   if (rc) return rc;
-  if (total_tokens < 0 || num_docs < 0) return SWA_EINVAL;
+  if (total_q < 0 || total_k < 0 || num_docs < 0) return SWA_EINVAL;
   if (causal_mode != SWA_CAUSAL && causal_mode != SWA_BLOCKWISE) return SWA_EUNSUPPORTED;
-  if (total_tokens == 0) return SWA_OK;  // nothing to compute
-  if (num_docs < 1) return SWA_EINVAL;
+  if (total_q == 0) return SWA_OK;  // nothing to compute
+  if (num_docs < 1 || total_k < 1) return SWA_EINVAL;
   if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out)) return SWA_EINVAL;
-  if (cu_seqlens == nullptr || ((uintptr_t)cu_seqlens & 3u)) return SWA_EINVAL;
+  if (cu_seqlens_q == nullptr || ((uintptr_t)cu_seqlens_q & 3u)) return SWA_EINVAL;
+  if (cu_seqlens_k == nullptr || ((uintptr_t)cu_seqlens_k & 3u)) return SWA_EINVAL;
   if (causal_mode == SWA_BLOCKWISE &&
       (doc_or_block_ids == nullptr || ((uintptr_t)doc_or_block_ids & 3u)))
     return SWA_EINVAL;
   // element offsets stay below 2^63; token indices below 2^31
-  if ((int64_t)total_tokens * hq * d >= (int64_t)1 << 62) return SWA_EUNSUPPORTED;
+  if ((int64_t)total_q * hq * d >= (int64_t)1 << 62 ||
+      (int64_t)total_k * hkv * d >= (int64_t)1 << 62)
+    return SWA_EUNSUPPORTED;
   if (!(scale > 0.f)) scale = 1.0f / __builtin_sqrtf((float)d);
-  return swa::launch_prefill(q, k, v, cu_seqlens,
-                             causal_mode == SWA_BLOCKWISE ? doc_or_block_ids : nullptr,
-                             window, causal_mode, out, total_tokens, num_docs, hq, hkv, d,
-                             dtype, scale, (hipStream_t)stream);
+  swa::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.ids = causal_mode == SWA_BLOCKWISE ? doc_or_block_ids : nullptr;
+  a.window = window;
+  a.mode = causal_mode;
+  a.out = out;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.num_docs = num_docs;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.dtype = dtype;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  return swa::launch_prefill(a);
 }
 
 SWA_API size_t swa_decode_workspace_bytes(int32_t batch, int32_t hq,

@@ -5,19 +5,14 @@
 
 namespace swa {
 
-int launch_prefill_d256(const void* q, const void* k, const void* v, const int32_t* cu,
-                       const int32_t* ids, int window, int mode, void* out, int total_tokens,
-                       int num_docs, int hq, int hkv, int dtype, float scale, hipStream_t s) {
-  const int g = hq / hkv;
-  if (dtype == SWA_BF16) {
+int launch_prefill_d256(const PrefillArgs& a) {
+  const int g = a.hq / a.hkv;
+  if (a.dtype == SWA_BF16) {
     if (g % 2 == 0)
-      return launch_prefill_cfg<256, __bf16, 2, 64, 4, 2, true>(q, k, v, cu, ids, window, mode, out,
-                                                       total_tokens, num_docs, hq, hkv, scale, s);
-    return launch_prefill_cfg<256, __bf16, 2, 64, 4, 1, true>(q, k, v, cu, ids, window, mode, out,
-                                                     total_tokens, num_docs, hq, hkv, scale, s);
+      return launch_prefill_cfg<256, __bf16, 2, 64, 4, 2, true>(a);
+    return launch_prefill_cfg<256, __bf16, 2, 64, 4, 1, true>(a);
   }
-  return launch_prefill_cfg<256, float, 1, 32, 4, 1>(q, k, v, cu, ids, window, mode, out,
-                                                  total_tokens, num_docs, hq, hkv, scale, s);
+  return launch_prefill_cfg<256, float, 1, 32, 4, 1>(a);
 }
 
 }  // namespace swa

@@ -283,19 +283,64 @@ __device__ __forceinline__ int cu_upper(const int* cu_s, int ndocs, int i) {
   return a;
 }
 
+// Key position and document key range of query row i.  Documents are
+// found in the query offsets cuq; the keys of document d are rows
+// cuk[d] .. cuk[d+1]-1 and its query rows are the LAST ones of them (a
+// prefill chunk; cuk == cuq for a whole prompt), so row i sits at key
+// position i + cuk[d+1] - cuq[d+1].  A row outside every document is a
+// one-token document at key position i.  Offsets come from LDS copies when
+// in_lds, else from global memory.
+struct RowKeys {
+  int kp, ds, de;  // key position; document keys [ds, de)
+};
+__device__ __forceinline__ RowKeys row_keys(const int* cuq_s, const int* cuk_s,
+                                            const int32_t* cuq, const int32_t* cuk,
+                                            bool in_lds, int ndocs, int i, int Tk) {
+  int a = 0, bnd = ndocs + 1;  // upper bound: first d with cuq[d] > i
+  while (a < bnd) {
+    const int mid = (a + bnd) >> 1;
+    const int c = in_lds ? cuq_s[mid] : cuq[mid];
+    if (c > i) bnd = mid; else a = mid + 1;
+  }
+  const int doc = a - 1;
+  RowKeys r;
+  if (doc >= 0 && doc < ndocs) {
+    if (cuk_s == cuq_s && cuk == cuq) {  // whole prompts: key rows = query rows
+      r.kp = i;
+      r.ds = in_lds ? cuq_s[doc] : cuq[doc];
+      r.de = in_lds ? cuq_s[doc + 1] : cuq[doc + 1];
+    } else {
+      const int ke = in_lds ? cuk_s[doc + 1] : cuk[doc + 1];
+      const int qe = in_lds ? cuq_s[doc + 1] : cuq[doc + 1];
+      r.kp = i + (ke - qe);
+      r.ds = in_lds ? cuk_s[doc] : cuk[doc];
+      r.de = ke;
+    }
+  } else {
+    r.kp = i;
+    r.ds = i;
+    r.de = i + 1;
+  }
+  // clamps against malformed offsets (then values are unspecified, but every
+  // key index stays inside the buffers: tiles past Tk load zeros)
+  r.ds = min(max(r.ds, 0), r.kp);
+  r.de = max(min(r.de, Tk), r.kp + 1);
+  return r;
+}
+
 // Cost bucket of query tile `tile`: the number of key tiles a causal /
 // windowed tile visits (the image-block extension is left out: the value
 // only orders the work).
 template <int BM, int BN>
-__device__ __forceinline__ int tile_cost_bucket(const int* cu_s, int ndocs, int tile, int Ttot,
-                                                int W) {
+__device__ __forceinline__ int tile_cost_bucket(const int* cu_s, const int* cuk_s, int ndocs,
+                                                int tile, int Ttot, int Tk, int W) {
   const int r0 = tile * BM;
   const int r1 = min(r0 + BM, Ttot) - 1;
-  const int doc = cu_upper(cu_s, ndocs, r0) - 1;
-  int ds = (doc >= 0 && doc < ndocs) ? cu_s[doc] : r0;
-  ds = min(max(ds, 0), r0);
-  const int lo = W > 0 ? max(ds, r0 - W + 1) : ds;
-  return min(r1 / BN - lo / BN + 1, kPlanBuckets - 1);
+  // (whole prompts: the caller passes cu_s as both tables)
+  const RowKeys rk = row_keys(cu_s, cuk_s, nullptr, nullptr, true, ndocs, r0, Tk);
+  const int lo = W > 0 ? max(rk.ds, rk.kp - W + 1) : rk.ds;
+  const int kp1 = rk.kp + (r1 - r0);
+  return min(max(kp1 / BN - lo / BN + 1, 1), kPlanBuckets - 1);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave, by DPP row shifts and
@@ -322,14 +367,15 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // block-wide scan.  Deterministic.  Called by all NT threads; ends with a
 // barrier.  sel_s: 6 ints, wsum_s: 2 * NT / 64 ints.
 template <int NT, int BM, int BN>
-__device__ void lpt_select(const int* cu_s, int ndocs, int Ttot, int W, int ntiles, int w0, int P,
+__device__ void lpt_select(const int* cu_s, const int* cuk_s, int ndocs, int Ttot, int Tk, int W,
+                           int ntiles, int w0, int P,
                            const int (&pos)[2], unsigned char* bk, int* hist_s, int* wsum_s,
                            int* sel_s, int (&out)[2]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NWV = NT / 64;
   for (int i = tid; i < P; i += NT) {
     const int w = w0 + i;
-    const int c = tile_cost_bucket<BM, BN>(cu_s, ndocs, ntiles - 1 - (w % ntiles), Ttot, W);
+    const int c = tile_cost_bucket<BM, BN>(cu_s, cuk_s, ndocs, ntiles - 1 - (w % ntiles), Ttot, Tk, W);
     bk[i] = (unsigned char)c;
     atomicAdd(&hist_s[c], 1);
   }
@@ -399,8 +445,9 @@ template <int D, typename T, int MB, int BN, int NW, int GH, bool PL>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 256 && (D <= 128 || !PL) && !std::is_same<T, float>::value) ? 2 : 1)
 void prefill_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int32_t* __restrict__ cu, int ndocs, const int32_t* __restrict__ ids,
-    int W, int mode, T* __restrict__ out, int Ttot, int hq, int hkv,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ cuk, int ndocs,
+    const int32_t* __restrict__ ids, int W, int mode, T* __restrict__ out, int Ttot, int Tk,
+    int hq, int hkv,
     float qk_scale_log2, int ntiles, int nwork, int work_per_xcd, int slots_per_xcd,
     int colocated) {
   using G = PfGeom<D, T, MB, BN, NW, GH, PL>;
@@ -411,8 +458,8 @@ void prefill_fwd_kernel(
   __shared__ int lo_s[G::BM], hi_s[G::BM];
   __shared__ int red_s[4][NW];
   __shared__ unsigned long long runmask_s[(G::BM + 63) / 64];
-  __shared__ int ext_end_s, de_last_s;
-  __shared__ int cu_s[kCuCache];
+  __shared__ int ext_end_s, de_last_s, kp_last_s;
+  __shared__ int cu_s[kCuCache], cuk_s[kCuCache];  // query and key document offsets
   __shared__ int hist_s[kPlanBuckets];
   __shared__ int plan_s[6 + 2 * NW];
 
@@ -435,8 +482,14 @@ void prefill_fwd_kernel(
   // cu_seqlens -> LDS with one cooperative load (one memory latency instead
   // of log2(ndocs) dependent ones per row)
   const bool cu_in_lds = ndocs + 1 <= kCuCache;
+  // (whole prompts, cuk == cu, use one table for both)
+  const bool chunked = cuk != cu;
+  const int* cukl = chunked ? cuk_s : cu_s;
   if (cu_in_lds)
-    for (int d = tid; d <= ndocs; d += G::NT) cu_s[d] = cu[d];
+    for (int d = tid; d <= ndocs; d += G::NT) {
+      cu_s[d] = cu[d];
+      if (chunked) cuk_s[d] = cuk[d];
+    }
   const bool plan = cu_in_lds && P > 1 && P <= kPlanMaxItems;
   // Pipelined path: S = slots_per_xcd work-groups per XCD with at most two
   // items each: the sorted positions pos and 2S-1-pos, so the longest items
@@ -459,7 +512,7 @@ void prefill_fwd_kernel(
   __syncthreads();  // cu_s and the histogram are ready
   if (plan) {
     const int posv[2] = {pos, pos2};
-    lpt_select<G::NT, G::BM, BN>(cu_s, ndocs, Ttot, W, ntiles, w0, P, posv, &ring[0][0], hist_s,
+    lpt_select<G::NT, G::BM, BN>(cu_s, cukl, ndocs, Ttot, Tk, W, ntiles, w0, P, posv, &ring[0][0], hist_s,
                                  plan_s + 6, plan_s, items);
   }
 #pragma nounroll
@@ -513,10 +566,10 @@ void prefill_fwd_kernel(
     const T* vt = vbase + (size_t)k0 * kv_row_stride;
     const uint32_t kl = ring_base + stage * G::STAGE_BYTES + wave_u * G::UPT * 1024;
     const uint32_t vl = kl + G::TILE_BYTES;
-    const bool whole = k0 + BN <= Ttot;
+    const bool whole = k0 + BN <= Tk;
 #pragma unroll
     for (int i = 0; i < G::UPT; ++i) {
-      const int back = whole ? 0 : max(k0 + unit_row[i] - (Ttot - 1), 0) * (int)kv_row_stride;
+      const int back = whole ? 0 : max(k0 + unit_row[i] - (Tk - 1), 0) * (int)kv_row_stride;
       dma16(kt + unit_off[i] - back, kl + i * 1024);
       dma16(vt + unit_off[i] - back, vl + i * 1024);
     }
@@ -527,16 +580,8 @@ void prefill_fwd_kernel(
   // so that the first K/V loads go out together with the Q loads
   int kt0;
   {
-    int a = 0, bnd = ndocs + 1;  // upper_bound over cu: first d with cu[d] > q0
-    while (a < bnd) {
-      const int mid = (a + bnd) >> 1;
-      const int c = cu_in_lds ? cu_s[mid] : cu[mid];
-      if (c > q0) bnd = mid; else a = mid + 1;
-    }
-    const int doc = a - 1;
-    int ds = (doc >= 0 && doc < ndocs) ? (cu_in_lds ? cu_s[doc] : cu[doc]) : q0;
-    ds = min(max(ds, 0), q0);
-    const int lo0 = (W > 0) ? max(ds, q0 - W + 1) : ds;
+    const RowKeys rk = row_keys(cu_s, cukl, cu, cuk, cu_in_lds, ndocs, q0, Tk);
+    const int lo0 = (W > 0) ? max(rk.ds, rk.kp - W + 1) : rk.ds;
     kt0 = __builtin_amdgcn_readfirstlane((lo0 / BN) * BN);
   }
   // pipelined layout: K ring of STAGES tiles, then V ring of STAGES tiles
@@ -545,12 +590,12 @@ void prefill_fwd_kernel(
 #pragma unroll
   for (int i = 0; i < G::UPT; ++i) voff[i] = unit_off[i] * (int)sizeof(T);
   // one K or V tile (keys k0 .. k0+BN-1 of this kv head) into an LDS stage;
-  // rows at or past Ttot fall outside the buffer and arrive as zeros
+  // key rows at or past Tk fall outside the buffer and arrive as zeros
   // descriptor of one K or V tile; `want` false gives an empty buffer, whose
   // loads fetch nothing and fill their LDS slots with zeros
   auto tile_rsrc = [&](const T* tb, int k0, bool want = true) {
     const T* p0 = tb + (size_t)k0 * kv_row_stride;
-    const long long rem = (long long)(Ttot - k0) * (long long)kv_row_stride * (long long)sizeof(T);
+    const long long rem = (long long)(Tk - k0) * (long long)kv_row_stride * (long long)sizeof(T);
     const uint32_t nrec = (rem <= 0 || !want) ? 0u : (rem > 0xffffffffLL ? 0xffffffffu : (uint32_t)rem);
     return make_buffer_rsrc(p0, nrec);
   };
@@ -594,29 +639,25 @@ void prefill_fwd_kernel(
   constexpr bool kDiagRef = PL && D == 128;
 
   // ---- prologue: per-row key interval [lo_i, hi_i] ------------------------
-  int my_de = 0;
+  // (intervals are key positions: row i sits at key position kp, equal to
+  // i unless the query rows are a chunk of longer documents)
+  int my_de = 0, my_kp = 0;
   if (tid < G::BM) {
     const int i = q0 + tid;
     int lo = 1, hi = 0;  // empty interval for rows past the end
     if (i < Ttot) {
-      int a = 0, bnd = ndocs + 1;  // upper_bound over cu: first d with cu[d] > i
-      while (a < bnd) {
-        const int mid = (a + bnd) >> 1;
-        const int c = cu_in_lds ? cu_s[mid] : cu[mid];
-        if (c > i) bnd = mid; else a = mid + 1;
-      }
-      const int doc = a - 1;
-      int ds = (doc >= 0 && doc < ndocs) ? (cu_in_lds ? cu_s[doc] : cu[doc]) : i;
-      int de = (doc >= 0 && doc < ndocs) ? (cu_in_lds ? cu_s[doc + 1] : cu[doc + 1]) : i + 1;
-      ds = min(max(ds, 0), i);  // clamp against malformed cu_seqlens
-      de = max(min(de, Ttot), i + 1);
-      lo = (W > 0) ? max(ds, i - W + 1) : ds;
-      hi = i;
-      my_de = de;
+      const RowKeys rk = row_keys(cu_s, cukl, cu, cuk, cu_in_lds, ndocs, i, Tk);
+      lo = (W > 0) ? max(rk.ds, rk.kp - W + 1) : rk.ds;
+      hi = rk.kp;
+      my_de = rk.de;
+      my_kp = rk.kp;
     }
     lo_s[tid] = lo;
     hi_s[tid] = hi;
-    if (tid == G::BM - 1) de_last_s = my_de;
+    if (tid == G::BM - 1) {
+      de_last_s = my_de;
+      kp_last_s = my_kp;
+    }
   }
   if (mode == SWA_BLOCKWISE) {
     // last_of_run(t): t is the final token of its run of equal ids in its
@@ -625,9 +666,9 @@ void prefill_fwd_kernel(
     int my_id = -1;
     if (tid < G::BM) {
       const int i = q0 + tid;
-      if (i < Ttot) {
-        my_id = ids[i];
-        lr = (i + 1 >= my_de) || (ids[i + 1] != my_id);
+      if (i < Ttot && my_kp < Tk) {
+        my_id = ids[my_kp];
+        lr = (my_kp + 1 >= my_de) || (ids[my_kp + 1] != my_id);
       }
     }
     const unsigned long long bal = __ballot(lr);
@@ -637,12 +678,13 @@ void prefill_fwd_kernel(
     // the last run of the tile may continue past it: wave 0 scans ahead
     if (wave == 0) {
       const int last = q0 + G::BM - 1;
-      const bool open_run = last < Ttot && ids[last] >= 0 &&
+      const int kp_last = kp_last_s;  // key position of the tile's last row
+      const bool open_run = last < Ttot && kp_last < Tk && ids[kp_last] >= 0 &&
                             !((runmask_s[(G::BM - 1) / 64] >> ((G::BM - 1) & 63)) & 1ull);
       if (open_run) {
-        const int run_id = ids[last];
-        const int de = de_last_s;  // document end of the tile's last row
-        int base = last + 1;
+        const int run_id = ids[kp_last];
+        const int de = de_last_s;  // document key end of the tile's last row
+        int base = kp_last + 1;
         int found = -1;
         while (found < 0) {  // terminates: t >= de always ends the run
           const int t = base + lane;
@@ -664,7 +706,8 @@ void prefill_fwd_kernel(
         if (m) end = ww * 64 + __builtin_ctzll(m);
       }
       if (end >= G::BM) end = -1;  // bits past the tile belong to no row
-      hi_s[tid] = end >= 0 ? q0 + end : ext_end_s;
+      // (the run's last row is in this row's document: same key offset)
+      hi_s[tid] = end >= 0 ? my_kp + (end - tid) : ext_end_s;
     }
   }
   __syncthreads();

@@ -9,12 +9,10 @@
 namespace swa {
 
 template <int D, typename T, int MB, int BN, int NW, int GH, bool PL = false>
-int launch_prefill_cfg(const void* q, const void* k, const void* v,
-                       const int32_t* cu, const int32_t* ids, int window,
-                       int mode, void* out, int total_tokens, int num_docs,
-                       int hq, int hkv, float scale, hipStream_t stream) {
+int launch_prefill_cfg(const PrefillArgs& a) {
   using G = PfGeom<D, T, MB, BN, NW, GH, PL>;
-  const int ntiles = (total_tokens + G::BM - 1) / G::BM;
+  const int ntiles = (a.total_q + G::BM - 1) / G::BM;
+  const int hq = a.hq, hkv = a.hkv;
   const int g = hq / hkv;
   const long long nwork = (long long)ntiles * hkv * (g / GH);
   const long long per_xcd = (nwork + 7) / 8;  // 8 XCDs, blocks round-robin over them
@@ -31,24 +29,17 @@ int launch_prefill_cfg(const void* q, const void* k, const void* v,
     colocated = kWgPerCu == 2 && slots == fill;  // two work-groups on every CU
   }
   hipLaunchKernelGGL((prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL>), dim3((unsigned)(8 * slots)),
-                     dim3(G::NT), 0, stream, (const T*)q, (const T*)k, (const T*)v, cu,
-                     num_docs, ids, window, mode, (T*)out, total_tokens, hq, hkv,
-                     scale * kPrefillLog2e, ntiles, (int)nwork, (int)per_xcd, slots, colocated);
+                     dim3(G::NT), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                     a.cu_q, a.cu_k, a.num_docs, a.ids, a.window, a.mode, (T*)a.out, a.total_q,
+                     a.total_k, hq, hkv, a.scale * kPrefillLog2e, ntiles, (int)nwork,
+                     (int)per_xcd, slots, colocated);
   return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
 }
 
 // One translation unit per head dimension keeps compile times parallel.
-int launch_prefill_d64(const void* q, const void* k, const void* v, const int32_t* cu,
-                       const int32_t* ids, int window, int mode, void* out, int total_tokens,
-                       int num_docs, int hq, int hkv, int dtype, float scale, hipStream_t s);
-int launch_prefill_d128(const void* q, const void* k, const void* v, const int32_t* cu,
-                        const int32_t* ids, int window, int mode, void* out, int total_tokens,
-                        int num_docs, int hq, int hkv, int dtype, float scale, hipStream_t s);
-int launch_prefill_d256(const void* q, const void* k, const void* v, const int32_t* cu,
-                        const int32_t* ids, int window, int mode, void* out, int total_tokens,
-                        int num_docs, int hq, int hkv, int dtype, float scale, hipStream_t s);
-int launch_prefill_d512(const void* q, const void* k, const void* v, const int32_t* cu,
-                        const int32_t* ids, int window, int mode, void* out, int total_tokens,
-                        int num_docs, int hq, int hkv, int dtype, float scale, hipStream_t s);
+int launch_prefill_d64(const PrefillArgs& a);
+int launch_prefill_d128(const PrefillArgs& a);
+int launch_prefill_d256(const PrefillArgs& a);
+int launch_prefill_d512(const PrefillArgs& a);
 
 }  // namespace swa

@@ -42,11 +42,22 @@ int launch_decode(const void* q, const void* k_new, const void* v_new, void* k_r
 // Compute units of the current device (queried once per device).
 int device_cu_count();
 
-// Prefill.
-int launch_prefill(const void* q, const void* k, const void* v,
-                   const int32_t* cu, const int32_t* ids, int window,
-                   int mode, void* out, int total_tokens, int num_docs,
-                   int hq, int hkv, int d, int dtype, float scale,
-                   hipStream_t stream);
+// Prefill.  Query rows are the last rows of each document's keys: cu_k ==
+// cu_q (and total_k == total_q) for whole prompts, per-document longer key
+// ranges for a chunk of each prompt.
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* ids;  // key-indexed block ids (SWA_BLOCKWISE), else NULL
+  int window, mode;
+  void* out;
+  int total_q, total_k, num_docs, hq, hkv, d, dtype;
+  float scale;
+  hipStream_t stream;
+};
+int launch_prefill(const PrefillArgs& a);
 
 }  // namespace swa

@@ -70,6 +70,33 @@ def test_prefill_rejects(kw, code):
     assert _prefill(**kw) == code
 
 
+def _prefill_chunk(**kw):
+    a = dict(q=A, k=A, v=A, cuq=B, cuk=B, ids=None, window=0, mode=0, out=A, Tq=10, Tk=20,
+             nd=1, hq=4, hkv=2, d=128, dtype=0)
+    a.update(kw)
+    return _lib.lib().swa_prefill_chunk(a["q"], a["k"], a["v"], a["cuq"], a["cuk"], a["ids"],
+                                        a["window"], a["mode"], a["out"], a["Tq"], a["Tk"],
+                                        a["nd"], a["hq"], a["hkv"], a["d"], a["dtype"], 0.0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cuk=None), _lib.SWA_EINVAL),
+    (dict(cuq=None), _lib.SWA_EINVAL),
+    (dict(Tk=0), _lib.SWA_EINVAL),
+    (dict(Tk=-1), _lib.SWA_EINVAL),
+    (dict(d=96), _lib.SWA_EUNSUPPORTED),
+    (dict(mode=1), _lib.SWA_EINVAL),
+    (dict(mode=2), _lib.SWA_EUNSUPPORTED),
+    (dict(k=A + 2), _lib.SWA_EINVAL),
+])
+def test_prefill_chunk_rejects(kw, code):
+    assert _prefill_chunk(**kw) == code
+
+
+def test_prefill_chunk_empty_is_a_no_op():
+    assert _prefill_chunk(Tq=0, q=None, out=None) == _lib.SWA_OK
+
+
 def test_prefill_empty_is_a_no_op():
     assert _prefill(T=0, q=None, k=None, v=None, out=None, cu=None) == _lib.SWA_OK
 

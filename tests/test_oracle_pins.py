@@ -279,6 +279,110 @@ def test_rows_subset_equals_full():
     np.testing.assert_array_equal(orc.prefill(q, k, v, c.cu_seqlens, None, c.window, CAUSAL, rows=rows), full[rows])
 
 
+# ----------------------------------------------------------------- chunked prefill
+def _brute_force_chunk(q, k, v, cu_q, cu_k, ids, W, mode):
+    """Dense (query row x key row) mask in key positions: query row i of
+    document b sits at position len_k - len_q + i of b; a dense fp64 softmax
+    over all key rows."""
+    Tq, hq, D = q.shape
+    Tk = k.shape[0]
+    g = hq // k.shape[1]
+    cu_q, cu_k = np.asarray(cu_q), np.asarray(cu_k)
+    kdoc = np.searchsorted(cu_k, np.arange(Tk), side="right") - 1
+    qdoc = np.searchsorted(cu_q, np.arange(Tq), side="right") - 1
+    qpos = np.arange(Tq) - cu_q[qdoc] + (cu_k[qdoc + 1] - cu_k[qdoc]) - (cu_q[qdoc + 1] - cu_q[qdoc])
+    qkey = cu_k[qdoc] + qpos  # key row of each query
+    run = np.zeros(Tk, np.int64)
+    for t in range(1, Tk):
+        run[t] = run[t - 1] + int(ids[t] != ids[t - 1] or kdoc[t] != kdoc[t - 1])
+    i = qkey[:, None]
+    j = np.arange(Tk)[None, :]
+    m = qdoc[:, None] == kdoc[None, :]
+    if W > 0:
+        m &= (i - j) < W
+    fut = np.zeros((Tq, Tk), bool)
+    if mode == BLOCKWISE:
+        fut = (ids[qkey][:, None] >= 0) & (run[qkey][:, None] == run[None, :])
+    m &= (j <= i) | fut
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    out = np.zeros((Tq, hq, D))
+    for h in range(hq):
+        s = qf[:, h, :] @ kf[:, h // g, :].T / math.sqrt(D)
+        s = np.where(m, s, -np.inf)
+        mx = s.max(axis=1, keepdims=True)
+        mx = np.where(np.isfinite(mx), mx, 0.0)
+        p = np.exp(s - mx)
+        l = p.sum(axis=1, keepdims=True)
+        out[:, h, :] = np.where(l > 0, (p @ vf[:, h // g, :]) / np.where(l > 0, l, 1), 0.0)
+    return out
+
+
+@pytest.mark.parametrize("trial", range(8))
+def test_chunk_brute_force_random_tiny(trial):
+    """Chunks of random length (0 .. len_k) of random documents, both modes:
+    the chunk oracle == a dense key-position mask within 1e-12."""
+    rng = si.rng_for(5000 + trial)
+    nd = int(rng.integers(1, 4))
+    lk = rng.integers(1, 30, size=nd)
+    lq = np.array([int(rng.integers(0, x + 1)) for x in lk])
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    Tk, Tq = int(cu_k[-1]), int(cu_q[-1])
+    hkv, g, D = int(rng.choice([1, 2])), int(rng.choice([1, 2])), 8
+    ids = np.full(Tk, -1, np.int32)
+    for b in range(int(rng.integers(0, 4))):
+        s0 = int(rng.integers(0, Tk))
+        ids[s0:min(Tk, s0 + int(rng.integers(1, 10)))] = b
+    q = _rand((Tq, hkv * g, D), 6000 + trial, "bf16")
+    k = _rand((Tk, hkv, D), 7000 + trial, "bf16")
+    v = _rand((Tk, hkv, D), 8000 + trial, "bf16")
+    for W in (1, 3, 7, 0):
+        for mode in (CAUSAL, BLOCKWISE):
+            got = orc.prefill_chunk(q, k, v, cu_q, cu_k, ids, W, mode)
+            want = _brute_force_chunk(q, k, v, cu_q, cu_k, ids, W, mode)
+            np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_causal_chunk_equals_rows_of_the_whole_document():
+    """CAUSAL: a chunk at positions o .. o+c-1 of a document, against keys
+    0 .. o+c-1, gives the rows o .. o+c-1 of the prefill of the WHOLE
+    document (the later keys are never allowed), for any window."""
+    hq, hkv, D = 4, 2, 16
+    L = 70
+    q = _rand((L, hq, D), 91, "bf16")
+    k = _rand((L, hkv, D), 92, "bf16")
+    v = _rand((L, hkv, D), 93, "bf16")
+    for W in (0, 1, 9, 33):
+        whole = orc.prefill(q, k, v, np.array([0, L], np.int32), None, W, CAUSAL)
+        for o, c in ((0, 70), (0, 10), (10, 25), (50, 20), (69, 1)):
+            got = orc.prefill_chunk(q[o:o + c], k[:o + c], v[:o + c], [0, c], [0, o + c],
+                                    None, W, CAUSAL)
+            np.testing.assert_array_equal(got, whole[o:o + c])
+
+
+def test_chunk_blockwise_cuts_image_at_cache_end():
+    """BLOCKWISE: a chunk whose last image run continues past the cached keys
+    sees only the cached part of it: its rows equal those of the prefill of
+    the document cut at the cache end, and differ from the whole document's
+    rows (which see the image's later tokens)."""
+    hq, hkv, D, W = 2, 1, 8, 0
+    L = 20
+    ids = np.full(L, -1, np.int32)
+    ids[8:16] = 0  # one image, tokens 8..15
+    q = _rand((L, hq, D), 94, "bf16")
+    k = _rand((L, hkv, D), 95, "bf16")
+    v = _rand((L, hkv, D), 96, "bf16")
+    o, c = 6, 6  # queries 6..11, keys 0..11: the image is cut after token 11
+    got = orc.prefill_chunk(q[o:o + c], k[:o + c], v[:o + c], [0, c], [0, o + c], ids[:o + c],
+                            W, BLOCKWISE)
+    cut = orc.prefill(q[:o + c], k[:o + c], v[:o + c], np.array([0, o + c], np.int32),
+                      ids[:o + c], W, BLOCKWISE)
+    whole = orc.prefill(q, k, v, np.array([0, L], np.int32), ids, W, BLOCKWISE)
+    np.testing.assert_array_equal(got, cut[o:])
+    assert np.abs(got[2:] - whole[o + 2:o + c]).max() > 1e-3  # image rows 8..11 differ
+    np.testing.assert_array_equal(got[:2], whole[o:o + 2])  # text rows 6, 7 do not
+
+
 # ----------------------------------------------------------------- decode on a linear cache
 def test_decode_linear_equals_prefill_last_row():
     """Decode of the token at position pos with left pad lo equals the
