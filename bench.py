@@ -157,6 +157,32 @@ def bench_prefill(name, steps, warmup, torch, api, nsets=None):
     }
 
 
+def bench_prefill_chunked(name, nchunks, steps, warmup, torch, api):
+    """The workload's single document prefilled in `nchunks` equal chunks
+    (swa_prefill_chunk: chunk j's queries against keys 0 .. end of chunk j),
+    one after another; useful work equals the whole-prompt prefill's."""
+    c = si.PREFILL_WORKLOADS[name]()
+    assert c.cu_seqlens.size == 2 and c.T % nchunks == 0 and c.ids is None
+    q, k, v = c.tensors("bf16")
+    qd, kd, vd = to_dev(q, torch), to_dev(k, torch), to_dev(v, torch)
+    out = torch.empty_like(qd)
+    L = c.T // nchunks
+    cuq = to_dev(np.array([0, L], np.int32), torch)
+    cuks = [to_dev(np.array([0, (j + 1) * L], np.int32), torch) for j in range(nchunks)]
+
+    def step(i):
+        for j in range(nchunks):
+            e = (j + 1) * L
+            api.prefill_chunk(qd[j * L:e], kd[:e], vd[:e], cuq, cuks[j], None, c.window, c.mode,
+                              out=out[j * L:e])
+
+    ms = time_loop(step, steps, warmup, torch)
+    fl = useful_flops(c)
+    return {"workload": name + "_in_%d_chunks" % nchunks, "chunk_tokens": L, "useful_flop": fl,
+            "ms_per_prompt": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
     """Append + decode per step over `layers` independent ring sets (one per
     simulated sliding layer).  The roll is issued before every A-th append
@@ -453,6 +479,10 @@ def main():
             print("%s: %.3f ms, %.1f TFLOP/s" % (name, workloads[name]["ms_per_call"],
                                                  workloads[name]["tflops"]), file=sys.stderr,
                   flush=True)
+        ch = bench_prefill_chunked("prefill_16k_gqa_d512", 8, 5, 2, torch, api)
+        workloads[ch["workload"]] = ch
+        print("%s: %.3f ms, %.1f TFLOP/s" % (ch["workload"], ch["ms_per_prompt"], ch["tflops"]),
+              file=sys.stderr, flush=True)
         for name in ("decode_b64_d256", "decode_single_d256"):
             workloads[name] = bench_decode(name, torch, api)
             print("%s: %.2f us/step, fused %.2f us/step (graph %.2f), decode %.2f us, %.0f GB/s" % (
