@@ -474,7 +474,7 @@ def main():
           file=sys.stderr, flush=True)
     workloads = {HEADLINE: head}
     if not args.only_headline:
-        for name in ("prefill_16k_gqa_d512", "prefill_vlm_4096_d256"):
+        for name in ("prefill_16k_gqa_d512", "prefill_vlm_4096_d256", "prefill_4x1024_gqa_d320"):
             workloads[name] = bench_prefill(name, max(5, args.steps // 5), 3, torch, api)
             print("%s: %.3f ms, %.1f TFLOP/s" % (name, workloads[name]["ms_per_call"],
                                                  workloads[name]["tflops"]), file=sys.stderr,

@@ -17,13 +17,15 @@ namespace {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool supported_d(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+// prefill also takes head dimension 320
+bool supported_prefill_d(int32_t d) { return supported_d(d) || d == 320; }
 
 size_t elem_size(int32_t dtype) { return dtype == SWA_BF16 ? 2 : 4; }
 
 // Shared checks of the head geometry and element type.
-int check_heads(int32_t hq, int32_t hkv, int32_t d, int32_t dtype) {
+int check_heads(int32_t hq, int32_t hkv, int32_t d, int32_t dtype, bool prefill = false) {
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return SWA_EINVAL;
-  if (!supported_d(d)) return SWA_EUNSUPPORTED;
+  if (!(prefill ? supported_prefill_d(d) : supported_d(d))) return SWA_EUNSUPPORTED;
   if (dtype != SWA_BF16 && dtype != SWA_F32) return SWA_EUNSUPPORTED;
   return SWA_OK;
 }
@@ -96,7 +98,7 @@ SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
                               int32_t causal_mode, void* out, int32_t total_q,
                               int32_t total_k, int32_t num_docs, int32_t hq, int32_t hkv,
                               int32_t d, int32_t dtype, float scale, void* stream) {
-  int rc = check_heads(hq, hkv, d, dtype);
+  int rc = check_heads(hq, hkv, d, dtype, true);
   if (rc) return rc;
   if (total_q < 0 || total_k < 0 || num_docs < 0) return SWA_EINVAL;
   if (causal_mode != SWA_CAUSAL && causal_mode != SWA_BLOCKWISE) return SWA_EUNSUPPORTED;

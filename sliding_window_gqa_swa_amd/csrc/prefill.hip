@@ -11,6 +11,8 @@ int launch_prefill(const PrefillArgs& a) {
       return launch_prefill_d128(a);
     case 256:
       return launch_prefill_d256(a);
+    case 320:
+      return launch_prefill_d320(a);
     case 512:
       return launch_prefill_d512(a);
     default:

@@ -80,17 +80,24 @@ constexpr int kPlanMaxItems = 65536;
 // 2 per row, which gives the bank pattern of a 32-byte row padding (the
 // 16-row K fragment reads and the transposed V reads are conflict-free)
 // while every row stays 16-byte contiguous for the DMA.  Rows of 8 chunks
-// use an XOR pattern instead.
+// use an XOR pattern instead, and so does the 8-chunk tail of a row whose
+// length is 8 more than a multiple of 16 chunks (head dimension 320).
+__device__ __forceinline__ int chunk_xor8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 template <int CPR>
 __device__ __forceinline__ int chunk_pos(int r, int ch) {
-  if constexpr (CPR >= 16) return (ch & ~15) | ((ch + 2 * r) & 15);
-  else return ch ^ (((r & 3) << 1) | ((r >> 2) & 1));
+  static_assert(CPR % 16 == 0 || CPR % 16 == 8, "rows of 16k or 16k + 8 chunks");
+  constexpr int FULL = CPR & ~15;
+  if constexpr (CPR % 16 == 0) return (ch & ~15) | ((ch + 2 * r) & 15);
+  else if constexpr (FULL == 0) return ch ^ chunk_xor8(r);
+  else return ch < FULL ? ((ch & ~15) | ((ch + 2 * r) & 15)) : FULL + ((ch - FULL) ^ chunk_xor8(r));
 }
 // inverse: the chunk stored at position pc of row r
 template <int CPR>
 __device__ __forceinline__ int chunk_src(int r, int pc) {
-  if constexpr (CPR >= 16) return (pc & ~15) | ((pc - 2 * r) & 15);
-  else return pc ^ (((r & 3) << 1) | ((r >> 2) & 1));
+  constexpr int FULL = CPR & ~15;
+  if constexpr (CPR % 16 == 0) return (pc & ~15) | ((pc - 2 * r) & 15);
+  else if constexpr (FULL == 0) return pc ^ chunk_xor8(r);
+  else return pc < FULL ? ((pc & ~15) | ((pc - 2 * r) & 15)) : FULL + ((pc - FULL) ^ chunk_xor8(r));
 }
 
 // One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from g land at

@@ -40,6 +40,7 @@ int launch_prefill_cfg(const PrefillArgs& a) {
 int launch_prefill_d64(const PrefillArgs& a);
 int launch_prefill_d128(const PrefillArgs& a);
 int launch_prefill_d256(const PrefillArgs& a);
+int launch_prefill_d320(const PrefillArgs& a);
 int launch_prefill_d512(const PrefillArgs& a);
 
 }  // namespace swa

@@ -127,10 +127,19 @@ def prefill_vlm_4096_d256() -> PrefillCase:
                        ids=image_block_ids(4096, 8, 256, seed=5), seed=5)
 
 
+def prefill_4x1024_gqa_d320() -> PrefillCase:
+    """The packed 4 x 1024-token causal shape with the non-power-of-two head
+    size 320 ([SDPA] Test plan) and GQA 16/8."""
+    return PrefillCase("prefill_4x1024_gqa_d320",
+                       np.array([0, 1024, 2048, 3072, 4096], dtype=np.int32),
+                       hq=16, hkv=8, d=320, window=1024, mode=CAUSAL, seed=6)
+
+
 PREFILL_WORKLOADS = {
     "prefill_4x1024_mha_d128": prefill_4x1024_mha_d128,
     "prefill_16k_gqa_d512": prefill_16k_gqa_d512,
     "prefill_vlm_4096_d256": prefill_vlm_4096_d256,
+    "prefill_4x1024_gqa_d320": prefill_4x1024_gqa_d320,
 }
 
 

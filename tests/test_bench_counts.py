@@ -18,6 +18,9 @@ def test_useful_flops_of_the_prefill_workloads():
     assert bench.useful_flops(si.prefill_4x1024_mha_d128()) == 34393292800
     assert bench.useful_flops(si.prefill_16k_gqa_d512()) == 1924212457472
     assert bench.useful_flops(si.prefill_vlm_4096_d256()) == 32208060416
+    # 4 documents x 524,800 causal pairs (the window covers each document),
+    # 16 heads, 4 * 320 flop per pair
+    assert bench.useful_flops(si.prefill_4x1024_gqa_d320()) == 4 * 524800 * 16 * 4 * 320
 
 
 def test_decode_valid_rows():

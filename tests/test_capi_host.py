@@ -54,7 +54,8 @@ def _prefill(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d=100), _lib.SWA_EUNSUPPORTED),
-    (dict(d=320), _lib.SWA_EUNSUPPORTED),
+    (dict(d=96), _lib.SWA_EUNSUPPORTED),
+    (dict(d=384), _lib.SWA_EUNSUPPORTED),
     (dict(dtype=7), _lib.SWA_EUNSUPPORTED),
     (dict(mode=2), _lib.SWA_EUNSUPPORTED),
     (dict(hq=3, hkv=2), _lib.SWA_EINVAL),
@@ -91,6 +92,15 @@ def _prefill_chunk(**kw):
 ])
 def test_prefill_chunk_rejects(kw, code):
     assert _prefill_chunk(**kw) == code
+
+
+def test_head_320_is_a_prefill_size_only():
+    """d = 320 passes the prefill checks (an empty call returns OK after
+    them) and is refused by decode."""
+    assert _prefill_chunk(d=320, Tq=0, q=None, out=None) == _lib.SWA_OK
+    assert _prefill_chunk(d=320, cuk=None) == _lib.SWA_EINVAL  # checked past the size
+    assert _decode(d=320) == _lib.SWA_EUNSUPPORTED
+    assert _decode_step(d=320) == _lib.SWA_EUNSUPPORTED
 
 
 def test_prefill_chunk_empty_is_a_no_op():

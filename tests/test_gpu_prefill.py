@@ -46,7 +46,7 @@ def _run(q, k, v, cu, ids, W, mode, dtype):
 
 
 CASES = []
-for d in (64, 128, 256, 512):
+for d in (64, 128, 256, 320, 512):
     for dtype in ("bf16", "f32"):
         for mode in (CAUSAL, BLOCKWISE):
             CASES.append((d, dtype, mode))
@@ -71,7 +71,7 @@ def test_prefill_small_ragged(d, dtype, mode):
         assert_close(got, want, dtype, "d=%d %s mode=%d W=%d" % (d, dtype, mode, W))
 
 
-@pytest.mark.parametrize("d", [128, 256, 512])
+@pytest.mark.parametrize("d", [128, 256, 320, 512])
 @pytest.mark.parametrize("mode", [CAUSAL, BLOCKWISE])
 def test_prefill_odd_group(d, mode):
     """Three query heads per kv head: work-groups that hold one query head
@@ -91,7 +91,7 @@ def test_prefill_odd_group(d, mode):
         assert_close(got, want, "bf16", "odd group d=%d mode=%d W=%d" % (d, mode, W))
 
 
-@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("d", [64, 128, 256, 320, 512])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_window_one_is_exact(d, dtype):
     """W = 1: every row attends only to itself, so out = v[i] bit for bit."""

@@ -33,7 +33,8 @@ def _ragged_chunks(rng, d):
     return cu_q, cu_k
 
 
-CASES = [(d, dt, m) for d in (64, 128, 256, 512) for dt in ("bf16", "f32") for m in (CAUSAL, BLOCKWISE)]
+CASES = [(d, dt, m) for d in (64, 128, 256, 320, 512) for dt in ("bf16", "f32")
+         for m in (CAUSAL, BLOCKWISE)]
 
 
 @pytest.mark.parametrize("d,dtype,mode", CASES)
