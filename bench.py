@@ -395,10 +395,14 @@ def summarize_trace(trace_dir):
     if not dbs:
         raise SystemExit("no rocprofv3 database under %s" % trace_dir)
     cur = sqlite3.connect(dbs[0]).cursor()
+    # (grouped by the mangled symbol: the trace's display names drop template
+    # arguments of some kernels)
     rows = cur.execute(
-        "select name, grid_x, workgroup_x, count(*), sum(duration), avg(duration), "
-        "min(duration), max(duration) from kernels group by name, grid_x "
-        "order by sum(duration) desc").fetchall()
+        "select coalesce(s.kernel_name, k.name), k.grid_x, k.workgroup_x, count(*), "
+        "sum(k.duration), avg(k.duration), min(k.duration), max(k.duration) from kernels k "
+        "left join kernel_symbols s on s.kernel_id = k.kernel_id "
+        "group by coalesce(s.kernel_name, k.name), k.grid_x "
+        "order by sum(k.duration) desc").fetchall()
     tot = sum(r[4] for r in rows) or 1
 
     def short(nm):
@@ -407,10 +411,11 @@ def summarize_trace(trace_dir):
             return "prefill_fwd_kernel<D=%s,%s,MB=%s,BN=%s,NW=%s,GH=%s%s>" % (
                 m.group(1), "bf16" if m.group(2) == "DF16b" else "f32", m.group(3), m.group(4),
                 m.group(5), m.group(6), ",pipelined" if m.group(7) == "1" else "")
-        m = re.search(r"decode_split_kernelILi(\d+)E(DF16b|f)Li(\d+)E", nm)
+        m = re.search(r"decode_split_kernelILi(\d+)E(DF16b|f)Li(\d+)ELb(\d)", nm)
         if m:
-            return "decode_split_kernel<D=%s,%s,GB=%s>" % (
-                m.group(1), "bf16" if m.group(2) == "DF16b" else "f32", m.group(3))
+            return "decode_split_kernel<D=%s,%s,GB=%s%s>" % (
+                m.group(1), "bf16" if m.group(2) == "DF16b" else "f32", m.group(3),
+                ",step" if m.group(4) == "1" else "")
         m = re.search(r"(ring_\w+_kernel)", nm)
         if m:
             return m.group(1)
