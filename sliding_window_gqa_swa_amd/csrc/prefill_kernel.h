@@ -1081,6 +1081,12 @@ void prefill_fwd_kernel(
         pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp + 1] = b1;
         // the row sum adds the same bf16 weights that multiply V
         if constexpr (kAsmS) l_part[mb] += (float)b0 + (float)b1;
+        if constexpr (kDiagRef) {  // one packed dot product with (1, 1)
+          typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+          const bf16x2v pr = {b0, b1};
+          const bf16x2v one2 = {(__bf16)1.0f, (__bf16)1.0f};
+          l_part[mb] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_part[mb], false);
+        }
       };
       auto exp_pair_pinned = [&](auto mbc, auto kbc, auto rpc) {
         exp_pair(mbc, kbc, rpc);
@@ -1175,7 +1181,7 @@ void prefill_fwd_kernel(
         constexpr int vs = j % (VLA + 1);
         lgkm_wait<4 * vahead>(vf[vs][0], vf[vs][1], vf[vs][2], vf[vs][3]);
         pv_mfmas(jc, vf[vs], pc);
-        if constexpr (!kAsmS && j % (NDT / 2) == NDT / 2 - 1) {
+        if constexpr (!kAsmS && !kDiagRef && j % (NDT / 2) == NDT / 2 - 1) {
           static_for<2>([&](auto mbc) {
             constexpr int mb = decltype(mbc)::value;
             l_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[mb][j / (NDT / 2)], l_acc[mb], 0, 0, 0);
@@ -1282,7 +1288,10 @@ void prefill_fwd_kernel(
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
           osum += (o_acc[mb][dt][0] + o_acc[mb][dt][1]) + (o_acc[mb][dt][2] + o_acc[mb][dt][3]);
-        bad |= !(l_acc[mb][0] < 0x1p64f) || !(__builtin_fabsf(osum) < INFINITY);
+        float l = l_part[mb];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        bad |= !(l < 0x1p64f) || !(__builtin_fabsf(osum) < INFINITY);
       }
       if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) plan_s[0] = 1;
       lds_barrier();
@@ -1374,7 +1383,7 @@ void prefill_fwd_kernel(
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         float l;
-        if constexpr (kAsmS) {
+        if constexpr (kAsmS || kDiagRef) {
           l = l_part[mb];
           l += __shfl_xor(l, 16, 64);
           l += __shfl_xor(l, 32, 64);
