@@ -33,6 +33,9 @@ def _load():
         lib.oracle_prefill_rows.restype = I
         lib.oracle_decode_linear.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, D, P, I]
         lib.oracle_decode_linear.restype = I
+        lib.oracle_prefill_backward.argtypes = [P, P, P, P, I, P, I, P, I, I, I, I, I, I, D,
+                                                P, I, P, I, P, P, P, I]
+        lib.oracle_prefill_backward.restype = I
         lib.oracle_count_allowed.argtypes = [P, I, P, I, I, I, I]
         lib.oracle_count_allowed.restype = ctypes.c_longlong
         lib.oracle_allowed.argtypes = [P, I, P, I, I, I, I]
@@ -122,6 +125,46 @@ def prefill_chunk(q, k, v, cu_q, cu_k, ids=None, window=0, mode=CAUSAL, scale=No
         return np.zeros((0, hq, d), dtype=np.float64)
     return prefill(full, k, v, ck.astype(np.int32), ids, window, mode, scale,
                    rows=sel.astype(np.int32), nthreads=nthreads)
+
+
+def prefill_backward(q, k, v, dout, cu_seqlens, ids=None, window=0, mode=CAUSAL,
+                     scale=None, rows=None, keys=None, nthreads=0):
+    """Gradients of the packed varlen SWA prefill, fp64.
+
+    For the loss sum(dout * out) (dout [T, Hq, D], the gradient arriving at
+    the output) returns (dq [len(rows), Hq, D], dk [len(keys), Hkv, D],
+    dv [len(keys), Hkv, D]) as float64, by the chain rule through the
+    prefill's definition (the forward recomputed per row in fp64).  ``rows``
+    selects the packed query rows of dq and ``keys`` the packed key rows of
+    dk and dv (default: all).  Inputs as for ``prefill``; dout has q's dtype.
+    """
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dout = np.ascontiguousarray(dout)
+    dt = _dtype_code(q)
+    assert _dtype_code(k) == dt and _dtype_code(v) == dt and _dtype_code(dout) == dt
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    assert k.shape == (T, hkv, d) and v.shape == (T, hkv, d) and dout.shape == q.shape
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    ids_a = None if ids is None else np.ascontiguousarray(ids, dtype=np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    keys_a = None if keys is None else np.ascontiguousarray(keys, dtype=np.int32)
+    nr = T if rows_a is None else rows_a.size
+    nk = T if keys_a is None else keys_a.size
+    dq = np.empty((nr, hq, d), dtype=np.float64)
+    dk = np.empty((nk, hkv, d), dtype=np.float64)
+    dv = np.empty((nk, hkv, d), dtype=np.float64)
+    rc = _load().oracle_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), dt, _ptr(cu), cu.size - 1, _ptr(ids_a),
+        int(window), int(mode), T, hq, hkv, d, float(scale), _ptr(rows_a), nr,
+        _ptr(keys_a), nk, _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_prefill_backward rejected its arguments (rc=%d)" % rc)
+    return dq, dk, dv
 
 
 def decode_linear(q, k_hist, v_hist, hist_off, first_pos, hist_len, pos, lo,

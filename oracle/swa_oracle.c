@@ -233,6 +233,159 @@ int oracle_decode_linear(const void* q, const void* k_lin, const void* v_lin,
   return err ? -1 : 0;
 }
 
+/* Gradient quantities of one query row (packed index i, query head h) of
+ * the prefill, in double, for the loss whose gradient with respect to the
+ * row's output is dO (dout[i, h]).  The forward is recomputed from its
+ * definition: the allowed keys j (listed in `keys`), the softmax weights
+ * p_j of the row's scores scale * <q_i, k_j>, and dp_j = <dO, v_j> (the
+ * gradient with respect to p_j, since the output is sum_j p_j v_j).
+ * `*delta` = sum_j p_j dp_j, the term the softmax's Jacobian subtracts:
+ * the gradient with respect to the score j is p_j (dp_j - delta).
+ * Returns the number of allowed keys. */
+static int row_grad_terms(const void* q, const void* k, const void* v, const void* dout,
+                          int dtype, const int32_t* cu, int ndocs, const int32_t* ids,
+                          int window, int mode, int hq, int hkv, int d, double scale,
+                          int i, int h, int* keys, double* p, double* dp, double* delta) {
+  const int g = hq / hkv, kvh = h / g;
+  const int di = doc_of(cu, ndocs, i);
+  *delta = 0.0;
+  if (di < 0) return 0;
+  const size_t qo = ((size_t)i * hq + h) * d;
+  int nk = 0;
+  double m = -INFINITY;
+  for (int j = cu[di]; j < cu[di + 1]; ++j) {
+    if (!oracle_allowed(cu, ndocs, ids, window, mode, i, j)) continue;
+    const size_t ko = ((size_t)j * hkv + kvh) * d;
+    double dot = 0.0, dov = 0.0;
+    for (int e = 0; e < d; ++e) {
+      dot += load_elem(q, dtype, qo + e) * load_elem(k, dtype, ko + e);
+      dov += load_elem(dout, dtype, qo + e) * load_elem(v, dtype, ko + e);
+    }
+    keys[nk] = j;
+    p[nk] = scale * dot;
+    dp[nk] = dov;
+    if (p[nk] > m) m = p[nk];
+    ++nk;
+  }
+  double l = 0.0;
+  for (int t = 0; t < nk; ++t) {
+    p[t] = exp(p[t] - m);
+    l += p[t];
+  }
+  double dl = 0.0;
+  for (int t = 0; t < nk; ++t) {
+    p[t] /= l;
+    dl += p[t] * dp[t];
+  }
+  *delta = dl;
+  return nk;
+}
+
+/*
+ * Backward of the packed variable-length prefill: the gradients of the
+ * loss L = sum over rows and heads of <dout[i, h], out[i, h]> with respect
+ * to q, k and v, in double, by the chain rule through the definition
+ * (out = sum_j p_j v_j, p = softmax of the scores, score_j = scale <q, k_j>):
+ *   dv[j, kvh] = sum over rows i and heads h of the group: p_ij dout[i, h]
+ *   ds_ij      = p_ij (dp_ij - delta_i)
+ *   dq[i, h]   = scale * sum_j ds_ij k[j, kvh]
+ *   dk[j, kvh] = scale * sum over rows i and heads h of the group: ds_ij q[i, h]
+ * (the GQA head map sends every query head of a group to the same K/V head,
+ * so their contributions add up).
+ *   rows: packed query rows whose dq to compute (NULL = all T), dq double[nrows, hq, d]
+ *   keys: packed key rows whose dk, dv to compute (NULL = all T), dk and dv
+ *         double[nkeys, hkv, d]
+ * Returns 0, or -1 on malformed arguments.
+ */
+int oracle_prefill_backward(const void* q, const void* k, const void* v, const void* dout,
+                            int dtype, const int32_t* cu, int ndocs, const int32_t* ids,
+                            int window, int mode, int T, int hq, int hkv, int d,
+                            double scale, const int32_t* rows, int nrows,
+                            const int32_t* keys, int nkeys, double* dq, double* dk,
+                            double* dv, int nthreads) {
+  if (hkv <= 0 || hq % hkv != 0 || d <= 0 || ndocs < 0 || T < 0) return -1;
+  if (cu[0] != 0 || cu[ndocs] != T) return -1;
+  for (int dd = 0; dd < ndocs; ++dd)
+    if (cu[dd + 1] < cu[dd]) return -1;
+  if (mode == ORACLE_BLOCKWISE && ids == NULL && T > 0) return -1;
+  const int g = hq / hkv;
+  const int nr = rows ? nrows : T, nkr = keys ? nkeys : T;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+  int err = 0;
+  const size_t cap = (size_t)(T > 0 ? T : 1);
+#pragma omp parallel
+  {
+    int* kl = (int*)malloc(sizeof(int) * cap);
+    double* p = (double*)malloc(sizeof(double) * cap);
+    double* dp = (double*)malloc(sizeof(double) * cap);
+    if (!kl || !p || !dp) {
+#pragma omp atomic write
+      err = 1;
+    }
+    /* dq: one (row, head) at a time */
+#pragma omp for schedule(dynamic, 4)
+    for (long long w = 0; w < (long long)nr * hq; ++w) {
+      if (!kl || !p || !dp) continue;
+      const int r = (int)(w / hq), h = (int)(w % hq), kvh = h / g;
+      const int i = rows ? rows[r] : r;
+      double* o = dq + ((size_t)r * hq + h) * d;
+      for (int e = 0; e < d; ++e) o[e] = 0.0;
+      if (i < 0 || i >= T) {
+        for (int e = 0; e < d; ++e) o[e] = NAN;
+        continue;
+      }
+      double delta;
+      const int nk = row_grad_terms(q, k, v, dout, dtype, cu, ndocs, ids, window, mode, hq,
+                                    hkv, d, scale, i, h, kl, p, dp, &delta);
+      for (int t = 0; t < nk; ++t) {
+        const double ds = p[t] * (dp[t] - delta);
+        const size_t ko = ((size_t)kl[t] * hkv + kvh) * d;
+        for (int e = 0; e < d; ++e) o[e] += scale * ds * load_elem(k, dtype, ko + e);
+      }
+    }
+    /* dk, dv: one (key row, kv head) at a time, gathering every (row, head)
+     * that admits the key */
+#pragma omp for schedule(dynamic, 1)
+    for (long long w = 0; w < (long long)nkr * hkv; ++w) {
+      if (!kl || !p || !dp) continue;
+      const int r = (int)(w / hkv), kvh = (int)(w % hkv);
+      const int j = keys ? keys[r] : r;
+      double* ok = dk + ((size_t)r * hkv + kvh) * d;
+      double* ov = dv + ((size_t)r * hkv + kvh) * d;
+      for (int e = 0; e < d; ++e) ok[e] = ov[e] = 0.0;
+      if (j < 0 || j >= T) {
+        for (int e = 0; e < d; ++e) ok[e] = ov[e] = NAN;
+        continue;
+      }
+      const int dj = doc_of(cu, ndocs, j);
+      if (dj < 0) continue;
+      for (int i = cu[dj]; i < cu[dj + 1]; ++i) {
+        if (!oracle_allowed(cu, ndocs, ids, window, mode, i, j)) continue;
+        for (int h = kvh * g; h < (kvh + 1) * g; ++h) {
+          double delta;
+          const int nk = row_grad_terms(q, k, v, dout, dtype, cu, ndocs, ids, window, mode,
+                                        hq, hkv, d, scale, i, h, kl, p, dp, &delta);
+          int t = 0;
+          while (t < nk && kl[t] != j) ++t;
+          if (t == nk) continue; /* cannot happen: the mask admitted j */
+          const double ds = p[t] * (dp[t] - delta);
+          const size_t qo = ((size_t)i * hq + h) * d;
+          for (int e = 0; e < d; ++e) {
+            ok[e] += scale * ds * load_elem(q, dtype, qo + e);
+            ov[e] += p[t] * load_elem(dout, dtype, qo + e);
+          }
+        }
+      }
+    }
+    free(kl);
+    free(p);
+    free(dp);
+  }
+  return err ? -1 : 0;
+}
+
 /* Number of (query, key) pairs the mask admits over the whole packed batch,
  * counted one pair at a time.  Used to pin the mask against closed forms. */
 long long oracle_count_allowed(const int32_t* cu, int ndocs, const int32_t* ids,
