@@ -144,6 +144,40 @@ SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
                               int32_t d, int32_t dtype, float scale, void* stream);
 
 /*
+ * swa_prefill_backward -- gradients of swa_prefill (whole prompts).
+ *
+ * [SDPA] Benchmarks time the attention implementations forward and
+ * backward in training at head sizes up to 512.  For the loss
+ * sum(dout * out), where out = swa_prefill(q, k, v, ...) with the same
+ * cu_seqlens, ids, window, mode and scale, this writes
+ *   dq = d loss / d q  [total_tokens, hq, d]
+ *   dk = d loss / d k  [total_tokens, hkv, d]   (summed over the hq / hkv
+ *   dv = d loss / d v  [total_tokens, hkv, d]    query heads of each group)
+ * in the element type of the inputs (bf16 rounded to nearest even).  out is
+ * the forward's output (read only for delta_i = <dout_i, out_i>, the term
+ * of the softmax's Jacobian); dout is the gradient arriving at out, laid
+ * out like q.  The softmax statistics are recomputed, so nothing else from
+ * the forward is needed.  Every output element is written exactly once,
+ * without atomics: the result is deterministic.
+ *   d: 64, 128, 256, 320 or 512 for bf16; 64, 128, 256 or 320 for fp32.
+ *   workspace: device memory of at least
+ *   swa_prefill_backward_workspace_bytes(total_tokens, hq) bytes, 16-byte
+ *   aligned, owned by the caller, contents on entry ignored (per-row
+ *   statistics and key intervals are written there); SWA_EWORKSPACE if
+ *   missing or too small.
+ *   Other arguments as for swa_prefill.  Calls sharing a workspace race
+ *   unless ordered on one stream.
+ */
+SWA_API size_t swa_prefill_backward_workspace_bytes(int32_t total_tokens, int32_t hq);
+SWA_API int swa_prefill_backward(const void* q, const void* k, const void* v, const void* out,
+                                 const void* dout, const int32_t* cu_seqlens,
+                                 const int32_t* doc_or_block_ids, int32_t window,
+                                 int32_t causal_mode, void* dq, void* dk, void* dv,
+                                 int32_t total_tokens, int32_t num_docs, int32_t hq, int32_t hkv,
+                                 int32_t d, int32_t dtype, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of workspace swa_decode needs for these sizes: split counters plus
  * fp32 split-K partials.  Depends only on the sizes, never on positions.
  */

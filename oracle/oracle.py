@@ -155,6 +155,11 @@ def prefill_backward(q, k, v, dout, cu_seqlens, ids=None, window=0, mode=CAUSAL,
     keys_a = None if keys is None else np.ascontiguousarray(keys, dtype=np.int32)
     nr = T if rows_a is None else rows_a.size
     nk = T if keys_a is None else keys_a.size
+    # an empty selection still passes a (dummy) array: NULL means "all"
+    if rows_a is not None and nr == 0:
+        rows_a = np.zeros(1, np.int32)
+    if keys_a is not None and nk == 0:
+        keys_a = np.zeros(1, np.int32)
     dq = np.empty((nr, hq, d), dtype=np.float64)
     dk = np.empty((nk, hkv, d), dtype=np.float64)
     dv = np.empty((nk, hkv, d), dtype=np.float64)

@@ -345,10 +345,36 @@ int oracle_prefill_backward(const void* q, const void* k, const void* v, const v
         for (int e = 0; e < d; ++e) o[e] += scale * ds * load_elem(k, dtype, ko + e);
       }
     }
-    /* dk, dv: one (key row, kv head) at a time, gathering every (row, head)
-     * that admits the key */
+    /* dk, dv of every key: one K/V head per thread; each (row, head) of the
+     * group adds its terms to the keys it admits */
 #pragma omp for schedule(dynamic, 1)
-    for (long long w = 0; w < (long long)nkr * hkv; ++w) {
+    for (int kvh = 0; kvh < (keys ? 0 : hkv); ++kvh) {
+      if (!kl || !p || !dp) continue;
+      for (int j = 0; j < T; ++j)
+        for (int e = 0; e < d; ++e)
+          dk[((size_t)j * hkv + kvh) * d + e] = dv[((size_t)j * hkv + kvh) * d + e] = 0.0;
+      for (int h = kvh * g; h < (kvh + 1) * g; ++h) {
+        for (int i = 0; i < T; ++i) {
+          double delta;
+          const int nk = row_grad_terms(q, k, v, dout, dtype, cu, ndocs, ids, window, mode, hq,
+                                        hkv, d, scale, i, h, kl, p, dp, &delta);
+          const size_t qo = ((size_t)i * hq + h) * d;
+          for (int t = 0; t < nk; ++t) {
+            const double ds = p[t] * (dp[t] - delta);
+            double* ok = dk + ((size_t)kl[t] * hkv + kvh) * d;
+            double* ov = dv + ((size_t)kl[t] * hkv + kvh) * d;
+            for (int e = 0; e < d; ++e) {
+              ok[e] += scale * ds * load_elem(q, dtype, qo + e);
+              ov[e] += p[t] * load_elem(dout, dtype, qo + e);
+            }
+          }
+        }
+      }
+    }
+    /* dk, dv of selected keys: one (key row, kv head) at a time, gathering
+     * every (row, head) that admits the key */
+#pragma omp for schedule(dynamic, 1)
+    for (long long w = 0; w < (keys ? (long long)nkr * hkv : 0); ++w) {
       if (!kl || !p || !dp) continue;
       const int r = (int)(w / hkv), kvh = (int)(w % hkv);
       const int j = keys ? keys[r] : r;

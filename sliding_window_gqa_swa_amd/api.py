@@ -95,6 +95,44 @@ def prefill_chunk(q, k, v, cu_seqlens_q, cu_seqlens_k, doc_or_block_ids=None, wi
     return out
 
 
+def prefill_backward_workspace_bytes(total_tokens, hq) -> int:
+    return int(_lib.lib().swa_prefill_backward_workspace_bytes(total_tokens, hq))
+
+
+def prefill_backward(q, k, v, out, dout, cu_seqlens, doc_or_block_ids=None, window=0,
+                     causal_mode=CAUSAL, dq=None, dk=None, dv=None, workspace=None, scale=0.0):
+    """Gradients (dq, dk, dv) of prefill for the loss sum(dout * out); see
+    swa_prefill_backward in swa.h.  out is prefill's output for the same
+    arguments, dout the gradient at out (both [T, Hq, D]).  Returns
+    (dq [T, Hq, D], dk [T, Hkv, D], dv [T, Hkv, D])."""
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (T, hkv, d) or v.shape != (T, hkv, d):
+        raise ValueError("k and v must be [T, Hkv, D] matching q")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must be [T, Hq, D] like q")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s dtype differs from q" % name)
+    nbytes = prefill_backward_workspace_bytes(T, hq)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    rc = _lib.lib().swa_prefill_backward(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32),
+        _dev(doc_or_block_ids, "doc_or_block_ids", torch.int32), int(window), int(causal_mode),
+        _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), T, cu_seqlens.numel() - 1, hq, hkv, d, dt,
+        float(scale), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(q))
+    _lib.check("swa_prefill_backward", rc)
+    return dq, dk, dv
+
+
 def decode_workspace_bytes(batch, hq, hkv, d, ring_rows) -> int:
     return int(_lib.lib().swa_decode_workspace_bytes(batch, hq, hkv, d, ring_rows))
 

@@ -1,0 +1,714 @@
+// bwd_kernel.h -- MFMA backward of the sliding-window GQA prefill (gfx950).
+//
+// Pages cited (title; section):
+//   [SDPA]   "Add SDPA attention implementation" (ServiceNow/Fast-LLM pull
+//            request 512): Summary (packed documents, GQA head map),
+//            Benchmarks (forward and backward timings of the attention
+//            implementations at head sizes up to 512)
+//   [SPYRE]  "Enable compact sliding-window attention for Gemma 3 and Gemma 4
+//            variants" (torch-spyre/hf-adapters pull request 496): Summary
+//            (window AND (causal OR vision-blockwise) mask)
+//
+// Gradients of the loss sum(dout * out) for out = softmax(scale Q K^T,
+// masked) V, per query head h and K/V head kvh = h / g:
+//   P      = exp2(S c - lse2_i)             (c = scale log2 e; lse2 the row's
+//                                            log2-sum-exp2 of S c)
+//   delta_i = <dout_i, out_i>                (= sum_j P_ij dP_ij)
+//   dP     = dout V^T,   dS = P (dP - delta)
+//   dq     = scale dS K,   dk = scale sum_h dS^T Q,   dv = sum_h P^T dout.
+// Three launches, no atomics (every output element is written by exactly one
+// work-group, so the result is deterministic):
+//   1. bwd_rows_kernel: the allowed key interval [lo_i, hi_i] of every row
+//      (the mask admits one contiguous interval per row, see the forward),
+//      both monotone in i;
+//   2. bwd_dq_kernel: per (query tile, head): a first pass over the key
+//      tiles gives each row's lse2 (online max and sum), a second forms
+//      S^T, dP^T, dS^T and accumulates dq^T = K^T dS^T; it also writes
+//      lse2 and delta for launch 3;
+//   3. bwd_dkdv_kernel: per (64-key tile, K/V head): each wave owns 16 keys
+//      (K and V fragments in registers) and walks the query tiles of every
+//      head of the group whose rows admit any of the 64 keys (a contiguous
+//      row range, found by binary search on the monotone intervals),
+//      accumulating dv^T += dout^T P and dk^T += Q^T dS.
+// Tiles travel HBM -> LDS by direct-to-LDS buffer loads into a 2-stage ring
+// (the next tile loads while the current one is used), with the forward's
+// chunk permutation, so the row-fragment reads (ds_read_b128) and the
+// transposed reads (ds_read_b64_tr_b16) are free of bank conflicts.
+#pragma once
+
+#include "prefill_kernel.h"
+
+namespace swa {
+
+// Tile geometry: BN rows (keys in the dq kernel, query rows in the dk/dv
+// kernel) of D elements per LDS tile, at most 32 KB per tile.
+template <int D, typename T>
+struct BwGeom {
+  using TR = PfTraits<T>;
+  static constexpr bool kF32 = std::is_same<T, float>::value;
+  static constexpr int NT = 256;                 // 4 waves
+  static constexpr int CPR = D / TR::VEC;        // 16-byte chunks per row
+  static constexpr int FRAG = kF32 ? 16 : 32;    // rows per P fragment step
+  static constexpr int RAW = 32768 / (D * (int)sizeof(T));
+  static constexpr int BN = RAW >= 64 ? 64 : (RAW / FRAG) * FRAG;
+  static constexpr int TILE_BYTES = BN * D * (int)sizeof(T);
+  static constexpr int UNITS = BN * CPR;
+  static constexpr int UPT = UNITS / NT;         // loads per thread per tile
+  static constexpr int QREG = D / TR::KW;        // fragments per 16-row block
+  static_assert(BN >= FRAG && BN % FRAG == 0, "whole fragments per tile");
+  static_assert(UNITS % NT == 0, "tile chunks split evenly over threads");
+  static_assert(2 * UPT + 4 <= 63, "loads in flight fit vmcnt");
+};
+
+// Per-row key intervals: lo[i] = max(doc start, i - W + 1) (doc start when
+// W <= 0); hi[i] = i, or the last token of i's image run when i is an image
+// token in blockwise mode (a run: consecutive tokens of one document with
+// the same non-negative id).  One wave per 64 rows; a run that continues
+// past the wave's rows is followed 64 tokens per step.
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const int32_t* __restrict__ cu, int ndocs,
+                                                       const int32_t* __restrict__ ids, int W,
+                                                       int mode, int T, int32_t* __restrict__ lo_out,
+                                                       int32_t* __restrict__ hi_out) {
+  const int lane = threadIdx.x & 63;
+  const int base = ((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * 64;
+  if (base >= T) return;  // uniform per wave
+  const int i = base + lane;
+  const bool valid = i < T;
+  int ds = i, de = i + 1;
+  if (valid) {
+    int a = 0, b = ndocs + 1;  // first d with cu[d] > i
+    while (a < b) {
+      const int m = (a + b) >> 1;
+      if (cu[m] > i) b = m; else a = m + 1;
+    }
+    const int d = a - 1;
+    if (d >= 0 && d < ndocs) {
+      ds = cu[d];
+      de = cu[d + 1];
+    }
+    ds = min(max(ds, 0), i);  // clamps against malformed offsets
+    de = max(min(de, T), i + 1);
+  }
+  const int lo = W > 0 ? max(ds, i - W + 1) : ds;
+  int hi = i;
+  if (mode == SWA_BLOCKWISE) {
+    const int id = valid ? ids[i] : -1;
+    const bool last = !valid || i + 1 >= de || ids[i + 1] != id;
+    const unsigned long long bal = __ballot(last);
+    const unsigned long long mine = bal & (~0ull << lane);
+    int end = mine ? base + __builtin_ctzll(mine) : -1;
+    // lanes with no run end at or after them share lane 63's open run
+    if (__ballot(valid && id >= 0 && end < 0)) {
+      const int rid = __builtin_amdgcn_readlane(id, 63);
+      const int rde = __builtin_amdgcn_readlane(de, 63);
+      int t0 = base + 64, found = -1;
+      while (found < 0) {  // ends: t >= rde stops the run
+        const int t = t0 + lane;
+        const bool stop = t >= rde || ids[t] != rid;
+        const unsigned long long m = __ballot(stop);
+        if (m) found = t0 + __builtin_ctzll(m) - 1;
+        t0 += 64;
+      }
+      if (end < 0) end = found;
+    }
+    if (valid && id >= 0) hi = end;
+  }
+  if (valid) {
+    lo_out[i] = lo;
+    hi_out[i] = hi;
+  }
+}
+
+// Descriptor of rows [r0, T) of a [T, heads, D] tensor at head h: row r of
+// the tile at byte offset r * heads * D * sizeof(T); rows at or past T fall
+// outside the buffer and load as zeros.
+template <typename T, int D>
+__device__ __forceinline__ i32x4 bw_rows_rsrc(const T* base, int r0, int h, int heads, int T_) {
+  const T* p0 = base + ((size_t)r0 * heads + h) * D;
+  const long long rem = (long long)(T_ - r0) * heads * D * (long long)sizeof(T);
+  const uint32_t n = rem <= 0 ? 0u : (rem > 0xffffffffLL ? 0xffffffffu : (uint32_t)rem);
+  return make_buffer_rsrc(p0, n);
+}
+
+// ---------------------------------------------------------------------------
+// dq (and lse2, delta): work-group = 64*MB query rows of one query head;
+// wave w owns rows 16*MB*w .. +16*MB.  S^T = K Q^T and dP^T = V dout^T take
+// K / V fragments from LDS and Q / dout fragments from registers (as the
+// forward's S^T); dq^T += K^T dS^T takes K^T by transposed LDS reads and
+// dS^T from the accumulator layout (as the forward's O^T += V^T P^T).
+template <int D, typename T, int MB>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ o, const T* __restrict__ dout, const int32_t* __restrict__ lo_a,
+    const int32_t* __restrict__ hi_a, int Ttot, int hq, int hkv, float c_scale, float scale,
+    int ntiles, int nwork, int per_xcd, T* __restrict__ dq, float* __restrict__ lse_out,
+    float* __restrict__ delta_out) {
+  using G = BwGeom<D, T>;
+  using TR = typename G::TR;
+  constexpr bool kF32 = G::kF32;
+  constexpr int BN = G::BN, TB = G::TILE_BYTES, WR = 16 * MB, BM = 4 * WR;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[2][2 * TB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, grp = lane >> 4;
+  // XCD-aware numbering: block b runs on XCD b % 8, which takes a
+  // contiguous slice of the work (the tiles of a few heads: their K/V rows
+  // meet in one L2)
+  const int b = (int)blockIdx.x;
+  const int slot = b >> 3;
+  const int work = (b & 7) * per_xcd + slot;
+  if (slot >= per_xcd || work >= nwork) return;  // uniform per block
+  const int h = work / ntiles;
+  const int tile = ntiles - 1 - (work - h * ntiles);  // long tiles first
+  const int q0 = tile * BM;
+  const int g = hq / hkv, kvh = h / g;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // key interval of the work-group and of this wave (monotone intervals:
+  // bounds come from the first and last rows)
+  const int last = min(q0 + BM, Ttot) - 1;
+  const int kmin = lo_a[q0], kmax = hi_a[last];
+  const int wr0 = q0 + wave_u * WR, wr1 = min(wr0 + WR, Ttot) - 1;
+  const bool wact = wr0 < Ttot;
+  const int wlo = wact ? lo_a[wr0] : 0x7fffffff, whi = wact ? hi_a[wr1] : -1;
+  const int wlomax = wact ? lo_a[wr1] : 0x7fffffff, whimin = wact ? hi_a[wr0] : -1;
+  const int kt0 = (kmin / BN) * BN;
+  // (malformed offsets could give kmax < kt0: one tile is still visited,
+  // so that every issued load is waited for)
+  const int nk = max((kmax - kt0) / BN + 1, 1);
+
+  int row_i[MB], row_lo[MB];
+  unsigned row_rng[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int i = wr0 + mb * 16 + c16;
+    row_i[mb] = i;
+    const int lo = i < Ttot ? lo_a[i] : 1, hi = i < Ttot ? hi_a[i] : 0;
+    row_lo[mb] = hi >= lo ? lo : 0x3fffffff;
+    row_rng[mb] = hi >= lo ? (unsigned)(hi - lo) : 0u;
+  }
+
+  // Q and dout fragments (B operands), and delta = <dout, out> per row
+  using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
+  QF qf[MB][G::QREG], df[MB][G::QREG];
+  float delta[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int i = row_i[mb];
+    const bool ok = i < Ttot;
+    const size_t roff = ((size_t)(ok ? i : 0) * hq + h) * D;
+    float dsum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < G::QREG; ++kk) {
+      const int d0 = kF32 ? grp * (D / 4) + kk * 4 : kk * 32 + 8 * grp;
+      QF a = QF{}, dd = QF{}, oo = QF{};
+      if (ok) {
+        a = *reinterpret_cast<const QF*>(q + roff + d0);
+        dd = *reinterpret_cast<const QF*>(dout + roff + d0);
+        oo = *reinterpret_cast<const QF*>(o + roff + d0);
+      }
+      qf[mb][kk] = a;
+      df[mb][kk] = dd;
+#pragma unroll
+      for (int e = 0; e < TR::VEC; ++e) dsum += (float)dd[e] * (float)oo[e];
+    }
+    dsum += __shfl_xor(dsum, 16, 64);
+    dsum += __shfl_xor(dsum, 32, 64);
+    delta[mb] = dsum;
+  }
+
+  // direct-to-LDS loads: slot s = (wave * UPT + u) * 64 + lane of a tile is
+  // row s / CPR, stored chunk position s % CPR (source chunk chunk_src)
+  int voff[G::UPT];
+#pragma unroll
+  for (int u = 0; u < G::UPT; ++u) {
+    const int s = (wave_u * G::UPT + u) * 64 + lane;
+    const int r = s / G::CPR, pc = s - r * G::CPR;
+    voff[u] = (r * hkv * D + chunk_src<G::CPR>(r, pc) * TR::VEC) * (int)sizeof(T);
+  }
+  const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(&ring[0][0]);
+  auto load_tile = [&](int k0, int stage, bool with_v) {
+    const uint32_t kl = ring_base + stage * 2 * TB + wave_u * G::UPT * 1024;
+    const i32x4 rk = bw_rows_rsrc<T, D>(k, k0, kvh, hkv, Ttot);
+#pragma unroll
+    for (int u = 0; u < G::UPT; ++u) dma16_buf(rk, voff[u], kl + u * 1024);
+    if (with_v) {
+      const i32x4 rv = bw_rows_rsrc<T, D>(v, k0, kvh, hkv, Ttot);
+#pragma unroll
+      for (int u = 0; u < G::UPT; ++u) dma16_buf(rv, voff[u], kl + TB + u * 1024);
+    }
+  };
+
+  // S^T of one key tile for this wave's rows, masked to -inf outside each
+  // row's interval
+  auto scores = [&](const T* Kb, int k0, floatx4 (&s)[MB][BN / 16]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb) s[mb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < G::QREG; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb) {
+        const int r = kb * 16 + c16;
+        if constexpr (kF32) {
+          const int ch = grp * (D / 16) + kk;
+          const floatx4 a = *reinterpret_cast<const floatx4*>(&Kb[(r * G::CPR + chunk_pos<G::CPR>(r, ch)) * 4]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+              s[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], qf[mb][kk][st], s[mb][kb], 0, 0, 0);
+        } else {
+          const int ch = kk * 4 + grp;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kb[(r * G::CPR + chunk_pos<G::CPR>(r, ch)) * 8]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            s[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[mb][kk], s[mb][kb], 0, 0, 0);
+        }
+      }
+    }
+    const bool full = k0 >= wlomax && k0 + BN - 1 <= whimin;
+    if (!full) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int rel0 = k0 + 4 * grp - row_lo[mb];
+#pragma unroll
+        for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            s[mb][kb][r] = (unsigned)(rel0 + kb * 16 + r) <= row_rng[mb] ? s[mb][kb][r] : -INFINITY;
+      }
+    }
+  };
+
+  auto sync_tile = [&]() {
+    wait_vmcnt<0>();  // this wave's loads of the tile have landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // ... and every wave's; the other stage is free
+    asm volatile("" ::: "memory");
+  };
+
+  // ---- pass 1: row statistics (max, then sum of exp2 relative to it) ----
+  float m_run[MB], l_part[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    m_run[mb] = -INFINITY;
+    l_part[mb] = 0.f;
+  }
+  load_tile(kt0, 0, false);
+  for (int it = 0; it < nk; ++it) {
+    const int k0 = kt0 + it * BN;
+    sync_tile();
+    if (it + 1 < nk) load_tile(k0 + BN, (it + 1) & 1, false);
+    if (!(wact && k0 <= whi && k0 + BN - 1 >= wlo)) continue;  // no key of the wave's rows
+    const T* Kb = reinterpret_cast<const T*>(&ring[it & 1][0]);
+    floatx4 s[MB][BN / 16];
+    scores(Kb, k0, s);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[mb][kb][r]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run[mb], tmax);
+      if (m_new == -INFINITY) continue;  // nothing admitted yet
+      const float alpha = m_run[mb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run[mb] - m_new) * c_scale);
+      const float mc = m_new * c_scale;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lsum += __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][kb][r], c_scale, -mc));
+      l_part[mb] = l_part[mb] * alpha + lsum;
+      m_run[mb] = m_new;
+    }
+  }
+  float lse2[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float l = l_part[mb];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    // log2 of sum_j exp2(s_j c); a row with no key gets +inf (P = 0)
+    lse2[mb] = l > 0.f ? m_run[mb] * c_scale + __builtin_log2f(l) : INFINITY;
+    const int i = row_i[mb];
+    if (grp == 0 && i < Ttot) {
+      lse_out[(size_t)h * Ttot + i] = lse2[mb];
+      delta_out[(size_t)h * Ttot + i] = delta[mb];
+    }
+  }
+
+  // ---- pass 2: dq^T += K^T dS^T -------------------------------------------
+  floatx4 acc[MB][D / 16];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // every wave is done with pass 1's stages
+  load_tile(kt0, 0, true);
+  for (int it = 0; it < nk; ++it) {
+    const int k0 = kt0 + it * BN;
+    sync_tile();
+    if (it + 1 < nk) load_tile(k0 + BN, (it + 1) & 1, true);
+    if (!(wact && k0 <= whi && k0 + BN - 1 >= wlo)) continue;
+    const T* Kb = reinterpret_cast<const T*>(&ring[it & 1][0]);
+    const T* Vb = reinterpret_cast<const T*>(&ring[it & 1][TB]);
+    floatx4 s[MB][BN / 16], dp[MB][BN / 16];
+    scores(Kb, k0, s);
+    // dP^T = V dout^T
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb) dp[mb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < G::QREG; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb) {
+        const int r = kb * 16 + c16;
+        if constexpr (kF32) {
+          const int ch = grp * (D / 16) + kk;
+          const floatx4 a = *reinterpret_cast<const floatx4*>(&Vb[(r * G::CPR + chunk_pos<G::CPR>(r, ch)) * 4]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+              dp[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], df[mb][kk][st], dp[mb][kb], 0, 0, 0);
+        } else {
+          const int ch = kk * 4 + grp;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vb[(r * G::CPR + chunk_pos<G::CPR>(r, ch)) * 8]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            dp[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, df[mb][kk], dp[mb][kb], 0, 0, 0);
+        }
+      }
+    }
+    // dS^T = P^T (dP^T - delta), P^T = exp2(S^T c - lse2)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mb][kb][r], c_scale, -lse2[mb]));
+          s[mb][kb][r] = p * (dp[mb][kb][r] - delta[mb]);
+        }
+    // dq^T += K^T dS^T
+    if constexpr (kF32) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const int d = dt * 16 + c16;
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const int r = kb * 16 + 4 * grp + st;
+            const float a = Kb[(r * G::CPR + chunk_pos<G::CPR>(r, d >> 2)) * 4 + (d & 3)];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              acc[mb][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[mb][kb][st], acc[mb][dt], 0, 0, 0);
+          }
+        }
+    } else {
+      const int tr_r = (lane & 15) >> 2, tr_m = lane & 3;
+#pragma unroll
+      for (int ks = 0; ks < BN / 32; ++ks) {
+        bf16x8 sf[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sf[mb][r] = (__bf16)s[mb][2 * ks][r];
+            sf[mb][4 + r] = (__bf16)s[mb][2 * ks + 1][r];
+          }
+        const int r0 = ks * 32 + 4 * grp + tr_r, r1 = r0 + 16;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const int ch = 2 * dt + (tr_m >> 1), off = (tr_m & 1) * 4;
+          const __bf16* p0 = &Kb[(r0 * G::CPR + chunk_pos<G::CPR>(r0, ch)) * 8 + off];
+          const __bf16* p1 = &Kb[(r1 * G::CPR + chunk_pos<G::CPR>(r1, ch)) * 8 + off];
+          const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p0));
+          const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p1));
+          const short8v x8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          const bf16x8 a = __builtin_bit_cast(bf16x8, x8);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, sf[mb], acc[mb][dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- store dq = scale dq^T: each lane holds 4 consecutive d of one row --
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int i = row_i[mb];
+    if (i >= Ttot) continue;
+    T* drow = dq + ((size_t)i * hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const floatx4 x = acc[mb][dt] * scale;
+      const int d0 = dt * 16 + 4 * grp;
+      if constexpr (kF32) {
+        *reinterpret_cast<floatx4*>(drow + d0) = x;
+      } else {
+        const bf16x4 w = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+        *reinterpret_cast<bf16x4*>(drow + d0) = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv: work-group = 64 keys of one K/V head, wave w owns keys 16w .. +16
+// (its K and V rows as B fragments in registers).  For each head of the
+// group and each query tile of BN rows that admits any of the 64 keys:
+// S = Q K^T and dP = dout V^T (Q, dout fragments from LDS), then
+// dv^T += dout^T P and dk^T += Q^T dS (dout^T, Q^T by transposed LDS reads,
+// P and dS from the accumulator layout).  Each stage also carries the
+// tile's lse2, delta, lo and hi (BN floats / ints each).
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dlt,
+    const int32_t* __restrict__ lo_a, const int32_t* __restrict__ hi_a, int Ttot, int hq,
+    int hkv, float c_scale, float scale, int nktiles, int nwork, int per_xcd,
+    T* __restrict__ dk, T* __restrict__ dv) {
+  using G = BwGeom<D, T>;
+  using TR = typename G::TR;
+  constexpr bool kF32 = G::kF32;
+  constexpr int BQ = G::BN, TB = G::TILE_BYTES, NRB = BQ / 16;
+  constexpr int META = 4096;  // lse2, delta, lo, hi: 1 KB each
+  static_assert(BQ * 4 <= 1024, "tile metadata fits its slot");
+  constexpr int STAGE = 2 * TB + META;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[2][STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, grp = lane >> 4;
+  const int b = (int)blockIdx.x;
+  const int slot = b >> 3;
+  const int work = (b & 7) * per_xcd + slot;
+  if (slot >= per_xcd || work >= nwork) return;  // uniform per block
+  const int kvh = work / nktiles;
+  const int kt = work - kvh * nktiles;
+  const int g = hq / hkv;
+  const int j0 = kt * 64;
+  const int j1 = min(j0 + 63, Ttot - 1);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wj0 = j0 + 16 * wave_u;  // this wave's first key
+  const int j = wj0 + c16;           // this lane's key (MFMA column)
+  const bool wact = wj0 < Ttot;
+
+  // rows admitting a key of [j0, j1]: hi_i >= j0 and lo_i <= j1, a
+  // contiguous range since both bounds are monotone in i
+  int i_min, i_max;
+  {
+    int a = 0, bnd = Ttot;  // first i with hi_i >= j0
+    while (a < bnd) {
+      const int m = (a + bnd) >> 1;
+      if (hi_a[m] >= j0) bnd = m; else a = m + 1;
+    }
+    i_min = a;
+    a = 0, bnd = Ttot;  // first i with lo_i > j1
+    while (a < bnd) {
+      const int m = (a + bnd) >> 1;
+      if (lo_a[m] > j1) bnd = m; else a = m + 1;
+    }
+    i_max = a - 1;
+  }
+  i_min = __builtin_amdgcn_readfirstlane(i_min);
+  i_max = __builtin_amdgcn_readfirstlane(i_max);
+  const int ntq = i_max >= i_min ? (i_max - i_min) / BQ + 1 : 0;
+  const int n = g * ntq;
+
+  // K and V fragments of this lane's key (B operands of S = Q K^T, dP = dout V^T)
+  using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
+  QF kf[G::QREG], vf[G::QREG];
+  {
+    const bool ok = j < Ttot;
+    const size_t roff = ((size_t)(ok ? j : 0) * hkv + kvh) * D;
+#pragma unroll
+    for (int kk = 0; kk < G::QREG; ++kk) {
+      const int d0 = kF32 ? grp * (D / 4) + kk * 4 : kk * 32 + 8 * grp;
+      kf[kk] = ok ? *reinterpret_cast<const QF*>(k + roff + d0) : QF{};
+      vf[kk] = ok ? *reinterpret_cast<const QF*>(v + roff + d0) : QF{};
+    }
+  }
+
+  int voff[G::UPT];
+#pragma unroll
+  for (int u = 0; u < G::UPT; ++u) {
+    const int s = (wave_u * G::UPT + u) * 64 + lane;
+    const int r = s / G::CPR, pc = s - r * G::CPR;
+    voff[u] = (r * hq * D + chunk_src<G::CPR>(r, pc) * TR::VEC) * (int)sizeof(T);
+  }
+  const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(&ring[0][0]);
+  auto load_tile = [&](int t, int stage) {
+    const int h = kvh * g + t / ntq;
+    const int i0 = i_min + (t - (t / ntq) * ntq) * BQ;
+    const uint32_t sb = ring_base + stage * STAGE;
+    const uint32_t ql = sb + wave_u * G::UPT * 1024;
+    const i32x4 rq = bw_rows_rsrc<T, D>(q, i0, h, hq, Ttot);
+    const i32x4 rd = bw_rows_rsrc<T, D>(dout, i0, h, hq, Ttot);
+#pragma unroll
+    for (int u = 0; u < G::UPT; ++u) dma16_buf(rq, voff[u], ql + u * 1024);
+#pragma unroll
+    for (int u = 0; u < G::UPT; ++u) dma16_buf(rd, voff[u], ql + TB + u * 1024);
+    if (wave_u == 0) {
+      // whole 16-byte chunks: up to 3 entries past the tile's last row are
+      // read (the workspace pads every array) and never used
+      const uint32_t nb = (uint32_t)(((min(BQ, Ttot - i0) * 4 + 15) / 16) * 16);
+      const uint32_t ml = sb + 2 * TB;
+      dma16_buf(make_buffer_rsrc(lse + (size_t)h * Ttot + i0, nb), lane * 16, ml);
+      dma16_buf(make_buffer_rsrc(dlt + (size_t)h * Ttot + i0, nb), lane * 16, ml + 1024);
+      dma16_buf(make_buffer_rsrc(lo_a + i0, nb), lane * 16, ml + 2048);
+      dma16_buf(make_buffer_rsrc(hi_a + i0, nb), lane * 16, ml + 3072);
+    }
+  };
+
+  floatx4 dka[D / 16], dva[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    dka[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    dva[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (n > 0) load_tile(0, 0);
+  for (int t = 0; t < n; ++t) {
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 1 < n) load_tile(t + 1, (t + 1) & 1);
+    const unsigned char* st = &ring[t & 1][0];
+    const T* Qb = reinterpret_cast<const T*>(st);
+    const T* Db = reinterpret_cast<const T*>(st + TB);
+    const float* lse_s = reinterpret_cast<const float*>(st + 2 * TB);
+    const float* dlt_s = reinterpret_cast<const float*>(st + 2 * TB + 1024);
+    const int* lo_s = reinterpret_cast<const int*>(st + 2 * TB + 2048);
+    const int* hi_s = reinterpret_cast<const int*>(st + 2 * TB + 3072);
+    const int i0 = i_min + (t - (t / ntq) * ntq) * BQ;
+    const int nrow = min(BQ, Ttot - i0);
+    // rows of the tile admit a key of this wave? (monotone bounds)
+    if (!(wact && lo_s[0] <= wj0 + 15 && hi_s[nrow - 1] >= wj0)) continue;
+
+    floatx4 s[NRB], dp[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      s[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dp[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kk = 0; kk < G::QREG; ++kk) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int r = rb * 16 + c16;
+        if constexpr (kF32) {
+          const int ch = grp * (D / 16) + kk;
+          const int e = (r * G::CPR + chunk_pos<G::CPR>(r, ch)) * 4;
+          const floatx4 a = *reinterpret_cast<const floatx4*>(&Qb[e]);
+          const floatx4 ad = *reinterpret_cast<const floatx4*>(&Db[e]);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], kf[kk][x], s[rb], 0, 0, 0);
+            dp[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ad[x], vf[kk][x], dp[rb], 0, 0, 0);
+          }
+        } else {
+          const int ch = kk * 4 + grp;
+          const int e = (r * G::CPR + chunk_pos<G::CPR>(r, ch)) * 8;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Qb[e]);
+          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&Db[e]);
+          s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[kk], s[rb], 0, 0, 0);
+          dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, vf[kk], dp[rb], 0, 0, 0);
+        }
+      }
+    }
+    // P and dS; lane holds rows 16 rb + 4 grp + x of key j
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int rr = rb * 16 + 4 * grp;
+      const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[rr]);
+      const floatx4 d4 = *reinterpret_cast<const floatx4*>(&dlt_s[rr]);
+      const int32_t* lo4 = &lo_s[rr];
+      const int32_t* hi4 = &hi_s[rr];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int lo = lo4[x], hi = hi4[x];
+        const bool ok = rr + x < nrow && (unsigned)(j - lo) <= (unsigned)(hi - lo);
+        const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][x], c_scale, -l4[x])) : 0.f;
+        s[rb][x] = p;
+        dp[rb][x] = p * (dp[rb][x] - d4[x]);
+      }
+    }
+    // dv^T += dout^T P,  dk^T += Q^T dS
+    if constexpr (kF32) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const int d = dt * 16 + c16;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int r = rb * 16 + 4 * grp + x;
+            const int e = (r * G::CPR + chunk_pos<G::CPR>(r, d >> 2)) * 4 + (d & 3);
+            dva[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Db[e], s[rb][x], dva[dt], 0, 0, 0);
+            dka[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Qb[e], dp[rb][x], dka[dt], 0, 0, 0);
+          }
+        }
+    } else {
+      const int tr_r = (lane & 15) >> 2, tr_m = lane & 3;
+#pragma unroll
+      for (int ks = 0; ks < BQ / 32; ++ks) {
+        bf16x8 pf, sf;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          pf[x] = (__bf16)s[2 * ks][x];
+          pf[4 + x] = (__bf16)s[2 * ks + 1][x];
+          sf[x] = (__bf16)dp[2 * ks][x];
+          sf[4 + x] = (__bf16)dp[2 * ks + 1][x];
+        }
+        const int r0 = ks * 32 + 4 * grp + tr_r, r1 = r0 + 16;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const int ch = 2 * dt + (tr_m >> 1), off = (tr_m & 1) * 4;
+          const int e0 = (r0 * G::CPR + chunk_pos<G::CPR>(r0, ch)) * 8 + off;
+          const int e1 = (r1 * G::CPR + chunk_pos<G::CPR>(r1, ch)) * 8 + off;
+          const short4v d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(&Db[e0]));
+          const short4v d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(&Db[e1]));
+          const short4v q0v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(&Qb[e0]));
+          const short4v q1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(&Qb[e1]));
+          const short8v dx = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+          const short8v qx = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
+          dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, dx), pf, dva[dt], 0, 0, 0);
+          dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qx), sf, dka[dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- store dk = scale dk^T, dv = dv^T: 4 consecutive d of key j per lane --
+  if (j < Ttot) {
+    T* krow = dk + ((size_t)j * hkv + kvh) * D;
+    T* vrow = dv + ((size_t)j * hkv + kvh) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const floatx4 xk = dka[dt] * scale;
+      const floatx4 xv = dva[dt];
+      const int d0 = dt * 16 + 4 * grp;
+      if constexpr (kF32) {
+        *reinterpret_cast<floatx4*>(krow + d0) = xk;
+        *reinterpret_cast<floatx4*>(vrow + d0) = xv;
+      } else {
+        const bf16x4 wk = {(__bf16)xk[0], (__bf16)xk[1], (__bf16)xk[2], (__bf16)xk[3]};
+        const bf16x4 wv = {(__bf16)xv[0], (__bf16)xv[1], (__bf16)xv[2], (__bf16)xv[3]};
+        *reinterpret_cast<bf16x4*>(krow + d0) = wk;
+        *reinterpret_cast<bf16x4*>(vrow + d0) = wv;
+      }
+    }
+  }
+}
+
+}  // namespace swa

@@ -137,6 +137,65 @@ SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
   return swa::launch_prefill(a);
 }
 
+SWA_API size_t swa_prefill_backward_workspace_bytes(int32_t total_tokens, int32_t hq) {
+  if (total_tokens < 0 || hq <= 0) return 0;
+  return swa::bwd_workspace_bytes(total_tokens, hq);
+}
+
+SWA_API int swa_prefill_backward(const void* q, const void* k, const void* v, const void* out,
+                                 const void* dout, const int32_t* cu_seqlens,
+                                 const int32_t* doc_or_block_ids, int32_t window,
+                                 int32_t causal_mode, void* dq, void* dk, void* dv,
+                                 int32_t total_tokens, int32_t num_docs, int32_t hq, int32_t hkv,
+                                 int32_t d, int32_t dtype, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  int rc = check_heads(hq, hkv, d, dtype, true);
+  if (rc) return rc;
+  if (!swa::bwd_supported(d, dtype)) return SWA_EUNSUPPORTED;
+  if (total_tokens < 0 || num_docs < 0) return SWA_EINVAL;
+  if (causal_mode != SWA_CAUSAL && causal_mode != SWA_BLOCKWISE) return SWA_EUNSUPPORTED;
+  if (total_tokens == 0) return SWA_OK;  // nothing to compute
+  if (num_docs < 1) return SWA_EINVAL;
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(out) || !ptr_ok(dout) || !ptr_ok(dq) ||
+      !ptr_ok(dk) || !ptr_ok(dv))
+    return SWA_EINVAL;
+  if (cu_seqlens == nullptr || ((uintptr_t)cu_seqlens & 3u)) return SWA_EINVAL;
+  if (causal_mode == SWA_BLOCKWISE &&
+      (doc_or_block_ids == nullptr || ((uintptr_t)doc_or_block_ids & 3u)))
+    return SWA_EINVAL;
+  // tile offsets (64 rows of hq * d elements) stay below 2^31 bytes
+  if ((int64_t)hq * d >= ((int64_t)1 << 22) ||
+      (int64_t)total_tokens * hq * d >= (int64_t)1 << 62)
+    return SWA_EUNSUPPORTED;
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < swa::bwd_workspace_bytes(total_tokens, hq))
+    return SWA_EWORKSPACE;
+  if (!(scale > 0.f)) scale = 1.0f / __builtin_sqrtf((float)d);
+  swa::PrefillBwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.cu = cu_seqlens;
+  a.ids = causal_mode == SWA_BLOCKWISE ? doc_or_block_ids : nullptr;
+  a.window = window;
+  a.mode = causal_mode;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.total = total_tokens;
+  a.num_docs = num_docs;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.dtype = dtype;
+  a.scale = scale;
+  a.workspace = workspace;
+  a.stream = (hipStream_t)stream;
+  return swa::launch_prefill_bwd(a);
+}
+
 SWA_API size_t swa_decode_workspace_bytes(int32_t batch, int32_t hq,
                                           int32_t hkv, int32_t d,
                                           int32_t ring_rows) {

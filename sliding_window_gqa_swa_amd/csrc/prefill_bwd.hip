@@ -1,0 +1,98 @@
+// prefill_bwd.hip -- host launchers of the prefill backward (bwd_kernel.h).
+#include "bwd_kernel.h"
+#include "swa_internal.h"
+
+#include <algorithm>
+
+namespace swa {
+
+namespace {
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// query rows per dq work-group: 32 rows per wave while the fragments fit
+template <int D, typename T>
+constexpr int dq_mb() {
+  return (!std::is_same<T, float>::value && D <= 128) ? 2 : 1;
+}
+
+template <int D, typename T>
+int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
+  constexpr int MB = dq_mb<D, T>();
+  constexpr int BM = 64 * MB;
+  const int T_ = a.total;
+  hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((T_ + 255) / 256)), dim3(256), 0, a.stream,
+                     a.cu, a.num_docs, a.ids, a.window, a.mode, T_, w.lo, w.hi);
+  const float c = a.scale * kPrefillLog2e;
+  {
+    const int ntiles = (T_ + BM - 1) / BM;
+    const long long nwork = (long long)ntiles * a.hq;
+    const long long per_xcd = (nwork + 7) / 8;
+    if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, T, MB>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
+                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.out,
+                       (const T*)a.dout, w.lo, w.hi, T_, a.hq, a.hkv, c, a.scale, ntiles,
+                       (int)nwork, (int)per_xcd, (T*)a.dq, w.lse, w.delta);
+  }
+  {
+    const int nkt = (T_ + 63) / 64;
+    const long long nwork = (long long)nkt * a.hkv;
+    const long long per_xcd = (nwork + 7) / 8;
+    if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
+                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
+                       w.lse, w.delta, w.lo, w.hi, T_, a.hq, a.hkv, c, a.scale, nkt, (int)nwork,
+                       (int)per_xcd, (T*)a.dk, (T*)a.dv);
+  }
+  return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int total, int hq) {
+  const size_t t = (size_t)(total > 0 ? total : 0);
+  // lse2 and delta [hq, T] fp32, lo and hi [T] int32, each padded for the
+  // 16-byte metadata loads that read a few entries past the end
+  return 2 * round256((size_t)hq * t * 4 + 16) + 2 * round256(t * 4 + 16);
+}
+
+BwdWorkspace bwd_workspace(void* base, int total, int hq) {
+  const size_t t = (size_t)total;
+  unsigned char* p = (unsigned char*)base;
+  BwdWorkspace w;
+  w.lse = (float*)p;
+  p += round256((size_t)hq * t * 4 + 16);
+  w.delta = (float*)p;
+  p += round256((size_t)hq * t * 4 + 16);
+  w.lo = (int32_t*)p;
+  p += round256(t * 4 + 16);
+  w.hi = (int32_t*)p;
+  return w;
+}
+
+bool bwd_supported(int d, int dtype) {
+  if (dtype == SWA_BF16) return d == 64 || d == 128 || d == 256 || d == 320 || d == 512;
+  return d == 64 || d == 128 || d == 256 || d == 320;
+}
+
+int launch_prefill_bwd(const PrefillBwdArgs& a) {
+  const BwdWorkspace w = bwd_workspace(a.workspace, a.total, a.hq);
+  const bool bf = a.dtype == SWA_BF16;
+  switch (a.d) {
+    case 64:
+      return bf ? launch_bwd_cfg<64, __bf16>(a, w) : launch_bwd_cfg<64, float>(a, w);
+    case 128:
+      return bf ? launch_bwd_cfg<128, __bf16>(a, w) : launch_bwd_cfg<128, float>(a, w);
+    case 256:
+      return bf ? launch_bwd_cfg<256, __bf16>(a, w) : launch_bwd_cfg<256, float>(a, w);
+    case 320:
+      return bf ? launch_bwd_cfg<320, __bf16>(a, w) : launch_bwd_cfg<320, float>(a, w);
+    case 512:
+      if (bf) return launch_bwd_cfg<512, __bf16>(a, w);
+      return SWA_EUNSUPPORTED;
+    default:
+      return SWA_EUNSUPPORTED;
+  }
+}
+
+}  // namespace swa

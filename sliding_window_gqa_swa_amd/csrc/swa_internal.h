@@ -60,4 +60,35 @@ struct PrefillArgs {
 };
 int launch_prefill(const PrefillArgs& a);
 
+// Prefill backward (whole prompts): dq, dk, dv from q, k, v, the forward
+// output and its gradient dout.
+struct PrefillBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const int32_t* cu;
+  const int32_t* ids;  // block ids (SWA_BLOCKWISE), else NULL
+  int window, mode;
+  void* dq;
+  void* dk;
+  void* dv;
+  int total, num_docs, hq, hkv, d, dtype;
+  float scale;
+  void* workspace;
+  hipStream_t stream;
+};
+// regions of the backward's workspace
+struct BwdWorkspace {
+  float* lse;    // [hq, T] log2-sum-exp2 of each row's scaled scores
+  float* delta;  // [hq, T] <dout, out> of each row
+  int32_t* lo;   // [T] first admitted key of each row
+  int32_t* hi;   // [T] last admitted key of each row
+};
+size_t bwd_workspace_bytes(int total, int hq);
+BwdWorkspace bwd_workspace(void* base, int total, int hq);
+bool bwd_supported(int d, int dtype);
+int launch_prefill_bwd(const PrefillBwdArgs& a);
+
 }  // namespace swa

@@ -111,6 +111,54 @@ def test_prefill_empty_is_a_no_op():
     assert _prefill(T=0, q=None, k=None, v=None, out=None, cu=None) == _lib.SWA_OK
 
 
+def _backward(**kw):
+    a = dict(q=A, k=A, v=A, out=A, dout=A, cu=B, ids=None, window=16, mode=0, dq=A, dk=A, dv=A,
+             T=10, nd=1, hq=4, hkv=2, d=128, dtype=0, ws=A, wsb=1 << 30)
+    a.update(kw)
+    return _lib.lib().swa_prefill_backward(
+        a["q"], a["k"], a["v"], a["out"], a["dout"], a["cu"], a["ids"], a["window"], a["mode"],
+        a["dq"], a["dk"], a["dv"], a["T"], a["nd"], a["hq"], a["hkv"], a["d"], a["dtype"], 0.0,
+        a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), _lib.SWA_EUNSUPPORTED),
+    (dict(d=512, dtype=1), _lib.SWA_EUNSUPPORTED),
+    (dict(dtype=7), _lib.SWA_EUNSUPPORTED),
+    (dict(mode=2), _lib.SWA_EUNSUPPORTED),
+    (dict(hq=3, hkv=2), _lib.SWA_EINVAL),
+    (dict(T=-1), _lib.SWA_EINVAL),
+    (dict(nd=0), _lib.SWA_EINVAL),
+    (dict(dout=None), _lib.SWA_EINVAL),
+    (dict(out=A + 4), _lib.SWA_EINVAL),
+    (dict(dk=None), _lib.SWA_EINVAL),
+    (dict(cu=None), _lib.SWA_EINVAL),
+    (dict(mode=1, ids=None), _lib.SWA_EINVAL),
+    (dict(ws=None), _lib.SWA_EWORKSPACE),
+    (dict(wsb=16), _lib.SWA_EWORKSPACE),
+    (dict(ws=A + 8), _lib.SWA_EWORKSPACE),
+])
+def test_prefill_backward_rejects(kw, code):
+    assert _backward(**kw) == code
+
+
+def test_prefill_backward_sizes():
+    """Empty input is a no-op; every supported head size passes the size
+    checks (a call with too little workspace gets past them); the
+    workspace holds two fp32 rows of statistics per head and two int32
+    intervals per token."""
+    assert _backward(T=0, q=None, dq=None, ws=None) == _lib.SWA_OK
+    for d in (64, 128, 256, 320, 512):
+        assert _backward(d=d, wsb=0) == _lib.SWA_EWORKSPACE
+    for d in (64, 128, 256, 320):
+        assert _backward(d=d, dtype=1, wsb=0) == _lib.SWA_EWORKSPACE
+    L = _lib.lib()
+    for T, hq in ((1, 1), (4096, 32), (16384, 16)):
+        n = L.swa_prefill_backward_workspace_bytes(T, hq)
+        assert n >= 8 * T * hq + 8 * T and n % 256 == 0
+    assert L.swa_prefill_backward_workspace_bytes(-1, 4) == 0
+
+
 def _decode(**kw):
     a = dict(q=A, k=A, v=A, meta=B, window=1024, out=A, b=2, R=1088, hq=8, hkv=4, d=256,
              dtype=0, ws=A, wsb=1 << 30)

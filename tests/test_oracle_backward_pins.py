@@ -167,8 +167,10 @@ def test_backward_document_sum_invariants(mode, W):
 
 
 def test_backward_subsets_equal_full():
-    """Selected rows of dq and selected key rows of dk, dv give the same bits
-    as the full computation (the full dk/dv path gathers row by row too)."""
+    """Selected rows of dq give the same bits as the full computation;
+    selected key rows of dk, dv (gathered key by key over the rows that
+    admit them) equal the full computation (scattered row by row) within
+    rounding: two summation orders of the same terms."""
     rng = si.rng_for(5)
     T, hq, hkv, D = 40, 4, 2, 8
     cu = np.array([0, 17, 40], np.int32)
@@ -178,5 +180,5 @@ def test_backward_subsets_equal_full():
     keys = np.array([39, 0, 20, 16], np.int32)
     dq, dk, dv = orc.prefill_backward(q, k, v, do, cu, None, 6, CAUSAL, rows=rows, keys=keys)
     np.testing.assert_array_equal(dq, full[0][rows])
-    np.testing.assert_array_equal(dk, full[1][keys])
-    np.testing.assert_array_equal(dv, full[2][keys])
+    np.testing.assert_allclose(dk, full[1][keys], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, full[2][keys], rtol=0, atol=1e-13)
