@@ -25,11 +25,12 @@
 //      tiles gives each row's lse2 (online max and sum), a second forms
 //      S^T, dP^T, dS^T and accumulates dq^T = K^T dS^T; it also writes
 //      lse2 and delta for launch 3;
-//   3. bwd_dkdv_kernel: per (64-key tile, K/V head): each wave owns 16 keys
-//      (K and V fragments in registers) and walks the query tiles of every
-//      head of the group whose rows admit any of the 64 keys (a contiguous
-//      row range, found by binary search on the monotone intervals),
-//      accumulating dv^T += dout^T P and dk^T += Q^T dS.
+//   3. bwd_dkdv_kernel: per (key tile, K/V head): each wave owns 16 keys
+//      (K and V fragments in registers; at large head sizes two waves
+//      share a key block, one half of d each) and walks the query tiles of
+//      every head of the group whose rows admit any of the tile's keys (a
+//      contiguous row range, found by binary search on the monotone
+//      intervals), accumulating dv^T += dout^T P and dk^T += Q^T dS.
 // Tiles travel HBM -> LDS by direct-to-LDS buffer loads into a 2-stage ring
 // (the next tile loads while the current one is used), with the forward's
 // chunk permutation, so the row-fragment reads (ds_read_b128) and the
@@ -463,14 +464,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv: work-group = 64 keys of one K/V head, wave w owns keys 16w .. +16
-// (its K and V rows as B fragments in registers).  For each head of the
-// group and each query tile of BN rows that admits any of the 64 keys:
-// S = Q K^T and dP = dout V^T (Q, dout fragments from LDS), then
-// dv^T += dout^T P and dk^T += Q^T dS (dout^T, Q^T by transposed LDS reads,
-// P and dS from the accumulator layout).  Each stage also carries the
-// tile's lse2, delta, lo and hi (BN floats / ints each).
-template <int D, typename T>
+// dk, dv: work-group = 64 / DS keys of one K/V head in 16-key blocks; wave w
+// owns key block w / DS and, with DS = 2, one half of the head dimension
+// (w % 2): its K and V rows (that half) as B fragments in registers and the
+// dk^T, dv^T accumulators of that half.  For each head of the group and
+// each query tile of BN rows that admits any of the work-group's keys:
+// S = Q K^T and dP = dout V^T (Q, dout fragments from LDS; with DS = 2 each
+// wave of a pair forms the products over its half of d and the pair adds
+// the two partial sums through LDS), then dv^T += dout^T P and
+// dk^T += Q^T dS (dout^T, Q^T by transposed LDS reads, P and dS from the
+// accumulator layout).  Each stage also carries the tile's lse2, delta, lo
+// and hi (BN floats / ints each).  DS = 2 halves the registers a wave
+// needs at large head sizes, at the cost of a second barrier per tile.
+template <int D, typename T, int DS>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dlt,
@@ -481,10 +487,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   using TR = typename G::TR;
   constexpr bool kF32 = G::kF32;
   constexpr int BQ = G::BN, TB = G::TILE_BYTES, NRB = BQ / 16;
+  constexpr int BK = 64 / DS;              // keys per work-group
+  constexpr int QH = G::QREG / DS;         // S / dP fragments of this wave's d range
+  constexpr int NDT = D / 16 / DS;         // 16-wide d blocks of this wave's accumulators
+  constexpr int CPW = G::CPR / DS;         // 16-byte chunks of this wave's d range
+  static_assert(DS == 1 || DS == 2, "one or two waves per key block");
+  static_assert(G::QREG % DS == 0 && (D / 16) % DS == 0, "d splits evenly");
   constexpr int META = 4096;  // lse2, delta, lo, hi: 1 KB each
   static_assert(BQ * 4 <= 1024, "tile metadata fits its slot");
   constexpr int STAGE = 2 * TB + META;
+  constexpr int XCH = DS == 2 ? 4 * 2 * NRB * 64 * 16 : 16;  // partial S, dP per wave
   __shared__ __attribute__((aligned(1024))) unsigned char ring[2][STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char xch[XCH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
@@ -495,12 +509,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   const int kvh = work / nktiles;
   const int kt = work - kvh * nktiles;
   const int g = hq / hkv;
-  const int j0 = kt * 64;
-  const int j1 = min(j0 + 63, Ttot - 1);
+  const int j0 = kt * BK;
+  const int j1 = min(j0 + BK - 1, Ttot - 1);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int wj0 = j0 + 16 * wave_u;  // this wave's first key
-  const int j = wj0 + c16;           // this lane's key (MFMA column)
+  const int kblk = wave_u / DS, dh = wave_u % DS;
+  const int wj0 = j0 + 16 * kblk;  // this wave's first key
+  const int j = wj0 + c16;         // this lane's key (MFMA column)
   const bool wact = wj0 < Ttot;
+  // chunk of fragment kk of this wave's d range (the permutation of the d
+  // index within a product step must match between Q / dout and K / V)
+  auto frag_ch = [&](int kk) {
+    return kF32 ? dh * CPW + grp * (CPW / 4) + kk : dh * CPW + kk * 4 + grp;
+  };
 
   // rows admitting a key of [j0, j1]: hi_i >= j0 and lo_i <= j1, a
   // contiguous range since both bounds are monotone in i
@@ -526,13 +546,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 
   // K and V fragments of this lane's key (B operands of S = Q K^T, dP = dout V^T)
   using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
-  QF kf[G::QREG], vf[G::QREG];
+  QF kf[QH], vf[QH];
   {
     const bool ok = j < Ttot;
     const size_t roff = ((size_t)(ok ? j : 0) * hkv + kvh) * D;
 #pragma unroll
-    for (int kk = 0; kk < G::QREG; ++kk) {
-      const int d0 = kF32 ? grp * (D / 4) + kk * 4 : kk * 32 + 8 * grp;
+    for (int kk = 0; kk < QH; ++kk) {
+      const int d0 = frag_ch(kk) * TR::VEC;
       kf[kk] = ok ? *reinterpret_cast<const QF*>(k + roff + d0) : QF{};
       vf[kk] = ok ? *reinterpret_cast<const QF*>(v + roff + d0) : QF{};
     }
@@ -569,9 +589,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     }
   };
 
-  floatx4 dka[D / 16], dva[D / 16];
+  floatx4 dka[NDT], dva[NDT];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
+  for (int dt = 0; dt < NDT; ++dt) {
     dka[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     dva[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
@@ -592,8 +612,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int* hi_s = reinterpret_cast<const int*>(st + 2 * TB + 3072);
     const int i0 = i_min + (t - (t / ntq) * ntq) * BQ;
     const int nrow = min(BQ, Ttot - i0);
-    // rows of the tile admit a key of this wave? (monotone bounds)
-    if (!(wact && lo_s[0] <= wj0 + 15 && hi_s[nrow - 1] >= wj0)) continue;
+    // rows of the tile admit a key of this wave's block? (monotone bounds;
+    // uniform over the waves that share the block)
+    const bool busy = wact && lo_s[0] <= wj0 + 15 && hi_s[nrow - 1] >= wj0;
+    if (DS == 1 && !busy) continue;
 
     floatx4 s[NRB], dp[NRB];
 #pragma unroll
@@ -601,29 +623,48 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       s[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
       dp[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+    if (busy) {
 #pragma unroll
-    for (int kk = 0; kk < G::QREG; ++kk) {
+      for (int kk = 0; kk < QH; ++kk) {
+        const int ch = frag_ch(kk);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const int r = rb * 16 + c16;
+          const int e = (r * G::CPR + chunk_pos<G::CPR>(r, ch)) * TR::VEC;
+          if constexpr (kF32) {
+            const floatx4 a = *reinterpret_cast<const floatx4*>(&Qb[e]);
+            const floatx4 ad = *reinterpret_cast<const floatx4*>(&Db[e]);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], kf[kk][x], s[rb], 0, 0, 0);
+              dp[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ad[x], vf[kk][x], dp[rb], 0, 0, 0);
+            }
+          } else {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Qb[e]);
+            const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&Db[e]);
+            s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[kk], s[rb], 0, 0, 0);
+            dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, vf[kk], dp[rb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if constexpr (DS == 2) {
+      // add the partner wave's partial products (the other half of d); the
+      // slots are rewritten only after the next tile's first barrier, which
+      // the partner reaches after reading them
+      floatx4* mine = reinterpret_cast<floatx4*>(xch) + wave_u * (2 * NRB * 64);
+      const floatx4* other = reinterpret_cast<const floatx4*>(xch) + (wave_u ^ 1) * (2 * NRB * 64);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const int r = rb * 16 + c16;
-        if constexpr (kF32) {
-          const int ch = grp * (D / 16) + kk;
-          const int e = (r * G::CPR + chunk_pos<G::CPR>(r, ch)) * 4;
-          const floatx4 a = *reinterpret_cast<const floatx4*>(&Qb[e]);
-          const floatx4 ad = *reinterpret_cast<const floatx4*>(&Db[e]);
+        mine[(2 * rb) * 64 + lane] = s[rb];
+        mine[(2 * rb + 1) * 64 + lane] = dp[rb];
+      }
+      lds_barrier();  // (the next tile's loads stay in flight)
+      if (!busy) continue;
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], kf[kk][x], s[rb], 0, 0, 0);
-            dp[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ad[x], vf[kk][x], dp[rb], 0, 0, 0);
-          }
-        } else {
-          const int ch = kk * 4 + grp;
-          const int e = (r * G::CPR + chunk_pos<G::CPR>(r, ch)) * 8;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Qb[e]);
-          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&Db[e]);
-          s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[kk], s[rb], 0, 0, 0);
-          dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, vf[kk], dp[rb], 0, 0, 0);
-        }
+      for (int rb = 0; rb < NRB; ++rb) {
+        s[rb] += other[(2 * rb) * 64 + lane];
+        dp[rb] += other[(2 * rb + 1) * 64 + lane];
       }
     }
     // P and dS; lane holds rows 16 rb + 4 grp + x of key j
@@ -643,13 +684,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         dp[rb][x] = p * (dp[rb][x] - d4[x]);
       }
     }
-    // dv^T += dout^T P,  dk^T += Q^T dS
+    // dv^T += dout^T P,  dk^T += Q^T dS  (this wave's d range)
     if constexpr (kF32) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const int d = dt * 16 + c16;
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int d = (dh * NDT + dt) * 16 + c16;
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const int r = rb * 16 + 4 * grp + x;
@@ -672,8 +713,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         }
         const int r0 = ks * 32 + 4 * grp + tr_r, r1 = r0 + 16;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const int ch = 2 * dt + (tr_m >> 1), off = (tr_m & 1) * 4;
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int ch = 2 * (dh * NDT + dt) + (tr_m >> 1), off = (tr_m & 1) * 4;
           const int e0 = (r0 * G::CPR + chunk_pos<G::CPR>(r0, ch)) * 8 + off;
           const int e1 = (r1 * G::CPR + chunk_pos<G::CPR>(r1, ch)) * 8 + off;
           const short4v d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(&Db[e0]));
@@ -694,10 +735,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     T* krow = dk + ((size_t)j * hkv + kvh) * D;
     T* vrow = dv + ((size_t)j * hkv + kvh) * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    for (int dt = 0; dt < NDT; ++dt) {
       const floatx4 xk = dka[dt] * scale;
       const floatx4 xv = dva[dt];
-      const int d0 = dt * 16 + 4 * grp;
+      const int d0 = (dh * NDT + dt) * 16 + 4 * grp;
       if constexpr (kF32) {
         *reinterpret_cast<floatx4*>(krow + d0) = xk;
         *reinterpret_cast<floatx4*>(vrow + d0) = xv;

@@ -16,6 +16,13 @@ constexpr int dq_mb() {
   return (!std::is_same<T, float>::value && D <= 128) ? 2 : 1;
 }
 
+// waves per 16-key block of the dk/dv kernel: two (each one half of d)
+// where one wave's fragments and accumulators would not fit its registers
+template <int D, typename T>
+constexpr int dkdv_split() {
+  return std::is_same<T, float>::value ? (D >= 256 ? 2 : 1) : (D >= 512 ? 2 : 1);
+}
+
 template <int D, typename T>
 int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
   constexpr int MB = dq_mb<D, T>();
@@ -35,11 +42,12 @@ int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
                        (int)nwork, (int)per_xcd, (T*)a.dq, w.lse, w.delta);
   }
   {
-    const int nkt = (T_ + 63) / 64;
+    constexpr int DS = dkdv_split<D, T>();
+    const int nkt = (T_ + 64 / DS - 1) / (64 / DS);
     const long long nwork = (long long)nkt * a.hkv;
     const long long per_xcd = (nwork + 7) / 8;
     if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, DS>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
                        w.lse, w.delta, w.lo, w.hi, T_, a.hq, a.hkv, c, a.scale, nkt, (int)nwork,
                        (int)per_xcd, (T*)a.dk, (T*)a.dv);
