@@ -183,6 +183,33 @@ def bench_prefill_chunked(name, nchunks, steps, warmup, torch, api):
             "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def bench_prefill_backward(name, steps, warmup, torch, api):
+    """swa_prefill_backward (dq, dk, dv: three launches) on the workload.
+    Useful work: 2.5x the forward's useful FLOPs, the five products of
+    2 * D FLOPs per allowed pair and head that a backward which keeps no
+    score matrix needs (S again, dP, dv, dk, dq); the kernels execute more
+    (the dq kernel forms S once more for the row statistics)."""
+    c = si.PREFILL_WORKLOADS[name]()
+    q, k, v = c.tensors("bf16")
+    qd, kd, vd = to_dev(q, torch), to_dev(k, torch), to_dev(v, torch)
+    cu = to_dev(c.cu_seqlens, torch)
+    ids = to_dev(c.ids, torch) if c.ids is not None else None
+    do = to_dev(si.normal(si.rng_for(c.seed + 500), q.shape, "bf16"), torch)
+    out = api.prefill(qd, kd, vd, cu, ids, c.window, c.mode)
+    ws = torch.empty(api.prefill_backward_workspace_bytes(c.T, c.hq), dtype=torch.uint8,
+                     device="cuda")
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+
+    def step(i):
+        api.prefill_backward(qd, kd, vd, out, do, cu, ids, c.window, c.mode, dq, dk, dv, ws)
+
+    ms = time_loop(step, steps, warmup, torch)
+    fl = 5 * useful_flops(c) // 2
+    return {"workload": name + "_backward", "useful_flop": fl, "ms_per_call": ms,
+            "tflops": fl / (ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
     """Append + decode per step over `layers` independent ring sets (one per
     simulated sliding layer).  The roll is issued before every A-th append
@@ -488,6 +515,12 @@ def main():
         workloads[ch["workload"]] = ch
         print("%s: %.3f ms, %.1f TFLOP/s" % (ch["workload"], ch["ms_per_prompt"], ch["tflops"]),
               file=sys.stderr, flush=True)
+        for name, st in (("prefill_4x1024_mha_d128", 20), ("prefill_vlm_4096_d256", 20),
+                         ("prefill_16k_gqa_d512", 3)):
+            b = bench_prefill_backward(name, st, 2, torch, api)
+            workloads[b["workload"]] = b
+            print("%s: %.3f ms, %.1f TFLOP/s" % (b["workload"], b["ms_per_call"], b["tflops"]),
+                  file=sys.stderr, flush=True)
         for name in ("decode_b64_d256", "decode_single_d256"):
             workloads[name] = bench_decode(name, torch, api)
             print("%s: %.2f us/step, fused %.2f us/step (graph %.2f), decode %.2f us, %.0f GB/s" % (
