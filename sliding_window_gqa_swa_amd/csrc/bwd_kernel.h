@@ -43,7 +43,7 @@ namespace swa {
 
 // Tile geometry: BN rows (keys in the dq kernel, query rows in the dk/dv
 // kernel) of D elements per LDS tile, at most 32 KB per tile.
-template <int D, typename T>
+template <int D, typename T, int BN_ = 0>
 struct BwGeom {
   using TR = PfTraits<T>;
   static constexpr bool kF32 = std::is_same<T, float>::value;
@@ -51,7 +51,7 @@ struct BwGeom {
   static constexpr int CPR = D / TR::VEC;        // 16-byte chunks per row
   static constexpr int FRAG = kF32 ? 16 : 32;    // rows per P fragment step
   static constexpr int RAW = 32768 / (D * (int)sizeof(T));
-  static constexpr int BN = RAW >= 64 ? 64 : (RAW / FRAG) * FRAG;
+  static constexpr int BN = BN_ > 0 ? BN_ : (RAW >= 64 ? 64 : (RAW / FRAG) * FRAG);
   static constexpr int TILE_BYTES = BN * D * (int)sizeof(T);
   static constexpr int UNITS = BN * CPR;
   static constexpr int UPT = UNITS / NT;         // loads per thread per tile
@@ -60,6 +60,15 @@ struct BwGeom {
   static_assert(UNITS % NT == 0, "tile chunks split evenly over threads");
   static_assert(2 * UPT + 4 <= 63, "loads in flight fit vmcnt");
 };
+
+// Work-groups per CU the backward kernels are compiled for: two at small
+// bf16 head sizes (two waves per SIMD hide each other's LDS and matrix
+// latencies: 197 vs 248 us for the D = 128 dk/dv kernel, measured), else
+// what the registers allow.
+template <int D, typename T>
+constexpr int bw_blocks_per_cu() {
+  return (!std::is_same<T, float>::value && D <= 128) ? 2 : 1;
+}
 
 // Per-row key intervals: lo[i] = max(doc start, i - W + 1) (doc start when
 // W <= 0); hi[i] = i, or the last token of i's image run when i is an image
@@ -138,7 +147,7 @@ __device__ __forceinline__ i32x4 bw_rows_rsrc(const T* base, int r0, int h, int 
 // forward's S^T); dq^T += K^T dS^T takes K^T by transposed LDS reads and
 // dS^T from the accumulator layout (as the forward's O^T += V^T P^T).
 template <int D, typename T, int MB>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ o, const T* __restrict__ dout, const int32_t* __restrict__ lo_a,
     const int32_t* __restrict__ hi_a, int Ttot, int hq, int hkv, float c_scale, float scale,
@@ -464,39 +473,44 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv: work-group = 64 / DS keys of one K/V head in 16-key blocks; wave w
-// owns key block w / DS and, with DS = 2, one half of the head dimension
-// (w % 2): its K and V rows (that half) as B fragments in registers and the
-// dk^T, dv^T accumulators of that half.  For each head of the group and
-// each query tile of BN rows that admits any of the work-group's keys:
-// S = Q K^T and dP = dout V^T (Q, dout fragments from LDS; with DS = 2 each
-// wave of a pair forms the products over its half of d and the pair adds
-// the two partial sums through LDS), then dv^T += dout^T P and
-// dk^T += Q^T dS (dout^T, Q^T by transposed LDS reads, P and dS from the
+// dk, dv: work-group = 4 / DS waves' worth of key blocks of one K/V head;
+// wave w owns KB consecutive 16-key blocks (w / DS) and, with DS > 1, one
+// part of the head dimension (w % DS): its K and V rows (that part) as B
+// fragments in registers and the dk^T, dv^T accumulators of that part.  For
+// each head of the group and each query tile of BQ rows that admits any of
+// the work-group's keys: S = Q K^T and dP = dout V^T (Q, dout fragments from
+// LDS, each feeding KB products; with DS = 2 each wave of a pair forms the
+// products over its half of d and the pair adds the two partial sums
+// through LDS), then dv^T += dout^T P and dk^T += Q^T dS (dout^T, Q^T by
+// transposed LDS reads, again each feeding KB products; P and dS from the
 // accumulator layout).  Each stage also carries the tile's lse2, delta, lo
-// and hi (BN floats / ints each).  DS = 2 halves the registers a wave
-// needs at large head sizes, at the cost of a second barrier per tile.
-template <int D, typename T, int DS>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+// and hi.  KB = 2 halves the LDS reads per product; DS = 2 halves the
+// registers a wave needs at large head sizes, at the cost of a second
+// barrier per tile.
+template <int D, typename T, int DS, int KB, int BQ_>
+__global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dlt,
     const int32_t* __restrict__ lo_a, const int32_t* __restrict__ hi_a, int Ttot, int hq,
     int hkv, float c_scale, float scale, int nktiles, int nwork, int per_xcd,
     T* __restrict__ dk, T* __restrict__ dv) {
-  using G = BwGeom<D, T>;
+  using G = BwGeom<D, T, BQ_>;
   using TR = typename G::TR;
   constexpr bool kF32 = G::kF32;
   constexpr int BQ = G::BN, TB = G::TILE_BYTES, NRB = BQ / 16;
-  constexpr int BK = 64 / DS;              // keys per work-group
+  constexpr int KW = 16 * KB;              // keys per wave
+  constexpr int BK = KW * 4 / DS;          // keys per work-group
   constexpr int QH = G::QREG / DS;         // S / dP fragments of this wave's d range
   constexpr int NDT = D / 16 / DS;         // 16-wide d blocks of this wave's accumulators
   constexpr int CPW = G::CPR / DS;         // 16-byte chunks of this wave's d range
   static_assert(DS == 1 || DS == 2, "one or two waves per key block");
+  static_assert(KB == 1 || KB == 2, "one or two key blocks per wave");
   static_assert(G::QREG % DS == 0 && (D / 16) % DS == 0, "d splits evenly");
   constexpr int META = 4096;  // lse2, delta, lo, hi: 1 KB each
   static_assert(BQ * 4 <= 1024, "tile metadata fits its slot");
   constexpr int STAGE = 2 * TB + META;
-  constexpr int XCH = DS == 2 ? 4 * 2 * NRB * 64 * 16 : 16;  // partial S, dP per wave
+  constexpr int XW = KB * 2 * NRB * 64;    // floatx4 partials per wave
+  constexpr int XCH = DS == 2 ? 4 * XW * 16 : 16;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[2][STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char xch[XCH];
 
@@ -512,9 +526,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   const int j0 = kt * BK;
   const int j1 = min(j0 + BK - 1, Ttot - 1);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int kblk = wave_u / DS, dh = wave_u % DS;
-  const int wj0 = j0 + 16 * kblk;  // this wave's first key
-  const int j = wj0 + c16;         // this lane's key (MFMA column)
+  const int dh = wave_u % DS;
+  const int wj0 = j0 + KW * (wave_u / DS);  // this wave's first key
   const bool wact = wj0 < Ttot;
   // chunk of fragment kk of this wave's d range (the permutation of the d
   // index within a product step must match between Q / dout and K / V)
@@ -544,17 +557,19 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   const int ntq = i_max >= i_min ? (i_max - i_min) / BQ + 1 : 0;
   const int n = g * ntq;
 
-  // K and V fragments of this lane's key (B operands of S = Q K^T, dP = dout V^T)
+  // K and V fragments of this lane's keys (B operands of S = Q K^T, dP = dout V^T)
   using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
-  QF kf[QH], vf[QH];
-  {
+  QF kf[KB][QH], vf[KB][QH];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int j = wj0 + 16 * kb + c16;
     const bool ok = j < Ttot;
     const size_t roff = ((size_t)(ok ? j : 0) * hkv + kvh) * D;
 #pragma unroll
     for (int kk = 0; kk < QH; ++kk) {
       const int d0 = frag_ch(kk) * TR::VEC;
-      kf[kk] = ok ? *reinterpret_cast<const QF*>(k + roff + d0) : QF{};
-      vf[kk] = ok ? *reinterpret_cast<const QF*>(v + roff + d0) : QF{};
+      kf[kb][kk] = ok ? *reinterpret_cast<const QF*>(k + roff + d0) : QF{};
+      vf[kb][kk] = ok ? *reinterpret_cast<const QF*>(v + roff + d0) : QF{};
     }
   }
 
@@ -589,12 +604,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     }
   };
 
-  floatx4 dka[NDT], dva[NDT];
+  floatx4 dka[KB][NDT], dva[KB][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    dka[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    dva[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      dka[kb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dva[kb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 
   if (n > 0) load_tile(0, 0);
   for (int t = 0; t < n; ++t) {
@@ -612,17 +629,19 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int* hi_s = reinterpret_cast<const int*>(st + 2 * TB + 3072);
     const int i0 = i_min + (t - (t / ntq) * ntq) * BQ;
     const int nrow = min(BQ, Ttot - i0);
-    // rows of the tile admit a key of this wave's block? (monotone bounds;
-    // uniform over the waves that share the block)
-    const bool busy = wact && lo_s[0] <= wj0 + 15 && hi_s[nrow - 1] >= wj0;
+    // rows of the tile admit a key of this wave? (monotone bounds; uniform
+    // over the waves that share the keys)
+    const bool busy = wact && lo_s[0] <= wj0 + KW - 1 && hi_s[nrow - 1] >= wj0;
     if (DS == 1 && !busy) continue;
 
-    floatx4 s[NRB], dp[NRB];
+    floatx4 s[KB][NRB], dp[KB][NRB];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      s[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      dp[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        s[kb][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        dp[kb][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
     if (busy) {
 #pragma unroll
       for (int kk = 0; kk < QH; ++kk) {
@@ -635,15 +654,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
             const floatx4 a = *reinterpret_cast<const floatx4*>(&Qb[e]);
             const floatx4 ad = *reinterpret_cast<const floatx4*>(&Db[e]);
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              s[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], kf[kk][x], s[rb], 0, 0, 0);
-              dp[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ad[x], vf[kk][x], dp[rb], 0, 0, 0);
-            }
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], kf[kb][kk][x], s[kb][rb], 0, 0, 0);
+                dp[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ad[x], vf[kb][kk][x], dp[kb][rb], 0, 0, 0);
+              }
           } else {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Qb[e]);
             const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&Db[e]);
-            s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[kk], s[rb], 0, 0, 0);
-            dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, vf[kk], dp[rb], 0, 0, 0);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[kb][kk], s[kb][rb], 0, 0, 0);
+              dp[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, vf[kb][kk], dp[kb][rb], 0, 0, 0);
+            }
           }
         }
       }
@@ -652,22 +676,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       // add the partner wave's partial products (the other half of d); the
       // slots are rewritten only after the next tile's first barrier, which
       // the partner reaches after reading them
-      floatx4* mine = reinterpret_cast<floatx4*>(xch) + wave_u * (2 * NRB * 64);
-      const floatx4* other = reinterpret_cast<const floatx4*>(xch) + (wave_u ^ 1) * (2 * NRB * 64);
+      floatx4* mine = reinterpret_cast<floatx4*>(xch) + wave_u * XW;
+      const floatx4* other = reinterpret_cast<const floatx4*>(xch) + (wave_u ^ 1) * XW;
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        mine[(2 * rb) * 64 + lane] = s[rb];
-        mine[(2 * rb + 1) * 64 + lane] = dp[rb];
-      }
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          mine[((kb * NRB + rb) * 2) * 64 + lane] = s[kb][rb];
+          mine[((kb * NRB + rb) * 2 + 1) * 64 + lane] = dp[kb][rb];
+        }
       lds_barrier();  // (the next tile's loads stay in flight)
       if (!busy) continue;
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        s[rb] += other[(2 * rb) * 64 + lane];
-        dp[rb] += other[(2 * rb + 1) * 64 + lane];
-      }
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          s[kb][rb] += other[((kb * NRB + rb) * 2) * 64 + lane];
+          dp[kb][rb] += other[((kb * NRB + rb) * 2 + 1) * 64 + lane];
+        }
     }
-    // P and dS; lane holds rows 16 rb + 4 grp + x of key j
+    // P and dS; lane holds rows 16 rb + 4 grp + x of key wj0 + 16 kb + c16
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int rr = rb * 16 + 4 * grp;
@@ -678,10 +706,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int lo = lo4[x], hi = hi4[x];
-        const bool ok = rr + x < nrow && (unsigned)(j - lo) <= (unsigned)(hi - lo);
-        const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][x], c_scale, -l4[x])) : 0.f;
-        s[rb][x] = p;
-        dp[rb][x] = p * (dp[rb][x] - d4[x]);
+        const bool row_ok = rr + x < nrow;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int j = wj0 + 16 * kb + c16;
+          const bool ok = row_ok && (unsigned)(j - lo) <= (unsigned)(hi - lo);
+          const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][rb][x], c_scale, -l4[x])) : 0.f;
+          s[kb][rb][x] = p;
+          dp[kb][rb][x] = p * (dp[kb][rb][x] - d4[x]);
+        }
       }
     }
     // dv^T += dout^T P,  dk^T += Q^T dS  (this wave's d range)
@@ -695,22 +728,28 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
           for (int x = 0; x < 4; ++x) {
             const int r = rb * 16 + 4 * grp + x;
             const int e = (r * G::CPR + chunk_pos<G::CPR>(r, d >> 2)) * 4 + (d & 3);
-            dva[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Db[e], s[rb][x], dva[dt], 0, 0, 0);
-            dka[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Qb[e], dp[rb][x], dka[dt], 0, 0, 0);
+            const float ad = Db[e], aq = Qb[e];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              dva[kb][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, s[kb][rb][x], dva[kb][dt], 0, 0, 0);
+              dka[kb][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, dp[kb][rb][x], dka[kb][dt], 0, 0, 0);
+            }
           }
         }
     } else {
       const int tr_r = (lane & 15) >> 2, tr_m = lane & 3;
 #pragma unroll
       for (int ks = 0; ks < BQ / 32; ++ks) {
-        bf16x8 pf, sf;
+        bf16x8 pf[KB], sf[KB];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          pf[x] = (__bf16)s[2 * ks][x];
-          pf[4 + x] = (__bf16)s[2 * ks + 1][x];
-          sf[x] = (__bf16)dp[2 * ks][x];
-          sf[4 + x] = (__bf16)dp[2 * ks + 1][x];
-        }
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            pf[kb][x] = (__bf16)s[kb][2 * ks][x];
+            pf[kb][4 + x] = (__bf16)s[kb][2 * ks + 1][x];
+            sf[kb][x] = (__bf16)dp[kb][2 * ks][x];
+            sf[kb][4 + x] = (__bf16)dp[kb][2 * ks + 1][x];
+          }
         const int r0 = ks * 32 + 4 * grp + tr_r, r1 = r0 + 16;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -723,21 +762,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
           const short4v q1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(&Qb[e1]));
           const short8v dx = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
           const short8v qx = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
-          dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, dx), pf, dva[dt], 0, 0, 0);
-          dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qx), sf, dka[dt], 0, 0, 0);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            dva[kb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, dx), pf[kb], dva[kb][dt], 0, 0, 0);
+            dka[kb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qx), sf[kb], dka[kb][dt], 0, 0, 0);
+          }
         }
       }
     }
   }
 
-  // ---- store dk = scale dk^T, dv = dv^T: 4 consecutive d of key j per lane --
-  if (j < Ttot) {
+  // ---- store dk = scale dk^T, dv = dv^T: 4 consecutive d of a key per lane --
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int j = wj0 + 16 * kb + c16;
+    if (j >= Ttot) continue;
     T* krow = dk + ((size_t)j * hkv + kvh) * D;
     T* vrow = dv + ((size_t)j * hkv + kvh) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const floatx4 xk = dka[dt] * scale;
-      const floatx4 xv = dva[dt];
+      const floatx4 xk = dka[kb][dt] * scale;
+      const floatx4 xv = dva[kb][dt];
       const int d0 = (dh * NDT + dt) * 16 + 4 * grp;
       if constexpr (kF32) {
         *reinterpret_cast<floatx4*>(krow + d0) = xk;

@@ -13,15 +13,22 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 // query rows per dq work-group: 32 rows per wave while the fragments fit
 template <int D, typename T>
 constexpr int dq_mb() {
-  return (!std::is_same<T, float>::value && D <= 128) ? 2 : 1;
+  return 1;
 }
 
-// waves per 16-key block of the dk/dv kernel: two (each one half of d)
-// where one wave's fragments and accumulators would not fit its registers
+// dk/dv kernel shape per head size: DS waves per key block (each one part
+// of d), KB 16-key blocks per wave, BQ query rows per tile; chosen so that
+// one wave's fragments and accumulators fit its registers and the stages
+// plus the partial-sum exchange fit the LDS
 template <int D, typename T>
-constexpr int dkdv_split() {
-  return std::is_same<T, float>::value ? (D >= 256 ? 2 : 1) : (D >= 512 ? 2 : 1);
-}
+struct DkdvCfg {
+  static constexpr bool F = std::is_same<T, float>::value;
+  static constexpr int DS = F ? (D >= 256 ? 2 : 1) : (D >= 512 ? 2 : 1);
+  // (two key blocks per wave halve the LDS reads per product but cost the
+  // second wave per SIMD: 241 vs 197 us at D = 128, measured)
+  static constexpr int KB = 1;
+  static constexpr int BQ = 0;  // the default tile
+};
 
 template <int D, typename T>
 int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
@@ -42,12 +49,13 @@ int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
                        (int)nwork, (int)per_xcd, (T*)a.dq, w.lse, w.delta);
   }
   {
-    constexpr int DS = dkdv_split<D, T>();
-    const int nkt = (T_ + 64 / DS - 1) / (64 / DS);
+    using C = DkdvCfg<D, T>;
+    constexpr int BK = 16 * C::KB * 4 / C::DS;  // keys per work-group
+    const int nkt = (T_ + BK - 1) / BK;
     const long long nwork = (long long)nkt * a.hkv;
     const long long per_xcd = (nwork + 7) / 8;
     if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, DS>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, C::DS, C::KB, C::BQ>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
                        w.lse, w.delta, w.lo, w.hi, T_, a.hq, a.hkv, c, a.scale, nkt, (int)nwork,
                        (int)per_xcd, (T*)a.dk, (T*)a.dv);
