@@ -29,7 +29,7 @@ def _load():
         path = _build.build(force=False)
         lib = ctypes.CDLL(path)
         P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
-        lib.oracle_prefill_rows.argtypes = [P, P, P, I, P, I, P, I, I, I, I, I, I, D, P, I, P, I]
+        lib.oracle_prefill_rows.argtypes = [P, P, P, I, P, I, P, I, I, I, I, I, I, D, P, I, P, P, I]
         lib.oracle_prefill_rows.restype = I
         lib.oracle_decode_linear.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, D, P, I]
         lib.oracle_decode_linear.restype = I
@@ -63,12 +63,14 @@ def max_threads() -> int:
 
 
 def prefill(q, k, v, cu_seqlens, ids=None, window=0, mode=CAUSAL, scale=None,
-            rows=None, nthreads=0):
+            rows=None, nthreads=0, return_lse=False):
     """Packed varlen SWA prefill in fp64.
 
     q [T, Hq, D], k/v [T, Hkv, D] (uint16 bf16 bits or float32); cu_seqlens
     int32 [ndocs+1].  ``rows`` selects packed query indices (default: all).
-    Returns float64 [len(rows), Hq, D].  ``scale`` defaults to 1/sqrt(D).
+    Returns float64 [len(rows), Hq, D]; with ``return_lse`` also each row's
+    log-sum-exp log(sum_j exp(scale * <q, k_j>)) over its allowed keys,
+    float64 [len(rows), Hq].  ``scale`` defaults to 1/sqrt(D).
     """
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
@@ -85,13 +87,14 @@ def prefill(q, k, v, cu_seqlens, ids=None, window=0, mode=CAUSAL, scale=None,
     rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
     n = T if rows_a is None else rows_a.size
     out = np.empty((n, hq, d), dtype=np.float64)
+    lse = np.empty((n, hq), dtype=np.float64) if return_lse else None
     rc = _load().oracle_prefill_rows(
         _ptr(q), _ptr(k), _ptr(v), dt, _ptr(cu), cu.size - 1, _ptr(ids_a),
         int(window), int(mode), T, hq, hkv, d, float(scale), _ptr(rows_a), n,
-        _ptr(out), int(nthreads))
+        _ptr(out), _ptr(lse), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_prefill_rows rejected its arguments (rc=%d)" % rc)
-    return out
+    return (out, lse) if return_lse else out
 
 
 def prefill_chunk(q, k, v, cu_q, cu_k, ids=None, window=0, mode=CAUSAL, scale=None,

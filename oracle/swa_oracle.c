@@ -89,11 +89,14 @@ int oracle_allowed(const int32_t* cu, int ndocs, const int32_t* ids, int window,
 
 /* One output row: out[0..d) = sum_j softmax(scale * <q, k_j>) v_j over the
  * keys listed in `keys` (already filtered by the mask), in double.  Query
- * row, key rows and value rows are addressed by element offsets. */
+ * row, key rows and value rows are addressed by element offsets.  When
+ * `lse` is given it receives log(sum_j exp(scale * <q, k_j>)), the row's
+ * log-sum-exp (-inf for an empty set). */
 static void attend_row(const void* q, size_t q_off, const void* k, const void* v,
                        const size_t* kv_offs, int nkeys, int dtype, int d,
-                       double scale, double* s_buf, double* out) {
+                       double scale, double* s_buf, double* out, double* lse) {
   for (int e = 0; e < d; ++e) out[e] = 0.0;
+  if (lse) *lse = -INFINITY;
   if (nkeys == 0) return; /* empty allowed set: zero row */
   double m = -INFINITY;
   for (int t = 0; t < nkeys; ++t) {
@@ -110,6 +113,7 @@ static void attend_row(const void* q, size_t q_off, const void* k, const void* v
     for (int e = 0; e < d; ++e) out[e] += p * load_elem(v, dtype, kv_offs[t] + e);
   }
   for (int e = 0; e < d; ++e) out[e] /= l;
+  if (lse) *lse = m + log(l);
 }
 
 /*
@@ -119,13 +123,14 @@ static void attend_row(const void* q, size_t q_off, const void* k, const void* v
  *   ids int32[T] image-block ids (-1 = text); read only when mode = BLOCKWISE
  *   rows: the packed query indices to compute (NULL = all T rows, nrows = T)
  *   out double[nrows, hq, d]
+ *   lse double[nrows, hq] or NULL: each row's log-sum-exp of its scaled scores
  * Returns 0, or -1 on malformed arguments.
  */
 int oracle_prefill_rows(const void* q, const void* k, const void* v, int dtype,
                         const int32_t* cu, int ndocs, const int32_t* ids,
                         int window, int mode, int T, int hq, int hkv, int d,
                         double scale, const int32_t* rows, int nrows,
-                        double* out, int nthreads) {
+                        double* out, double* lse, int nthreads) {
   if (hkv <= 0 || hq % hkv != 0 || d <= 0 || ndocs < 0 || T < 0) return -1;
   if (cu[0] != 0 || cu[ndocs] != T) return -1;
   for (int dd = 0; dd < ndocs; ++dd)
@@ -154,6 +159,7 @@ int oracle_prefill_rows(const void* q, const void* k, const void* v, int dtype,
       double* o = out + ((size_t)r * hq + h) * d;
       if (i < 0 || i >= T) {
         for (int e = 0; e < d; ++e) o[e] = NAN;
+        if (lse) lse[(size_t)r * hq + h] = NAN;
         continue;
       }
       int kvh = h / g;
@@ -163,7 +169,7 @@ int oracle_prefill_rows(const void* q, const void* k, const void* v, int dtype,
         if (oracle_allowed(cu, ndocs, ids, window, mode, i, j))
           offs[nk++] = ((size_t)j * hkv + kvh) * d;
       attend_row(q, ((size_t)i * hq + h) * d, k, v, offs, nk, dtype, d, scale,
-                 sbuf, o);
+                 sbuf, o, lse ? lse + (size_t)r * hq + h : NULL);
     }
     free(offs);
     free(sbuf);
@@ -225,7 +231,7 @@ int oracle_decode_linear(const void* q, const void* k_lin, const void* v_lin,
         offs[nk++] = (row * hkv + kvh) * d;
       }
       attend_row(q, ((size_t)b * hq + h) * d, k_lin, v_lin, offs, nk, dtype, d,
-                 scale, sbuf, out + ((size_t)b * hq + h) * d);
+                 scale, sbuf, out + ((size_t)b * hq + h) * d, NULL);
     }
     free(offs);
     free(sbuf);

@@ -182,3 +182,47 @@ def test_backward_subsets_equal_full():
     np.testing.assert_array_equal(dq, full[0][rows])
     np.testing.assert_allclose(dk, full[1][keys], rtol=0, atol=1e-13)
     np.testing.assert_allclose(dv, full[2][keys], rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------------------------- row log-sum-exp
+@pytest.mark.parametrize("trial", range(6))
+def test_lse_matches_dense_logsumexp(trial):
+    """The forward's per-row log-sum-exp equals logsumexp over the row of
+    an explicit-mask dense score matrix (scipy), within 1e-12."""
+    from scipy.special import logsumexp
+    rng = si.rng_for(8000 + trial)
+    T = int(rng.integers(2, 50))
+    cu = si.ragged_cu_seqlens(rng, T, int(rng.integers(1, 4)))
+    hkv, g, D = 2, int(rng.choice([1, 2])), 8
+    ids = np.full(T, -1, np.int32)
+    s0 = int(rng.integers(0, T))
+    ids[s0:min(T, s0 + 9)] = 0
+    q = si.normal(rng, (T, hkv * g, D), "bf16")
+    k = si.normal(rng, (T, hkv, D), "bf16")
+    v = si.normal(rng, (T, hkv, D), "bf16")
+    for W in (1, 4, 0):
+        for mode in (CAUSAL, BLOCKWISE):
+            _, lse = orc.prefill(q, k, v, cu, ids, W, mode, return_lse=True)
+            m = _dense_mask(cu, ids, W, mode, T)
+            for h in range(hkv * g):
+                s = _f64(q)[:, h] @ _f64(k)[:, h // g].T / math.sqrt(D)
+                want = logsumexp(np.where(m, s, -np.inf), axis=1)
+                np.testing.assert_allclose(lse[:, h], want, rtol=0, atol=1e-12)
+
+
+def test_lse_closed_forms():
+    """W = 1: the row's only key is itself, lse = scale <q_i, k_i>.  K = 0:
+    every score is 0, lse = log of the number of allowed keys, which for a
+    causal window is min(W, position in the document + 1)."""
+    rng = si.rng_for(17)
+    T, hq, hkv, D = 30, 4, 2, 16
+    cu = np.array([0, 11, 30], np.int32)
+    q, k, v = (si.normal(rng, s, "f32") for s in [(T, hq, D), (T, hkv, D), (T, hkv, D)])
+    _, lse = orc.prefill(q, k, v, cu, None, 1, CAUSAL, return_lse=True)
+    dots = np.einsum("thd,thd->th", q.astype(np.float64), np.repeat(k, 2, axis=1).astype(np.float64))
+    np.testing.assert_allclose(lse, dots / math.sqrt(D), rtol=0, atol=1e-13)
+    for W in (5, 0):
+        _, lse = orc.prefill(q, np.zeros_like(k), v, cu, None, W, CAUSAL, return_lse=True)
+        pos = np.concatenate([np.arange(11), np.arange(19)])
+        n = pos + 1 if W <= 0 else np.minimum(W, pos + 1)
+        np.testing.assert_allclose(lse, np.log(n)[:, None] * np.ones((1, hq)), rtol=0, atol=1e-14)
