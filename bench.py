@@ -183,31 +183,48 @@ def bench_prefill_chunked(name, nchunks, steps, warmup, torch, api):
             "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
-def bench_prefill_backward(name, steps, warmup, torch, api):
-    """swa_prefill_backward (dq, dk, dv: three launches) on the workload.
-    Useful work: 2.5x the forward's useful FLOPs, the five products of
+def bench_prefill_backward(name, steps, warmup, torch, api, pages_fwd_bwd_ms=None):
+    """swa_prefill_backward (dq, dk, dv: three launches) on the workload, as
+    a training step runs it: the forward (swa_prefill_lse) stores each row's
+    log-sum-exp and the backward takes it.  Also timed: the backward that
+    recomputes the log-sum-exp itself, and forward + backward.  Useful work
+    of the backward: 2.5x the forward's useful FLOPs, the five products of
     2 * D FLOPs per allowed pair and head that a backward which keeps no
-    score matrix needs (S again, dP, dv, dk, dq); the kernels execute more
-    (the dq kernel forms S once more for the row statistics)."""
+    score matrix needs (S again, dP, dv, dk, dq)."""
     c = si.PREFILL_WORKLOADS[name]()
     q, k, v = c.tensors("bf16")
     qd, kd, vd = to_dev(q, torch), to_dev(k, torch), to_dev(v, torch)
     cu = to_dev(c.cu_seqlens, torch)
     ids = to_dev(c.ids, torch) if c.ids is not None else None
     do = to_dev(si.normal(si.rng_for(c.seed + 500), q.shape, "bf16"), torch)
-    out = api.prefill(qd, kd, vd, cu, ids, c.window, c.mode)
+    out, lse = api.prefill_lse(qd, kd, vd, cu, ids, c.window, c.mode)
     ws = torch.empty(api.prefill_backward_workspace_bytes(c.T, c.hq), dtype=torch.uint8,
                      device="cuda")
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
 
-    def step(i):
+    def bwd(i):
+        api.prefill_backward(qd, kd, vd, out, do, cu, ids, c.window, c.mode, dq, dk, dv, ws,
+                             lse=lse)
+
+    def bwd_recompute(i):
         api.prefill_backward(qd, kd, vd, out, do, cu, ids, c.window, c.mode, dq, dk, dv, ws)
 
-    ms = time_loop(step, steps, warmup, torch)
+    def fwd_bwd(i):
+        api.prefill_lse(qd, kd, vd, cu, ids, c.window, c.mode, out=out, lse=lse)
+        bwd(i)
+
+    ms = time_loop(bwd, steps, warmup, torch)
+    ms_rc = time_loop(bwd_recompute, steps, warmup, torch)
+    ms_fb = time_loop(fwd_bwd, steps, warmup, torch)
     fl = 5 * useful_flops(c) // 2
-    return {"workload": name + "_backward", "useful_flop": fl, "ms_per_call": ms,
-            "tflops": fl / (ms * 1e-3) / 1e12,
-            "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    r = {"workload": name + "_backward", "useful_flop": fl, "ms_per_call": ms,
+         "tflops": fl / (ms * 1e-3) / 1e12,
+         "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+         "ms_per_call_recomputing_lse": ms_rc, "ms_forward_plus_backward": ms_fb}
+    if pages_fwd_bwd_ms is not None:
+        # context only: another machine's forward + backward of this shape
+        r["pages_h100_sdpa_mask_fwd_bwd_ms"] = pages_fwd_bwd_ms
+    return r
 
 
 def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
@@ -506,7 +523,8 @@ def main():
           file=sys.stderr, flush=True)
     workloads = {HEADLINE: head}
     if not args.only_headline:
-        for name in ("prefill_16k_gqa_d512", "prefill_vlm_4096_d256", "prefill_4x1024_gqa_d320"):
+        for name in ("prefill_16k_gqa_d512", "prefill_vlm_4096_d256", "prefill_4x1024_gqa_d320",
+                     "prefill_16k_mha_d128_w4k"):
             workloads[name] = bench_prefill(name, max(5, args.steps // 5), 3, torch, api)
             print("%s: %.3f ms, %.1f TFLOP/s" % (name, workloads[name]["ms_per_call"],
                                                  workloads[name]["tflops"]), file=sys.stderr,
@@ -515,12 +533,18 @@ def main():
         workloads[ch["workload"]] = ch
         print("%s: %.3f ms, %.1f TFLOP/s" % (ch["workload"], ch["ms_per_prompt"], ch["tflops"]),
               file=sys.stderr, flush=True)
-        for name, st in (("prefill_4x1024_mha_d128", 20), ("prefill_vlm_4096_d256", 20),
-                         ("prefill_16k_gqa_d512", 3)):
-            b = bench_prefill_backward(name, st, 2, torch, api)
+        # ([SDPA] Benchmark: forward + backward on H100 with the explicit-mask
+        # SDPA path: 612 ms for the 16K, window-4K, 16/8-head, D = 512 shape
+        # and 50 ms for the 16K, window-4K, 32-head, D = 128 shape)
+        for name, st, pages in (("prefill_4x1024_mha_d128", 20, None),
+                                ("prefill_vlm_4096_d256", 20, None),
+                                ("prefill_16k_gqa_d512", 3, 612.0),
+                                ("prefill_16k_mha_d128_w4k", 5, 50.0)):
+            b = bench_prefill_backward(name, st, 2, torch, api, pages)
             workloads[b["workload"]] = b
-            print("%s: %.3f ms, %.1f TFLOP/s" % (b["workload"], b["ms_per_call"], b["tflops"]),
-                  file=sys.stderr, flush=True)
+            print("%s: %.3f ms, %.1f TFLOP/s (recomputing lse %.3f ms; forward + backward %.3f ms)" % (
+                b["workload"], b["ms_per_call"], b["tflops"], b["ms_per_call_recomputing_lse"],
+                b["ms_forward_plus_backward"]), file=sys.stderr, flush=True)
         for name in ("decode_b64_d256", "decode_single_d256"):
             workloads[name] = bench_decode(name, torch, api)
             print("%s: %.2f us/step, fused %.2f us/step (graph %.2f), decode %.2f us, %.0f GB/s" % (

@@ -156,8 +156,9 @@ SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
  * in the element type of the inputs (bf16 rounded to nearest even).  out is
  * the forward's output (read only for delta_i = <dout_i, out_i>, the term
  * of the softmax's Jacobian); dout is the gradient arriving at out, laid
- * out like q.  The softmax statistics are recomputed, so nothing else from
- * the forward is needed.  Every output element is written exactly once,
+ * out like q.  lse: the rows' log-sum-exp as swa_prefill_lse stores it
+ * (float32 [hq, total_tokens], 4-byte aligned), or NULL, in which case the
+ * backward recomputes it with one more pass over the keys.  Every output element is written exactly once,
  * without atomics: the result is deterministic.
  *   d: 64, 128, 256, 320 or 512 for bf16; 64, 128, 256 or 320 for fp32.
  *   workspace: device memory of at least
@@ -172,10 +173,28 @@ SWA_API size_t swa_prefill_backward_workspace_bytes(int32_t total_tokens, int32_
 SWA_API int swa_prefill_backward(const void* q, const void* k, const void* v, const void* out,
                                  const void* dout, const int32_t* cu_seqlens,
                                  const int32_t* doc_or_block_ids, int32_t window,
-                                 int32_t causal_mode, void* dq, void* dk, void* dv,
-                                 int32_t total_tokens, int32_t num_docs, int32_t hq, int32_t hkv,
-                                 int32_t d, int32_t dtype, float scale, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+                                 int32_t causal_mode, const float* lse, void* dq, void* dk,
+                                 void* dv, int32_t total_tokens, int32_t num_docs, int32_t hq,
+                                 int32_t hkv, int32_t d, int32_t dtype, float scale,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * swa_prefill_lse -- swa_prefill that also stores each row's log-sum-exp,
+ * the softmax statistic a backward pass needs: for query row i and head h,
+ *   lse[h * total_tokens + i] = log(sum over allowed keys j of
+ *                                   exp(scale * <q[i, h], k[j, h / g]>))
+ * (natural log; -inf for a row with no allowed key).  lse: float32
+ * [hq, total_tokens] (device, 4-byte aligned, caller-owned), required when
+ * total_tokens > 0.  Every other argument and the output as for
+ * swa_prefill; out is bitwise the same as swa_prefill's.  Passing this lse
+ * to swa_prefill_backward spares the backward its pass over the keys that
+ * recomputes it.
+ */
+SWA_API int swa_prefill_lse(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens, const int32_t* doc_or_block_ids,
+                            int32_t window, int32_t causal_mode, void* out, float* lse,
+                            int32_t total_tokens, int32_t num_docs, int32_t hq, int32_t hkv,
+                            int32_t d, int32_t dtype, float scale, void* stream);
 
 /*
  * Bytes of workspace swa_decode needs for these sizes: split counters plus

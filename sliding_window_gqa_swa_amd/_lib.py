@@ -31,8 +31,10 @@ SIGNATURES = {
     "swa_prefill_chunk": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _I,
                                          _I, _F, _P]),
     "swa_prefill_backward_workspace_bytes": (_S, [_I, _I]),
-    "swa_prefill_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _I, _I,
-                                            _I, _I, _I, _I, _F, _P, _S, _P]),
+    "swa_prefill_lse": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _I,
+                                       _F, _P]),
+    "swa_prefill_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _I,
+                                            _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "swa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "swa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "swa_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P,

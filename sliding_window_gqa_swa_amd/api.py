@@ -65,6 +65,31 @@ def prefill(q, k, v, cu_seqlens, doc_or_block_ids=None, window=0, causal_mode=CA
     return out
 
 
+def prefill_lse(q, k, v, cu_seqlens, doc_or_block_ids=None, window=0, causal_mode=CAUSAL,
+                out=None, lse=None, scale=0.0):
+    """prefill that also returns each row's log-sum-exp; see swa_prefill_lse
+    in swa.h.  Returns (out [T, Hq, D], lse float32 [Hq, T])."""
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (T, hkv, d) or v.shape != (T, hkv, d):
+        raise ValueError("k and v must be [T, Hkv, D] matching q")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    if lse.shape != (hq, T):
+        raise ValueError("lse must be [Hq, T]")
+    dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s dtype differs from q" % name)
+    rc = _lib.lib().swa_prefill_lse(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+        _dev(doc_or_block_ids, "doc_or_block_ids", torch.int32), int(window), int(causal_mode),
+        _dev(out, "out"), _dev(lse, "lse", torch.float32), T, cu_seqlens.numel() - 1, hq, hkv, d,
+        dt, float(scale), _stream(q))
+    _lib.check("swa_prefill_lse", rc)
+    return out, lse
+
+
 def prefill_chunk(q, k, v, cu_seqlens_q, cu_seqlens_k, doc_or_block_ids=None, window=0,
                   causal_mode=CAUSAL, out=None, scale=0.0):
     """Prefill of one chunk of each document against its cache so far; see
@@ -100,11 +125,13 @@ def prefill_backward_workspace_bytes(total_tokens, hq) -> int:
 
 
 def prefill_backward(q, k, v, out, dout, cu_seqlens, doc_or_block_ids=None, window=0,
-                     causal_mode=CAUSAL, dq=None, dk=None, dv=None, workspace=None, scale=0.0):
+                     causal_mode=CAUSAL, dq=None, dk=None, dv=None, workspace=None, scale=0.0,
+                     lse=None):
     """Gradients (dq, dk, dv) of prefill for the loss sum(dout * out); see
     swa_prefill_backward in swa.h.  out is prefill's output for the same
-    arguments, dout the gradient at out (both [T, Hq, D]).  Returns
-    (dq [T, Hq, D], dk [T, Hkv, D], dv [T, Hkv, D])."""
+    arguments, dout the gradient at out (both [T, Hq, D]); lse optionally
+    the forward's row log-sum-exp from prefill_lse ([Hq, T] float32).
+    Returns (dq [T, Hq, D], dk [T, Hkv, D], dv [T, Hkv, D])."""
     T, hq, d = q.shape
     hkv = k.shape[1]
     if k.shape != (T, hkv, d) or v.shape != (T, hkv, d):
@@ -126,6 +153,7 @@ def prefill_backward(q, k, v, out, dout, cu_seqlens, doc_or_block_ids=None, wind
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), _dev(dout, "dout"),
         _dev(cu_seqlens, "cu_seqlens", torch.int32),
         _dev(doc_or_block_ids, "doc_or_block_ids", torch.int32), int(window), int(causal_mode),
+        _dev(lse, "lse", torch.float32),
         _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), T, cu_seqlens.numel() - 1, hq, hkv, d, dt,
         float(scale), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(q))

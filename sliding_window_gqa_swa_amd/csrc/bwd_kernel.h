@@ -22,7 +22,8 @@
 //      (the mask admits one contiguous interval per row, see the forward),
 //      both monotone in i;
 //   2. bwd_dq_kernel: per (query tile, head): a first pass over the key
-//      tiles gives each row's lse2 (online max and sum), a second forms
+//      tiles gives each row's lse2 (online max and sum; skipped when the
+//      forward's log-sum-exp is given), a second forms
 //      S^T, dP^T, dS^T and accumulates dq^T = K^T dS^T; it also writes
 //      lse2 and delta for launch 3;
 //   3. bwd_dkdv_kernel: per (key tile, K/V head): each wave owns 16 keys
@@ -150,9 +151,9 @@ template <int D, typename T, int MB>
 __global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ o, const T* __restrict__ dout, const int32_t* __restrict__ lo_a,
-    const int32_t* __restrict__ hi_a, int Ttot, int hq, int hkv, float c_scale, float scale,
-    int ntiles, int nwork, int per_xcd, T* __restrict__ dq, float* __restrict__ lse_out,
-    float* __restrict__ delta_out) {
+    const int32_t* __restrict__ hi_a, const float* __restrict__ lse_in, int Ttot, int hq,
+    int hkv, float c_scale, float scale, int ntiles, int nwork, int per_xcd, T* __restrict__ dq,
+    float* __restrict__ lse_out, float* __restrict__ delta_out) {
   using G = BwGeom<D, T>;
   using TR = typename G::TR;
   constexpr bool kF32 = G::kF32;
@@ -299,6 +300,15 @@ __global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dq_kernel
     asm volatile("" ::: "memory");
   };
 
+  float lse2[MB];
+  if (lse_in != nullptr) {
+    // the forward's log-sum-exp (natural log) in log2 units
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int i = row_i[mb];
+      lse2[mb] = i < Ttot ? lse_in[(size_t)h * Ttot + i] * kPrefillLog2e : INFINITY;
+    }
+  } else {
   // ---- pass 1: row statistics (max, then sum of exp2 relative to it) ----
   float m_run[MB], l_part[MB];
 #pragma unroll
@@ -337,7 +347,6 @@ __global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dq_kernel
       m_run[mb] = m_new;
     }
   }
-  float lse2[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     float l = l_part[mb];
@@ -345,6 +354,11 @@ __global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dq_kernel
     l += __shfl_xor(l, 32, 64);
     // log2 of sum_j exp2(s_j c); a row with no key gets +inf (P = 0)
     lse2[mb] = l > 0.f ? m_run[mb] * c_scale + __builtin_log2f(l) : INFINITY;
+  }
+  __syncthreads();  // every wave is done with pass 1's stages
+  }  // pass 1
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
     const int i = row_i[mb];
     if (grp == 0 && i < Ttot) {
       lse_out[(size_t)h * Ttot + i] = lse2[mb];
@@ -358,7 +372,6 @@ __global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dq_kernel
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();  // every wave is done with pass 1's stages
   load_tile(kt0, 0, true);
   for (int it = 0; it < nk; ++it) {
     const int k0 = kt0 + it * BN;

@@ -92,12 +92,16 @@ SWA_API int swa_prefill(const void* q, const void* k, const void* v,
                            dtype, scale, stream);
 }
 
-SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
-                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                              const int32_t* doc_or_block_ids, int32_t window,
-                              int32_t causal_mode, void* out, int32_t total_q,
-                              int32_t total_k, int32_t num_docs, int32_t hq, int32_t hkv,
-                              int32_t d, int32_t dtype, float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// swa_prefill_chunk with an optional per-row log-sum-exp output
+int prefill_impl(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                 const int32_t* cu_seqlens_k, const int32_t* doc_or_block_ids, int32_t window,
+                 int32_t causal_mode, void* out, float* lse, int32_t total_q, int32_t total_k,
+                 int32_t num_docs, int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
+                 float scale, void* stream) {
   int rc = check_heads(hq, hkv, d, dtype, true);
   if (rc) return rc;
   if (total_q < 0 || total_k < 0 || num_docs < 0) return SWA_EINVAL;
@@ -125,6 +129,7 @@ SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
   a.window = window;
   a.mode = causal_mode;
   a.out = out;
+  a.lse = lse;
   a.total_q = total_q;
   a.total_k = total_k;
   a.num_docs = num_docs;
@@ -137,6 +142,32 @@ SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
   return swa::launch_prefill(a);
 }
 
+}  // namespace
+
+extern "C" {
+
+SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              const int32_t* doc_or_block_ids, int32_t window,
+                              int32_t causal_mode, void* out, int32_t total_q,
+                              int32_t total_k, int32_t num_docs, int32_t hq, int32_t hkv,
+                              int32_t d, int32_t dtype, float scale, void* stream) {
+  return prefill_impl(q, k, v, cu_seqlens_q, cu_seqlens_k, doc_or_block_ids, window,
+                      causal_mode, out, nullptr, total_q, total_k, num_docs, hq, hkv, d, dtype,
+                      scale, stream);
+}
+
+SWA_API int swa_prefill_lse(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens, const int32_t* doc_or_block_ids,
+                            int32_t window, int32_t causal_mode, void* out, float* lse,
+                            int32_t total_tokens, int32_t num_docs, int32_t hq, int32_t hkv,
+                            int32_t d, int32_t dtype, float scale, void* stream) {
+  if (total_tokens > 0 && (lse == nullptr || ((uintptr_t)lse & 3u))) return SWA_EINVAL;
+  return prefill_impl(q, k, v, cu_seqlens, cu_seqlens, doc_or_block_ids, window, causal_mode,
+                      out, lse, total_tokens, total_tokens, num_docs, hq, hkv, d, dtype, scale,
+                      stream);
+}
+
 SWA_API size_t swa_prefill_backward_workspace_bytes(int32_t total_tokens, int32_t hq) {
   if (total_tokens < 0 || hq <= 0) return 0;
   return swa::bwd_workspace_bytes(total_tokens, hq);
@@ -145,10 +176,10 @@ SWA_API size_t swa_prefill_backward_workspace_bytes(int32_t total_tokens, int32_
 SWA_API int swa_prefill_backward(const void* q, const void* k, const void* v, const void* out,
                                  const void* dout, const int32_t* cu_seqlens,
                                  const int32_t* doc_or_block_ids, int32_t window,
-                                 int32_t causal_mode, void* dq, void* dk, void* dv,
-                                 int32_t total_tokens, int32_t num_docs, int32_t hq, int32_t hkv,
-                                 int32_t d, int32_t dtype, float scale, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 int32_t causal_mode, const float* lse, void* dq, void* dk,
+                                 void* dv, int32_t total_tokens, int32_t num_docs, int32_t hq,
+                                 int32_t hkv, int32_t d, int32_t dtype, float scale,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_heads(hq, hkv, d, dtype, true);
   if (rc) return rc;
   if (!swa::bwd_supported(d, dtype)) return SWA_EUNSUPPORTED;
@@ -163,6 +194,7 @@ SWA_API int swa_prefill_backward(const void* q, const void* k, const void* v, co
   if (causal_mode == SWA_BLOCKWISE &&
       (doc_or_block_ids == nullptr || ((uintptr_t)doc_or_block_ids & 3u)))
     return SWA_EINVAL;
+  if ((uintptr_t)lse & 3u) return SWA_EINVAL;
   // tile offsets (64 rows of hq * d elements) stay below 2^31 bytes
   if ((int64_t)hq * d >= ((int64_t)1 << 22) ||
       (int64_t)total_tokens * hq * d >= (int64_t)1 << 62)
@@ -191,6 +223,7 @@ SWA_API int swa_prefill_backward(const void* q, const void* k, const void* v, co
   a.d = d;
   a.dtype = dtype;
   a.scale = scale;
+  a.lse = lse;
   a.workspace = workspace;
   a.stream = (hipStream_t)stream;
   return swa::launch_prefill_bwd(a);

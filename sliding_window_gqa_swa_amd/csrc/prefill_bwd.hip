@@ -45,7 +45,7 @@ int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
     if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
     hipLaunchKernelGGL((bwd_dq_kernel<D, T, MB>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.out,
-                       (const T*)a.dout, w.lo, w.hi, T_, a.hq, a.hkv, c, a.scale, ntiles,
+                       (const T*)a.dout, w.lo, w.hi, a.lse, T_, a.hq, a.hkv, c, a.scale, ntiles,
                        (int)nwork, (int)per_xcd, (T*)a.dq, w.lse, w.delta);
   }
   {

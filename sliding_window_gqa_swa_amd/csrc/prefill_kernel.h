@@ -60,6 +60,7 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 
 constexpr float kPrefillLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 // cu_seqlens entries cached in LDS for the per-row document lookup; larger
 // batches of documents search global memory instead
 constexpr int kCuCache = 1024;
@@ -448,12 +449,13 @@ __device__ void lpt_select(const int* cu_s, const int* cuk_s, int ndocs, int Tto
   for (int x = 0; x < 2; ++x) out[x] = pos[x] < P ? min(max(sel_s[4 + x], 0), P - 1) : -1;
 }
 
-template <int D, typename T, int MB, int BN, int NW, int GH, bool PL>
+template <int D, typename T, int MB, int BN, int NW, int GH, bool PL, bool LSE>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 256 && (D <= 128 || !PL) && !std::is_same<T, float>::value) ? 2 : 1)
 void prefill_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ cuk, int ndocs,
-    const int32_t* __restrict__ ids, int W, int mode, T* __restrict__ out, int Ttot, int Tk,
+    const int32_t* __restrict__ ids, int W, int mode, T* __restrict__ out,
+    float* __restrict__ lse_out, int Ttot, int Tk,
     int hq, int hkv,
     float qk_scale_log2, int ntiles, int nwork, int work_per_xcd, int slots_per_xcd,
     int colocated) {
@@ -1392,6 +1394,13 @@ void prefill_fwd_kernel(
         }
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const int rr = mb * 16 + c16;  // row within the wave
+        if (LSE && grp == 0 && q0 + rb * G::WR + rr < Ttot) {
+          // the row's log-sum-exp: its reference (log2 units) plus log2 of
+          // its sum relative to it, in natural-log units
+          const float ref2 = kDiagRef ? -s_init[mb][0] : m_ref[mb] * c_scale;
+          lse_out[(size_t)h * Ttot + q0 + rb * G::WR + rr] =
+              l > 0.f ? (ref2 + __builtin_log2f(l)) * kLn2 : -INFINITY;
+        }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const floatx4 x = o_acc[mb][dt] * inv;
@@ -1611,6 +1620,8 @@ void prefill_fwd_kernel(
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int i = row_i[mb];
     if (i >= Ttot) continue;
+    if (LSE && grp == 0)
+      lse_out[(size_t)h * Ttot + i] = l > 0.f ? (m_ref[mb] * c_scale + __builtin_log2f(l)) * kLn2 : -INFINITY;
     T* orow = out + ((size_t)i * hq + h) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {

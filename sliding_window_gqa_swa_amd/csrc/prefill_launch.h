@@ -28,11 +28,15 @@ int launch_prefill_cfg(const PrefillArgs& a) {
     slots = std::max(slots, 1);
     colocated = kWgPerCu == 2 && slots == fill;  // two work-groups on every CU
   }
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL>), dim3((unsigned)(8 * slots)),
-                     dim3(G::NT), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                     a.cu_q, a.cu_k, a.num_docs, a.ids, a.window, a.mode, (T*)a.out, a.total_q,
-                     a.total_k, hq, hkv, a.scale * kPrefillLog2e, ntiles, (int)nwork,
-                     (int)per_xcd, slots, colocated);
+  // (the variant that stores the row log-sum-exp is a separate kernel, so
+  // that its extra live values cost the plain forward no registers)
+  auto kern = a.lse != nullptr ? prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL, true>
+                               : prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(8 * slots)), dim3(G::NT), 0, a.stream,
+                     (const T*)a.q, (const T*)a.k, (const T*)a.v, a.cu_q, a.cu_k, a.num_docs,
+                     a.ids, a.window, a.mode, (T*)a.out, a.lse, a.total_q, a.total_k, hq, hkv,
+                     a.scale * kPrefillLog2e, ntiles, (int)nwork, (int)per_xcd, slots,
+                     colocated);
   return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
 }
 

@@ -54,6 +54,7 @@ struct PrefillArgs {
   const int32_t* ids;  // key-indexed block ids (SWA_BLOCKWISE), else NULL
   int window, mode;
   void* out;
+  float* lse;  // [hq, total_q] row log-sum-exp (natural log), or NULL
   int total_q, total_k, num_docs, hq, hkv, d, dtype;
   float scale;
   hipStream_t stream;
@@ -76,6 +77,7 @@ struct PrefillBwdArgs {
   void* dv;
   int total, num_docs, hq, hkv, d, dtype;
   float scale;
+  const float* lse;  // [hq, T] forward row log-sum-exp, or NULL (recomputed)
   void* workspace;
   hipStream_t stream;
 };

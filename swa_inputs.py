@@ -121,6 +121,14 @@ def prefill_16k_gqa_d512() -> PrefillCase:
                        hq=16, hkv=8, d=512, window=4096, mode=CAUSAL, seed=4)
 
 
+def prefill_16k_mha_d128_w4k() -> PrefillCase:
+    """One 16K-token document, 32 MHA heads of size 128, window 4K: the
+    Llama-7B-shaped windowed row of the [SDPA] Benchmark table (timed there
+    as forward + backward)."""
+    return PrefillCase("prefill_16k_mha_d128_w4k", np.array([0, 16384], dtype=np.int32),
+                       hq=32, hkv=32, d=128, window=4096, mode=CAUSAL, seed=7)
+
+
 def prefill_vlm_4096_d256() -> PrefillCase:
     return PrefillCase("prefill_vlm_4096_d256", np.array([0, 4096], dtype=np.int32),
                        hq=8, hkv=4, d=256, window=1024, mode=BLOCKWISE,
@@ -140,6 +148,7 @@ PREFILL_WORKLOADS = {
     "prefill_16k_gqa_d512": prefill_16k_gqa_d512,
     "prefill_vlm_4096_d256": prefill_vlm_4096_d256,
     "prefill_4x1024_gqa_d320": prefill_4x1024_gqa_d320,
+    "prefill_16k_mha_d128_w4k": prefill_16k_mha_d128_w4k,
 }
 
 

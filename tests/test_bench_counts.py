@@ -21,6 +21,8 @@ def test_useful_flops_of_the_prefill_workloads():
     # 4 documents x 524,800 causal pairs (the window covers each document),
     # 16 heads, 4 * 320 flop per pair
     assert bench.useful_flops(si.prefill_4x1024_gqa_d320()) == 4 * 524800 * 16 * 4 * 320
+    # the 16k window-4096 pair count of the D = 512 workload, 32 heads, D = 128
+    assert bench.useful_flops(si.prefill_16k_mha_d128_w4k()) == 58722304 * 32 * 4 * 128
 
 
 def test_decode_valid_rows():

@@ -112,12 +112,13 @@ def test_prefill_empty_is_a_no_op():
 
 
 def _backward(**kw):
-    a = dict(q=A, k=A, v=A, out=A, dout=A, cu=B, ids=None, window=16, mode=0, dq=A, dk=A, dv=A,
+    a = dict(q=A, k=A, v=A, out=A, dout=A, cu=B, ids=None, window=16, mode=0, lse=None, dq=A,
+             dk=A, dv=A,
              T=10, nd=1, hq=4, hkv=2, d=128, dtype=0, ws=A, wsb=1 << 30)
     a.update(kw)
     return _lib.lib().swa_prefill_backward(
         a["q"], a["k"], a["v"], a["out"], a["dout"], a["cu"], a["ids"], a["window"], a["mode"],
-        a["dq"], a["dk"], a["dv"], a["T"], a["nd"], a["hq"], a["hkv"], a["d"], a["dtype"], 0.0,
+        a["lse"], a["dq"], a["dk"], a["dv"], a["T"], a["nd"], a["hq"], a["hkv"], a["d"], a["dtype"], 0.0,
         a["ws"], a["wsb"], None)
 
 
@@ -137,6 +138,7 @@ def _backward(**kw):
     (dict(ws=None), _lib.SWA_EWORKSPACE),
     (dict(wsb=16), _lib.SWA_EWORKSPACE),
     (dict(ws=A + 8), _lib.SWA_EWORKSPACE),
+    (dict(lse=B + 2), _lib.SWA_EINVAL),
 ])
 def test_prefill_backward_rejects(kw, code):
     assert _backward(**kw) == code
@@ -157,6 +159,17 @@ def test_prefill_backward_sizes():
         n = L.swa_prefill_backward_workspace_bytes(T, hq)
         assert n >= 8 * T * hq + 8 * T and n % 256 == 0
     assert L.swa_prefill_backward_workspace_bytes(-1, 4) == 0
+
+
+def test_prefill_lse_rejects():
+    L = _lib.lib()
+
+    def call(lse, T=10, d=128):
+        return L.swa_prefill_lse(A, A, A, B, None, 16, 0, A, lse, T, 1, 4, 2, d, 0, 0.0, None)
+    assert call(None) == _lib.SWA_EINVAL
+    assert call(B + 2) == _lib.SWA_EINVAL
+    assert call(B, d=96) == _lib.SWA_EUNSUPPORTED
+    assert call(None, T=0) == _lib.SWA_OK
 
 
 def _decode(**kw):
