@@ -450,11 +450,22 @@ def summarize_trace(trace_dir):
     tot = sum(r[4] for r in rows) or 1
 
     def short(nm):
-        m = re.search(r"prefill_fwd_kernelILi(\d+)E(DF16b|f)Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)", nm)
+        m = re.search(r"prefill_fwd_kernelILi(\d+)E(DF16b|f)Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)", nm)
         if m:
-            return "prefill_fwd_kernel<D=%s,%s,MB=%s,BN=%s,NW=%s,GH=%s%s>" % (
+            return "prefill_fwd_kernel<D=%s,%s,MB=%s,BN=%s,NW=%s,GH=%s%s%s>" % (
                 m.group(1), "bf16" if m.group(2) == "DF16b" else "f32", m.group(3), m.group(4),
-                m.group(5), m.group(6), ",pipelined" if m.group(7) == "1" else "")
+                m.group(5), m.group(6), ",pipelined" if m.group(7) == "1" else "",
+                ",lse" if m.group(8) == "1" else "")
+        m = re.search(r"bwd_dq_kernelILi(\d+)E(DF16b|f)Li(\d+)E", nm)
+        if m:
+            return "bwd_dq_kernel<D=%s,%s,MB=%s>" % (
+                m.group(1), "bf16" if m.group(2) == "DF16b" else "f32", m.group(3))
+        m = re.search(r"bwd_dkdv_kernelILi(\d+)E(DF16b|f)Li(\d+)ELi(\d+)ELi(\d+)E", nm)
+        if m:
+            return "bwd_dkdv_kernel<D=%s,%s,DS=%s,KB=%s>" % (
+                m.group(1), "bf16" if m.group(2) == "DF16b" else "f32", m.group(3), m.group(4))
+        if "bwd_rows_kernel" in nm:
+            return "bwd_rows_kernel"
         m = re.search(r"decode_split_kernelILi(\d+)E(DF16b|f)Li(\d+)ELb(\d)", nm)
         if m:
             return "decode_split_kernel<D=%s,%s,GB=%s%s>" % (
