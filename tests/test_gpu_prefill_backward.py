@@ -149,6 +149,23 @@ def test_backward_window_one(d, dtype):
     assert_grad_close(dv, want, dtype, "dv W=1 d=%d %s" % (d, dtype))
 
 
+def test_backward_is_deterministic():
+    """Every output element has one writer and a fixed summation order:
+    two runs give the same bits."""
+    require_gpu()
+    rng = si.rng_for(3)
+    T, hq, hkv, d = 700, 4, 2, 128
+    cu = np.array([0, 300, T], np.int32)
+    q, k, v, do = (si.normal(rng, s, "bf16") for s in [(T, hq, d), (T, hkv, d), (T, hkv, d), (T, hq, d)])
+    args = [dev(x) for x in (q, k, v)]
+    out = api.prefill(*args, dev(cu), None, 100, CAUSAL)
+    log("backward determinism")
+    a = [host(x) for x in api.prefill_backward(*args, out, dev(do), dev(cu), None, 100, CAUSAL)]
+    b = [host(x) for x in api.prefill_backward(*args, out, dev(do), dev(cu), None, 100, CAUSAL)]
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_backward_empty_is_a_no_op():
     require_gpu()
     q = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device="cuda")
