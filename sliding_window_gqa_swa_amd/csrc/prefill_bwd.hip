@@ -10,7 +10,10 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// query rows per dq work-group: 32 rows per wave while the fragments fit
+// 16-row blocks per dq wave: one at every head size (at D = 128 the 16-row
+// wave lets two work-groups share each CU: 147 us against 187 us for
+// 32-row waves with one work-group per CU, measured; larger D have no
+// registers for 32 rows)
 template <int D, typename T>
 constexpr int dq_mb() {
   return 1;
