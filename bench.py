@@ -491,6 +491,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="run the decode workloads only and print their results (for "
+                         "counter runs; not the benchmark line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy 4 times (known bytes, for "
                          "scaling HBM counters)")
@@ -529,6 +532,15 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.only_decode:
+        res = {}
+        for name in ("decode_b64_d256", "decode_single_d256"):
+            res[name] = bench_decode(name, torch, api)
+            print("%s: decode %.2f us, %.0f GB/s; fused step %.2f us" % (
+                name, res[name]["decode_us"], res[name]["decode_gbs"],
+                res[name]["us_per_step_fused"]), file=sys.stderr, flush=True)
+        print(json.dumps({"workloads": res}), flush=True)
+        return
     head = bench_prefill(HEADLINE, args.steps, args.warmup, torch, api)
     print("headline %s: %.3f ms, %.1f TFLOP/s" % (HEADLINE, head["ms_per_call"], head["tflops"]),
           file=sys.stderr, flush=True)
