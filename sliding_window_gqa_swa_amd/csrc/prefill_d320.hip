@@ -9,9 +9,10 @@ namespace swa {
 int launch_prefill_d320(const PrefillArgs& a) {
   const int g = a.hq / a.hkv;
   if (a.dtype == SWA_BF16) {
+    // computed as head size 384 with zero padding on the pipelined loop
     if (g % 2 == 0)
-      return launch_prefill_cfg<320, __bf16, 1, 32, 4, 2>(a);
-    return launch_prefill_cfg<320, __bf16, 1, 32, 4, 1>(a);
+      return launch_prefill_cfg<384, __bf16, 2, 32, 4, 2, true, 320>(a);
+    return launch_prefill_cfg<384, __bf16, 2, 32, 4, 1, true, 320>(a);
   }
   return launch_prefill_cfg<320, float, 1, 16, 4, 1>(a);
 }

@@ -449,7 +449,7 @@ __device__ void lpt_select(const int* cu_s, const int* cuk_s, int ndocs, int Tto
   for (int x = 0; x < 2; ++x) out[x] = pos[x] < P ? min(max(sel_s[4 + x], 0), P - 1) : -1;
 }
 
-template <int D, typename T, int MB, int BN, int NW, int GH, bool PL, bool LSE>
+template <int D, typename T, int MB, int BN, int NW, int GH, bool PL, bool LSE, int DM>
 __global__ __launch_bounds__(NW * 64, (NW == 4 && D <= 256 && (D <= 128 || !PL) && !std::is_same<T, float>::value) ? 2 : 1)
 void prefill_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -462,6 +462,14 @@ void prefill_fwd_kernel(
   using G = PfGeom<D, T, MB, BN, NW, GH, PL>;
   using TR = typename G::TR;
   constexpr bool kF32 = std::is_same<T, float>::value;
+  // DM: the head size of the tensors in memory.  D >= DM is the size the
+  // kernel computes with: the extra dimensions are zeros (K, V and Q loads
+  // past DM bring zeros, which add nothing to a score, and output columns
+  // past DM are not stored), so a head size with no schedule of its own
+  // runs on the pipelined loop of the next multiple of 128.
+  static_assert(DM <= D && DM % TR::VEC == 0, "memory rows are whole chunks of the computed rows");
+  static_assert(DM == D || PL, "padded head sizes run the pipelined loop only");
+  constexpr int CPM = DM / TR::VEC;  // 16-byte chunks of a row in memory
 
   __shared__ __attribute__((aligned(1024))) unsigned char ring[G::STAGES][G::STAGE_BYTES];
   __shared__ int lo_s[G::BM], hi_s[G::BM];
@@ -551,9 +559,9 @@ void prefill_fwd_kernel(
   const int rb = wave / GH;  // row block of this wave
   const int h = hbase + jh;
 
-  const size_t kv_row_stride = (size_t)hkv * D;
-  const T* kbase = k + (size_t)kvh * D;
-  const T* vbase = v + (size_t)kvh * D;
+  const size_t kv_row_stride = (size_t)hkv * DM;
+  const T* kbase = k + (size_t)kvh * DM;
+  const T* vbase = v + (size_t)kvh * DM;
   // Direct-to-LDS tile loads.  Wave w issues UPT loads per tensor per tile;
   // load i covers LDS slots [(w*UPT + i)*64, +64) of 16 bytes, slot s being
   // row s / CPR, stored chunk position s % CPR, i.e. source chunk
@@ -597,7 +605,14 @@ void prefill_fwd_kernel(
   const uint32_t kring = ring_base, vring = ring_base + G::STAGES * G::TILE_BYTES;
   int voff[G::UPT];
 #pragma unroll
-  for (int i = 0; i < G::UPT; ++i) voff[i] = unit_off[i] * (int)sizeof(T);
+  for (int i = 0; i < G::UPT; ++i) {
+    voff[i] = unit_off[i] * (int)sizeof(T);
+    if constexpr (DM < D) {  // padding chunks: out of range, they load zeros
+      const int s_ = (wave_u * G::UPT + i) * 64 + lane;
+      const int r_ = s_ / G::CPR;
+      if (chunk_src<G::CPR>(r_, s_ - r_ * G::CPR) >= CPM) voff[i] = kBufferOob;
+    }
+  }
   // one K or V tile (keys k0 .. k0+BN-1 of this kv head) into an LDS stage;
   // key rows at or past Tk fall outside the buffer and arrive as zeros
   // descriptor of one K or V tile; `want` false gives an empty buffer, whose
@@ -635,12 +650,12 @@ void prefill_fwd_kernel(
   for (int mb = 0; mb < MB; ++mb) {
     const int i = q0 + rb * G::WR + mb * 16 + c16;
     const bool ok = i < Ttot;
-    const T* qrow = q + ((size_t)(ok ? i : 0) * hq + h) * D;
+    const T* qrow = q + ((size_t)(ok ? i : 0) * hq + h) * DM;
 #pragma unroll
     for (int kk = 0; kk < G::QREG; ++kk) {
       const int d0 = kF32 ? grp * (D / 4) + kk * 4 : kk * 32 + 8 * grp;
       QF x = QF{};
-      if (ok) x = *reinterpret_cast<const QF*>(qrow + d0);
+      if (ok && d0 < DM) x = *reinterpret_cast<const QF*>(qrow + d0);
       qf[mb][kk] = x;
     }
   }
@@ -1411,14 +1426,30 @@ void prefill_fwd_kernel(
           *reinterpret_cast<bf16x4*>(ost + rr * ROWB + pc * 16 + (grp & 1) * 8) = w;
         }
       }
-      constexpr int RPI = 64 / CPO;  // rows per wave-wide store
+      if constexpr (DM == D && 64 % CPO == 0) {
+        constexpr int RPI = 64 / CPO;  // rows per wave-wide store
 #pragma unroll
-      for (int j = 0; j < G::WR / RPI; ++j) {
-        const int rr = j * RPI + lane / CPO, ch = lane % CPO;
-        const int pc = (ch & ~15) | ((ch + rr) & 15);
-        const u32x4 x = *reinterpret_cast<const u32x4*>(ost + rr * ROWB + pc * 16);
-        const int i = q0 + rb * G::WR + rr;
-        if (i < Ttot) *reinterpret_cast<u32x4*>(out + ((size_t)i * hq + h) * D + ch * 8) = x;
+        for (int j = 0; j < G::WR / RPI; ++j) {
+          const int rr = j * RPI + lane / CPO, ch = lane % CPO;
+          const int pc = (ch & ~15) | ((ch + rr) & 15);
+          const u32x4 x = *reinterpret_cast<const u32x4*>(ost + rr * ROWB + pc * 16);
+          const int i = q0 + rb * G::WR + rr;
+          if (i < Ttot) *reinterpret_cast<u32x4*>(out + ((size_t)i * hq + h) * D + ch * 8) = x;
+        }
+      } else {
+        // the wave's rows' stored chunks (CPM of each) in order, 64 per pass
+        constexpr int CPW = G::WR * CPM;
+#pragma unroll
+        for (int j = 0; j < (CPW + 63) / 64; ++j) {
+          const int idx = j * 64 + lane;
+          const int rr = idx / CPM, ch = idx - rr * CPM;
+          const int i = q0 + rb * G::WR + rr;
+          if (idx < CPW && i < Ttot) {
+            const int pc = (ch & ~15) | ((ch + rr) & 15);
+            const u32x4 x = *reinterpret_cast<const u32x4*>(ost + rr * ROWB + pc * 16);
+            *reinterpret_cast<u32x4*>(out + ((size_t)i * hq + h) * DM + ch * 8) = x;
+          }
+        }
       }
     }
     return;

@@ -8,7 +8,9 @@
 
 namespace swa {
 
-template <int D, typename T, int MB, int BN, int NW, int GH, bool PL = false>
+// DM: the head size in memory (D > DM: computed zero-padded to D, see the
+// kernel)
+template <int D, typename T, int MB, int BN, int NW, int GH, bool PL = false, int DM = D>
 int launch_prefill_cfg(const PrefillArgs& a) {
   using G = PfGeom<D, T, MB, BN, NW, GH, PL>;
   const int ntiles = (a.total_q + G::BM - 1) / G::BM;
@@ -30,8 +32,8 @@ int launch_prefill_cfg(const PrefillArgs& a) {
   }
   // (the variant that stores the row log-sum-exp is a separate kernel, so
   // that its extra live values cost the plain forward no registers)
-  auto kern = a.lse != nullptr ? prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL, true>
-                               : prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL, false>;
+  auto kern = a.lse != nullptr ? prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL, true, DM>
+                               : prefill_fwd_kernel<D, T, MB, BN, NW, GH, PL, false, DM>;
   hipLaunchKernelGGL(kern, dim3((unsigned)(8 * slots)), dim3(G::NT), 0, a.stream,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, a.cu_q, a.cu_k, a.num_docs,
                      a.ids, a.window, a.mode, (T*)a.out, a.lse, a.total_q, a.total_k, hq, hkv,
