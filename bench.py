@@ -450,12 +450,13 @@ def summarize_trace(trace_dir):
     tot = sum(r[4] for r in rows) or 1
 
     def short(nm):
-        m = re.search(r"prefill_fwd_kernelILi(\d+)E(DF16b|f)Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)", nm)
+        m = re.search(r"prefill_fwd_kernelILi(\d+)E(DF16b|f)Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)ELi(\d+)E", nm)
         if m:
-            return "prefill_fwd_kernel<D=%s,%s,MB=%s,BN=%s,NW=%s,GH=%s%s%s>" % (
+            return "prefill_fwd_kernel<D=%s,%s,MB=%s,BN=%s,NW=%s,GH=%s%s%s%s>" % (
                 m.group(1), "bf16" if m.group(2) == "DF16b" else "f32", m.group(3), m.group(4),
                 m.group(5), m.group(6), ",pipelined" if m.group(7) == "1" else "",
-                ",lse" if m.group(8) == "1" else "")
+                ",lse" if m.group(8) == "1" else "",
+                "" if m.group(9) == m.group(1) else ",head size %s in memory" % m.group(9))
         m = re.search(r"bwd_dq_kernelILi(\d+)E(DF16b|f)Li(\d+)E", nm)
         if m:
             return "bwd_dq_kernel<D=%s,%s,MB=%s>" % (
