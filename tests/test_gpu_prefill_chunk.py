@@ -111,3 +111,71 @@ def test_chunk_of_16k_gqa_d512_window_4096_sampled_rows():
                     np.int32)
     want = orc.prefill_chunk(qc, k, v, cu_q, c.cu_seqlens, None, c.window, CAUSAL, rows=rows)
     assert_close(got[rows], want, "bf16", "16k chunk")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunked_prefill_then_compact_then_decode(dtype):
+    """The serving flow of [SPYRE] Summary end to end on the GPU: three
+    prompts of ragged lengths are prefilled in 256-token chunks into one
+    packed prompt-sized cache (each chunk against its document's keys so
+    far), the rings are compacted directly from that cache, and fused decode
+    steps run past a roll.  Every chunk's rows are checked against the
+    oracle's whole-prompt prefill rows, every step against the oracle's
+    decode on the linear history."""
+    require_gpu()
+    rng = si.rng_for(4242)
+    lens = [700, 1200, 301]
+    hq, hkv, d, W, A, C = 4, 2, 128, 512, 64, 256
+    R = W + A
+    B = len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = si.normal(rng, (T, hq, d), dtype)
+    k = si.normal(rng, (T, hkv, d), dtype)
+    v = si.normal(rng, (T, hkv, d), dtype)
+    kd, vd = dev(k), dev(v)
+    # chunk j of every prompt that still has rows: queries [j C, min((j+1) C, L))
+    want_all = orc.prefill(q, k, v, cu, None, W, CAUSAL)
+    for j in range((max(lens) + C - 1) // C):
+        rows, cuq, cuk = [], [0], [0]
+        for b, L in enumerate(lens):
+            a, e = min(j * C, L), min((j + 1) * C, L)
+            rows += list(range(int(cu[b]) + a, int(cu[b]) + e))
+            cuq.append(cuq[-1] + (e - a))
+            cuk.append(cuk[-1] + e)
+        if not rows:
+            break
+        rows = np.array(rows, np.int64)
+        # each document's keys so far, packed: its first e rows
+        kidx = np.concatenate([np.arange(int(cu[b]), int(cu[b]) + min((j + 1) * C, L))
+                               for b, L in enumerate(lens)])
+        log("chunk %d %s rows %d" % (j, dtype, rows.size))
+        out = api.prefill_chunk(dev(q[rows]), dev(k[kidx]), dev(v[kidx]),
+                                dev(np.array(cuq, np.int32)), dev(np.array(cuk, np.int32)),
+                                None, W, CAUSAL)
+        assert_close(host(out), want_all[rows], dtype, "chunk %d" % j)
+    # compaction straight from the packed prompt cache, then decode steps
+    kr = torch.zeros((B, hkv, R, d), dtype=kd.dtype, device="cuda")
+    vr = torch.zeros_like(kr)
+    meta = torch.zeros((B, 4), dtype=torch.int32, device="cuda")
+    api.cache_compact(kd, vd, dev(cu), kr, vr, meta, W, dev(np.array(lens, np.int32)), None)
+    hist_k = [k[cu[b]:cu[b + 1]] for b in range(B)]
+    hist_v = [v[cu[b]:cu[b + 1]] for b in range(B)]
+    pos = np.array(lens, np.int64) - 1
+    for s in range(A + 6):  # the 64th append after compaction needs the roll
+        qn = si.normal(rng, (B, hq, d), dtype)
+        kn = si.normal(rng, (B, hkv, d), dtype)
+        vn = si.normal(rng, (B, hkv, d), dtype)
+        log("decode step %d %s" % (s, dtype))
+        out = api.decode_step(dev(qn), dev(kn), dev(vn), kr, vr, meta, W)
+        pos += 1
+        for b in range(B):
+            hist_k[b] = np.concatenate([hist_k[b], kn[b:b + 1]])
+            hist_v[b] = np.concatenate([hist_v[b], vn[b:b + 1]])
+        off = np.concatenate([[0], np.cumsum([h.shape[0] for h in hist_k])[:-1]])
+        want = orc.decode_linear(qn, np.concatenate(hist_k), np.concatenate(hist_v), off,
+                                 [0] * B, [h.shape[0] for h in hist_k], pos, [0] * B, W)
+        assert_close(host(out), want, dtype, "decode step %d" % s)
+    m = host(meta)
+    assert not (m[:, 3] < 0).any(), "a sequence overflowed its ring"
+    assert (m[:, 0] == pos).all()
