@@ -9,7 +9,10 @@ step is one swa_prefill over one batch; inputs rotate over several resident
 copies so the 256 MB Infinity Cache cannot hold them.  The other prefill
 workloads and the two ring-decode workloads (append + decode per step, the
 roll every 64 steps) are measured in the same run and reported under
-"workloads".  Times come from HIP events on the stream the kernels run on.
+"workloads".  Times come from HIP events on the stream the kernels run on,
+taken on settled GPU clocks: the default warm-up (1000 steps, about 60 ms
+of the headline kernel) and at least 60 ms of untimed work before every
+other timed region (an idle GPU runs the first launches at lower clocks).
 
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the headline
 workload on this host's cores.  `roofline.traffic` is read from the counter
@@ -42,6 +45,11 @@ KERNEL_SOURCES = {
 
 
 # ------------------------------------------------------------ work counts
+# untimed GPU work before each timed region of the non-headline workloads,
+# so that it starts on settled clocks (see settle())
+SETTLE_MS = 60.0
+
+
 def causal_window_pairs(n: int, W: int) -> int:
     """Pairs (i, j), j <= i, i - j < W in one document of n tokens."""
     if W <= 0 or W >= n:
@@ -106,10 +114,33 @@ def to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def time_loop(fn, steps, warmup, torch):
-    """ms per call of fn(i) over `steps` calls, HIP events on the current stream."""
+def settle(fn, torch, ms):
+    """Call fn(i) until at least `ms` of GPU time has passed: an idle MI355X
+    runs the first launches at lower clocks (the headline prefill takes ~68
+    us per call from idle, ~60 us after 15 ms of sustained work and 53-56 us
+    after 30 ms, measured), so every timed region starts on settled clocks."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    done, n, i = 0.0, 4, 0
+    while done < ms:
+        e0.record()
+        for _ in range(n):
+            fn(i)
+            i += 1
+        e1.record()
+        torch.cuda.synchronize()
+        done += e0.elapsed_time(e1)
+        n = min(n * 2, 4096)
+
+
+def time_loop(fn, steps, warmup, torch, settle_ms=0.0):
+    """ms per call of fn(i) over `steps` calls, HIP events on the current
+    stream, after `warmup` untimed calls (and, with settle_ms, untimed calls
+    until the clocks have settled)."""
     for i in range(warmup):
         fn(i)
+    if settle_ms > 0:
+        settle(fn, torch, settle_ms)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -121,7 +152,7 @@ def time_loop(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps
 
 
-def bench_prefill(name, steps, warmup, torch, api, nsets=None):
+def bench_prefill(name, steps, warmup, torch, api, nsets=None, settle_ms=0.0):
     c = si.PREFILL_WORKLOADS[name]()
     q, k, v = c.tensors("bf16")
     in_bytes = (q.nbytes + k.nbytes + v.nbytes) * 2  # + out
@@ -142,9 +173,9 @@ def bench_prefill(name, steps, warmup, torch, api, nsets=None):
         s = i % nsets
         api.prefill(sets[s][0], sets[s][1], sets[s][2], cu, ids, c.window, c.mode, out=outs[s])
 
-    ms = time_loop(step, steps, warmup, torch)
+    ms = time_loop(step, steps, warmup, torch, settle_ms)
     # warm: one input set every call (K/V and Q stay in the Infinity Cache)
-    warm_ms = time_loop(lambda i: step(0), steps, warmup, torch)
+    warm_ms = time_loop(lambda i: step(0), steps, warmup, torch, settle_ms)
     fl = useful_flops(c)
     return {
         "workload": name, "T": c.T, "docs": int(c.cu_seqlens.size - 1), "hq": c.hq,
@@ -176,7 +207,7 @@ def bench_prefill_chunked(name, nchunks, steps, warmup, torch, api):
             api.prefill_chunk(qd[j * L:e], kd[:e], vd[:e], cuq, cuks[j], None, c.window, c.mode,
                               out=out[j * L:e])
 
-    ms = time_loop(step, steps, warmup, torch)
+    ms = time_loop(step, steps, warmup, torch, SETTLE_MS)
     fl = useful_flops(c)
     return {"workload": name + "_in_%d_chunks" % nchunks, "chunk_tokens": L, "useful_flop": fl,
             "ms_per_prompt": ms, "tflops": fl / (ms * 1e-3) / 1e12,
@@ -213,9 +244,9 @@ def bench_prefill_backward(name, steps, warmup, torch, api, pages_fwd_bwd_ms=Non
         api.prefill_lse(qd, kd, vd, cu, ids, c.window, c.mode, out=out, lse=lse)
         bwd(i)
 
-    ms = time_loop(bwd, steps, warmup, torch)
-    ms_rc = time_loop(bwd_recompute, steps, warmup, torch)
-    ms_fb = time_loop(fwd_bwd, steps, warmup, torch)
+    ms = time_loop(bwd, steps, warmup, torch, SETTLE_MS)
+    ms_rc = time_loop(bwd_recompute, steps, warmup, torch, SETTLE_MS)
+    ms_fb = time_loop(fwd_bwd, steps, warmup, torch, SETTLE_MS)
     fl = 5 * useful_flops(c) // 2
     r = {"workload": name + "_backward", "useful_flop": fl, "ms_per_call": ms,
          "tflops": fl / (ms * 1e-3) / 1e12,
@@ -267,6 +298,11 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
             api.cache_append(kn, vn, kr, vr, meta)
     torch.cuda.synchronize()
     timed = steps_in[c.pre_appends:]
+    # settled clocks first (decode alone only reads the rings)
+    q_last = timed[-1][0]
+    settle(lambda i: api.decode(q_last, rings[i % layers][0], rings[i % layers][1],
+                                rings[i % layers][2], W, out=outs[i % layers], workspace=ws),
+           torch, SETTLE_MS)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -287,10 +323,11 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
         kr, vr, meta = rings[i % layers]
         api.decode(q, kr, vr, meta, W, out=outs[i % layers], workspace=ws)
 
-    dec_ms = time_loop(dstep, reps * layers, warmup * layers, torch)
+    dec_ms = time_loop(dstep, reps * layers, warmup * layers, torch, SETTLE_MS)
     # warm: the same ring set every call
     warm_ms = time_loop(lambda i: api.decode(q, rings[0][0], rings[0][1], rings[0][2], W,
-                                             out=outs[0], workspace=ws), reps, warmup, torch)
+                                             out=outs[0], workspace=ws), reps, warmup, torch,
+                        SETTLE_MS)
 
     # the same steps as one swa_decode_step launch per layer (roll by
     # metadata + append + decode), on freshly compacted ring sets
@@ -304,6 +341,7 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
                 api.decode_step(q0, kn0, vn0, kr, vr, meta, W, out=outs[li], workspace=ws)
         torch.cuda.synchronize()
 
+    settle(dstep, torch, SETTLE_MS)
     fresh_rings()
     e0.record()
     for t, (qq, kn, vn) in enumerate(timed):
@@ -321,6 +359,7 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
                 api.decode_step(qq, kn, vn, kr, vr, meta, W, out=outs[li], workspace=ws)
     fresh_rings()
     graph.replay()  # warm-up
+    settle(dstep, torch, SETTLE_MS)
     fresh_rings()
     e0.record()
     graph.replay()
@@ -489,7 +528,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # (the default warm-up, about 60 ms of the headline prefill, brings the
+    # GPU to its settled clocks before the timed steps)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only-decode", action="store_true",
@@ -549,7 +590,8 @@ def main():
     if not args.only_headline:
         for name in ("prefill_16k_gqa_d512", "prefill_vlm_4096_d256", "prefill_4x1024_gqa_d320",
                      "prefill_16k_mha_d128_w4k"):
-            workloads[name] = bench_prefill(name, max(5, args.steps // 5), 3, torch, api)
+            workloads[name] = bench_prefill(name, max(5, args.steps // 5), 3, torch, api,
+                                            settle_ms=SETTLE_MS)
             print("%s: %.3f ms, %.1f TFLOP/s" % (name, workloads[name]["ms_per_call"],
                                                  workloads[name]["tflops"]), file=sys.stderr,
                   flush=True)
