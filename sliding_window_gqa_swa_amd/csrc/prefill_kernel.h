@@ -507,7 +507,7 @@ void prefill_fwd_kernel(
       cu_s[d] = cu[d];
       if (chunked) cuk_s[d] = cuk[d];
     }
-  const bool plan = cu_in_lds && P > 1 && P <= kPlanMaxItems;
+  const bool may_plan = cu_in_lds && P > 1 && P <= kPlanMaxItems;
   // Pipelined path: S = slots_per_xcd work-groups per XCD with at most two
   // items each: the sorted positions pos and 2S-1-pos, so the longest items
   // are paired with the shortest and run back to back (one launch ramp, one
@@ -524,9 +524,23 @@ void prefill_fwd_kernel(
     pos2 = pos < hs ? 3 * hs - 1 - pos : 4 * hs - 1 - (pos - hs);
   }
   int items[2] = {pos, pos2 < P ? pos2 : -1};
-  if (plan)
+  if (may_plan)
     for (int c = tid; c < kPlanBuckets; c += G::NT) hist_s[c] = 0;
   __syncthreads();  // cu_s and the histogram are ready
+  // Documents of equal query and key lengths (one document, or a batch of
+  // equal prompts): the work numbering already runs each head's tiles from
+  // the last (the longest under a causal or windowed mask) to the first,
+  // document after document, so positions pos and 2S-1-pos pair
+  // complementary tiles and the sort would only cost its time (2-3 us of a
+  // 60 us launch, measured).
+  bool plan = may_plan;
+  if (may_plan) {
+    bool same = true;
+    const int lq0 = cu_s[1] - cu_s[0], lk0 = cukl[1] - cukl[0];
+    for (int d = 1 + tid; d < ndocs; d += G::NT)
+      same &= (cu_s[d + 1] - cu_s[d] == lq0) && (cukl[d + 1] - cukl[d] == lk0);
+    plan = !__syncthreads_and(same);
+  }
   if (plan) {
     const int posv[2] = {pos, pos2};
     lpt_select<G::NT, G::BM, BN>(cu_s, cukl, ndocs, Ttot, Tk, W, ntiles, w0, P, posv, &ring[0][0], hist_s,
