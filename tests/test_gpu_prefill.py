@@ -167,9 +167,10 @@ def test_prefill_edge_shapes():
     api.prefill(z, zk, zk, torch.zeros(1, dtype=torch.int32, device="cuda"))
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("ndocs", [300, 1500])
 @pytest.mark.parametrize("mode", [CAUSAL, BLOCKWISE])
-def test_prefill_many_documents(ndocs, mode):
+def test_prefill_many_documents(ndocs, mode, d):
     """Many short documents of random length (1..24 tokens, some empty):
     tiles that span several documents and work items of many different
     costs.  1500 documents exceed the length table kept in LDS, which takes
@@ -179,16 +180,16 @@ def test_prefill_many_documents(ndocs, mode):
     lens = rng.integers(0, 25, size=ndocs)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu[-1])
-    d, hkv, g = 64, 2, 2
+    hkv, g = 2, 2
     q = si.normal(rng, (T, hkv * g, d), "bf16")
     k = si.normal(rng, (T, hkv, d), "bf16")
     v = si.normal(rng, (T, hkv, d), "bf16")
     ids = _ids_for(T, cu, 7100 + ndocs) if mode == BLOCKWISE else None
     for W in (0, 5):
-        log("prefill many docs ndocs=%d T=%d mode=%d W=%d" % (ndocs, T, mode, W))
+        log("prefill many docs ndocs=%d T=%d mode=%d W=%d d=%d" % (ndocs, T, mode, W, d))
         got = _run(q, k, v, cu, ids, W, mode, "bf16")
         want = orc.prefill(q, k, v, cu, ids, W, mode)
-        assert_close(got, want, "bf16", "many docs %d W=%d" % (ndocs, W))
+        assert_close(got, want, "bf16", "many docs %d W=%d d=%d" % (ndocs, W, d))
 
 
 def test_prefill_deterministic():

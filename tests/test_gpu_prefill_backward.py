@@ -149,6 +149,29 @@ def test_backward_window_one(d, dtype):
     assert_grad_close(dv, want, dtype, "dv W=1 d=%d %s" % (d, dtype))
 
 
+@pytest.mark.parametrize("ndocs", [300, 1500])
+@pytest.mark.parametrize("mode", [CAUSAL, BLOCKWISE])
+def test_backward_many_documents(ndocs, mode):
+    """Hundreds of short documents (empty ones among them), more than the
+    forward keeps in LDS at 1500: every row interval ends at a document
+    boundary, so most tiles are split between documents."""
+    require_gpu()
+    rng = si.rng_for(7300 + ndocs + mode)
+    lens = rng.integers(0, 25, size=ndocs)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    hq, hkv, d = 4, 2, 128
+    q, k, v, do = (si.normal(rng, s, "bf16") for s in [(T, hq, d), (T, hkv, d), (T, hkv, d), (T, hq, d)])
+    ids = _ids_for(T, cu, 7400 + ndocs) if mode == BLOCKWISE else None
+    for W in (0, 7):
+        out = _round_out(orc.prefill(q, k, v, cu, ids, W, mode), "bf16")
+        log("backward many docs ndocs=%d T=%d mode=%d W=%d" % (ndocs, T, mode, W))
+        got = _run(q, k, v, out, do, cu, ids, W, mode)
+        want = orc.prefill_backward(q, k, v, do, cu, ids, W, mode)
+        for name, a, b in zip(("dq", "dk", "dv"), got, want):
+            assert_grad_close(a, b, "bf16", "%s many docs %d mode=%d W=%d" % (name, ndocs, mode, W))
+
+
 def test_backward_is_deterministic():
     """Every output element has one writer and a fixed summation order:
     two runs give the same bits."""
