@@ -250,3 +250,32 @@ def test_backward_full_size_sampled(name, rows, keys):
         assert_grad_close(dk[ka], wk, "bf16", "%s dk keys" % name)
         assert_grad_close(dv[ka], wv, "bf16", "%s dv keys" % name)
     _sum_properties(case, dk, dv, do)
+
+
+def test_long_document_forward_and_backward_sampled():
+    """One 65536-token document (window 4096, 8 MHA heads, D = 128): the
+    forward, its log-sum-exp and the backward at a length four times the
+    largest benchmark workload, on sampled rows against the oracle and with
+    the document-sum properties of dk and dv over every key."""
+    require_gpu()
+    rng = si.rng_for(65536)
+    T, h, d, W = 65536, 8, 128, 4096
+    cu = np.array([0, T], np.int32)
+    q, k, v, do = (si.normal(rng, (T, h, d), "bf16") for _ in range(4))
+    qd, kd, vd, dod, cud = dev(q), dev(k), dev(v), dev(do), dev(cu)
+    log("long document forward T=%d" % T)
+    out, lse = api.prefill_lse(qd, kd, vd, cud, None, W, CAUSAL)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 4095, 4096, 4097, 30000, 65534, 65535], np.int32)
+    want_o, want_l = orc.prefill(q, k, v, cu, None, W, CAUSAL, rows=rows, return_lse=True)
+    got_o = as_f64(host(out))[rows]
+    assert np.abs(got_o - want_o).max() <= 2e-2
+    assert np.abs(host(lse).astype(np.float64).T[rows] - want_l).max() <= 1e-2
+    log("long document backward T=%d" % T)
+    dq, dk, dv = api.prefill_backward(qd, kd, vd, out, dod, cud, None, W, CAUSAL, lse=lse)
+    torch.cuda.synchronize()
+    wq, _, _ = orc.prefill_backward(q, k, v, do, cu, None, W, CAUSAL, rows=rows,
+                                    keys=np.array([], np.int32))
+    assert_grad_close(host(dq)[rows], wq, "bf16", "long document dq rows")
+    case = si.PrefillCase("long", cu, h, h, d, W, CAUSAL, seed=0)
+    _sum_properties(case, host(dk), host(dv), do)
