@@ -160,7 +160,7 @@ SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
  * (float32 [hq, total_tokens], 4-byte aligned), or NULL, in which case the
  * backward recomputes it with one more pass over the keys.  Every output element is written exactly once,
  * without atomics: the result is deterministic.
- *   d: 64, 128, 256, 320 or 512 for bf16; 64, 128, 256 or 320 for fp32.
+ *   d: 64, 128, 256, 320 or 512.
  *   workspace: device memory of at least
  *   swa_prefill_backward_workspace_bytes(total_tokens, hq) bytes, 16-byte
  *   aligned, owned by the caller, contents on entry ignored (per-row

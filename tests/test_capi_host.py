@@ -124,7 +124,7 @@ def _backward(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d=96), _lib.SWA_EUNSUPPORTED),
-    (dict(d=512, dtype=1), _lib.SWA_EUNSUPPORTED),
+    (dict(d=384), _lib.SWA_EUNSUPPORTED),
     (dict(dtype=7), _lib.SWA_EUNSUPPORTED),
     (dict(mode=2), _lib.SWA_EUNSUPPORTED),
     (dict(hq=3, hkv=2), _lib.SWA_EINVAL),
@@ -152,7 +152,7 @@ def test_prefill_backward_sizes():
     assert _backward(T=0, q=None, dq=None, ws=None) == _lib.SWA_OK
     for d in (64, 128, 256, 320, 512):
         assert _backward(d=d, wsb=0) == _lib.SWA_EWORKSPACE
-    for d in (64, 128, 256, 320):
+    for d in (64, 128, 256, 320, 512):
         assert _backward(d=d, dtype=1, wsb=0) == _lib.SWA_EWORKSPACE
     L = _lib.lib()
     for T, hq in ((1, 1), (4096, 32), (16384, 16)):

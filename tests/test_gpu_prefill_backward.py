@@ -78,7 +78,7 @@ def _ids_for(T, cu, seed):
 
 
 def _supported(d, dtype):
-    return dtype == "bf16" or d <= 320
+    return True
 
 
 CASES = [(d, dtype, mode) for d in (64, 128, 256, 320, 512) for dtype in ("bf16", "f32")
@@ -130,8 +130,6 @@ def test_backward_window_one(d, dtype):
     """W = 1: every row attends only itself with weight 1, so dq = dk = 0
     and dv[j] = the sum of dout[j] over the group's heads."""
     require_gpu()
-    if not _supported(d, dtype):
-        pytest.skip("fp32 backward takes d <= 320")
     rng = si.rng_for(40 + d)
     T, hkv, g = 333, 2, 2
     cu = np.array([0, 100, 101, T], np.int32)
@@ -140,10 +138,10 @@ def test_backward_window_one(d, dtype):
     log("backward W=1 d=%d %s" % (d, dtype))
     dq, dk, dv = _run(q, k, v, out, do, cu, None, 1, CAUSAL)
     # dS = P (dP - delta) with dP from the matrix cores and delta from a
-    # vector sum: their fp32 rounding differs by ~1e-6 |dP|, which leaves
-    # dq, dk of order 1e-6 where the exact value is 0 (a wrongly admitted
-    # key would give O(0.1))
-    floor = 1e-5
+    # vector sum: their fp32 rounding differs by ~1e-6 |dP| (|dP| grows as
+    # sqrt(D)), which leaves dq, dk of order 1e-6 .. 1e-5 where the exact
+    # value is 0 (a wrongly admitted key would give O(0.1))
+    floor = 1e-5 * np.sqrt(d / 128.0)
     assert np.abs(as_f64(dq)).max() <= floor and np.abs(as_f64(dk)).max() <= floor
     want = as_f64(do).reshape(T, hkv, g, d).sum(axis=2)
     assert_grad_close(dv, want, dtype, "dv W=1 d=%d %s" % (d, dtype))
