@@ -44,11 +44,11 @@ namespace swa {
 
 // Tile geometry: BN rows (keys in the dq kernel, query rows in the dk/dv
 // kernel) of D elements per LDS tile, at most 32 KB per tile.
-template <int D, typename T, int BN_ = 0>
+template <int D, typename T, int BN_ = 0, int NW_ = 4>
 struct BwGeom {
   using TR = PfTraits<T>;
   static constexpr bool kF32 = std::is_same<T, float>::value;
-  static constexpr int NT = 256;                 // 4 waves
+  static constexpr int NT = 64 * NW_;            // NW_ waves (4 unless given)
   static constexpr int CPR = D / TR::VEC;        // 16-byte chunks per row
   static constexpr int FRAG = kF32 ? 16 : 32;    // rows per P fragment step
   static constexpr int RAW = 32768 / (D * (int)sizeof(T));
@@ -147,14 +147,14 @@ __device__ __forceinline__ i32x4 bw_rows_rsrc(const T* base, int r0, int h, int 
 // K / V fragments from LDS and Q / dout fragments from registers (as the
 // forward's S^T); dq^T += K^T dS^T takes K^T by transposed LDS reads and
 // dS^T from the accumulator layout (as the forward's O^T += V^T P^T).
-template <int D, typename T, int MB>
-__global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dq_kernel(
+template <int D, typename T, int MB, int BN_>
+__global__ __launch_bounds__(256, (BN_ > 0 ? 2 : bw_blocks_per_cu<D, T>())) void bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ o, const T* __restrict__ dout, const int32_t* __restrict__ lo_a,
     const int32_t* __restrict__ hi_a, const float* __restrict__ lse_in, int Ttot, int hq,
     int hkv, float c_scale, float scale, int ntiles, int nwork, int per_xcd, T* __restrict__ dq,
     float* __restrict__ lse_out, float* __restrict__ delta_out) {
-  using G = BwGeom<D, T>;
+  using G = BwGeom<D, T, BN_>;
   using TR = typename G::TR;
   constexpr bool kF32 = G::kF32;
   constexpr int BN = G::BN, TB = G::TILE_BYTES, WR = 16 * MB, BM = 4 * WR;
@@ -500,19 +500,19 @@ __global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dq_kernel
 // and hi.  KB = 2 halves the LDS reads per product; DS = 2 halves the
 // registers a wave needs at large head sizes, at the cost of a second
 // barrier per tile.
-template <int D, typename T, int DS, int KB, int BQ_>
-__global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dkdv_kernel(
+template <int D, typename T, int DS, int KB, int BQ_, int NW>
+__global__ __launch_bounds__(NW * 64, (NW == 4 ? bw_blocks_per_cu<D, T>() : 1)) void bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dlt,
     const int32_t* __restrict__ lo_a, const int32_t* __restrict__ hi_a, int Ttot, int hq,
     int hkv, float c_scale, float scale, int nktiles, int nwork, int per_xcd,
     T* __restrict__ dk, T* __restrict__ dv) {
-  using G = BwGeom<D, T, BQ_>;
+  using G = BwGeom<D, T, BQ_, NW>;
   using TR = typename G::TR;
   constexpr bool kF32 = G::kF32;
   constexpr int BQ = G::BN, TB = G::TILE_BYTES, NRB = BQ / 16;
   constexpr int KW = 16 * KB;              // keys per wave
-  constexpr int BK = KW * 4 / DS;          // keys per work-group
+  constexpr int BK = KW * NW / DS;         // keys per work-group
   constexpr int QH = G::QREG / DS;         // S / dP fragments of this wave's d range
   constexpr int NDT = D / 16 / DS;         // 16-wide d blocks of this wave's accumulators
   constexpr int CPW = G::CPR / DS;         // 16-byte chunks of this wave's d range
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(256, (bw_blocks_per_cu<D, T>())) void bwd_dkdv_kern
   static_assert(BQ * 4 <= 1024, "tile metadata fits its slot");
   constexpr int STAGE = 2 * TB + META;
   constexpr int XW = KB * 2 * NRB * 64;    // floatx4 partials per wave
-  constexpr int XCH = DS == 2 ? 4 * XW * 16 : 16;
+  constexpr int XCH = DS == 2 ? NW * XW * 16 : 16;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[2][STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char xch[XCH];
 

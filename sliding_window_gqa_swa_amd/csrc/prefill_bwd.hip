@@ -26,17 +26,21 @@ constexpr int dq_mb() {
 template <int D, typename T>
 struct DkdvCfg {
   static constexpr bool F = std::is_same<T, float>::value;
-  static constexpr int DS = F ? (D >= 256 ? 2 : 1) : (D >= 512 ? 2 : 1);
+  static constexpr int DS = F ? (D >= 256 ? 2 : 1) : (D >= 512 || D == 256 ? 2 : 1);
   // (two key blocks per wave halve the LDS reads per product but cost the
   // second wave per SIMD: 241 vs 197 us at D = 128, measured)
   static constexpr int KB = 1;
-  static constexpr int BQ = 0;  // the default tile
+  static constexpr int BQ = (!F && D == 256) ? 32 : 0;  // 0: the default tile
+  static constexpr int NW = (!F && D == 256) ? 8 : 4;   // waves per work-group
 };
 
 template <int D, typename T>
 int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
   constexpr int MB = dq_mb<D, T>();
   constexpr int BM = 64 * MB;
+  // dq key tile: 32 keys at bf16 D = 256 (a 64 KB ring: two work-groups
+  // per CU), else the default
+  constexpr int DQBN = (!std::is_same<T, float>::value && D == 256) ? 32 : 0;
   const int T_ = a.total;
   hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((T_ + 255) / 256)), dim3(256), 0, a.stream,
                      a.cu, a.num_docs, a.ids, a.window, a.mode, T_, w.lo, w.hi);
@@ -46,19 +50,20 @@ int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
     const long long nwork = (long long)ntiles * a.hq;
     const long long per_xcd = (nwork + 7) / 8;
     if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, T, MB>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, T, MB, DQBN>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.out,
                        (const T*)a.dout, w.lo, w.hi, a.lse, T_, a.hq, a.hkv, c, a.scale, ntiles,
                        (int)nwork, (int)per_xcd, (T*)a.dq, w.lse, w.delta);
   }
   {
     using C = DkdvCfg<D, T>;
-    constexpr int BK = 16 * C::KB * 4 / C::DS;  // keys per work-group
+    constexpr int BK = 16 * C::KB * C::NW / C::DS;  // keys per work-group
     const int nkt = (T_ + BK - 1) / BK;
     const long long nwork = (long long)nkt * a.hkv;
     const long long per_xcd = (nwork + 7) / 8;
     if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, C::DS, C::KB, C::BQ>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, C::DS, C::KB, C::BQ, C::NW>), dim3((unsigned)(8 * per_xcd)),
+                       dim3(64 * C::NW), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
                        w.lse, w.delta, w.lo, w.hi, T_, a.hq, a.hkv, c, a.scale, nkt, (int)nwork,
                        (int)per_xcd, (T*)a.dk, (T*)a.dv);
