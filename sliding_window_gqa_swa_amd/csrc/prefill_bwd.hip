@@ -30,7 +30,7 @@ struct DkdvCfg {
   // (two key blocks per wave halve the LDS reads per product but cost the
   // second wave per SIMD: 241 vs 197 us at D = 128, measured)
   static constexpr int KB = 1;
-  static constexpr int BQ = (!F && D == 256) ? 32 : 0;  // 0: the default tile
+  static constexpr int BQ = (!F && D <= 256) ? 32 : 0;  // 0: the default tile
   static constexpr int NW = (!F && D == 256) ? 8 : 4;   // waves per work-group
 };
 
@@ -40,7 +40,7 @@ int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
   constexpr int BM = 64 * MB;
   // dq key tile: 32 keys at bf16 D = 256 (a 64 KB ring: two work-groups
   // per CU), else the default
-  constexpr int DQBN = (!std::is_same<T, float>::value && D == 256) ? 32 : 0;
+  constexpr int DQBN = (!std::is_same<T, float>::value && D <= 256) ? 32 : 0;
   const int T_ = a.total;
   hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((T_ + 255) / 256)), dim3(256), 0, a.stream,
                      a.cu, a.num_docs, a.ids, a.window, a.mode, T_, w.lo, w.hi);
