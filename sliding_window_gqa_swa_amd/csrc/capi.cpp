@@ -119,7 +119,7 @@ int prefill_impl(const void* q, const void* k, const void* v, const int32_t* cu_
       (int64_t)total_k * hkv * d >= (int64_t)1 << 62)
     return SWA_EUNSUPPORTED;
   if (!(scale > 0.f)) scale = 1.0f / __builtin_sqrtf((float)d);
-  swa::PrefillArgs a;
+  swa::PrefillArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -203,7 +203,7 @@ SWA_API int swa_prefill_backward(const void* q, const void* k, const void* v, co
       workspace_bytes < swa::bwd_workspace_bytes(total_tokens, hq))
     return SWA_EWORKSPACE;
   if (!(scale > 0.f)) scale = 1.0f / __builtin_sqrtf((float)d);
-  swa::PrefillBwdArgs a;
+  swa::PrefillBwdArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
