@@ -385,6 +385,18 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
 
 
 # ------------------------------------------------------------ CPU baseline
+def cpu_model_name():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(budget_s=15.0):
     """fp64 oracle on a bounded, seeded sample of the headline workload."""
     from oracle import oracle as orc
@@ -407,6 +419,7 @@ def cpu_baseline(budget_s=15.0):
     dt = time.perf_counter() - t0
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model_name(),
         "sample": "%d query rows x %d heads of %s (%.2f passes over its %d rows, seeded "
                   "random order), fp64, %.1f s" % (done, c.hq, HEADLINE, done / c.T, c.T, dt),
     }
