@@ -8,4 +8,6 @@ The work runs in hand-written HIP kernels behind the C ABI of ``libswa.so``
 """
 from . import api  # noqa: F401
 from .api import (BLOCKWISE, CAUSAL, cache_append, cache_compact, cache_roll,  # noqa: F401
-                  decode, decode_workspace, decode_workspace_bytes, prefill)
+                  decode, decode_step, decode_workspace, decode_workspace_bytes, prefill,
+                  prefill_backward, prefill_backward_workspace_bytes, prefill_chunk,
+                  prefill_lse)
