@@ -384,6 +384,23 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
     }
 
 
+def peak_clock_mhz(device=0):
+    """The GPU's peak shader clock as the HIP runtime of libswa reports it
+    (hipDeviceGetAttribute with hipDeviceAttributeClockRate, in kHz), or
+    None.  The clock under load is lower; kernel traces show it."""
+    import ctypes
+    from sliding_window_gqa_swa_amd import _lib
+    try:
+        fn = _lib.lib().hipDeviceGetAttribute  # resolved through libswa's HIP runtime
+    except AttributeError:
+        return None
+    fn.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    fn.restype = ctypes.c_int
+    v = ctypes.c_int(0)
+    kClockRate = 5  # position of hipDeviceAttributeClockRate in hipDeviceAttribute_t
+    return v.value / 1000.0 if fn(ctypes.byref(v), kClockRate, device) == 0 else None
+
+
 # ------------------------------------------------------------ CPU baseline
 def cpu_model_name():
     """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
@@ -653,7 +670,8 @@ def main():
                    "hq": 32, "hkv": 32, "head_dim": 128, "window": 1024, "mask": "causal",
                    "useful_flop_per_step": head["useful_flop"], "input_sets": head["input_sets"]},
         "roofline": roof, "cpu_baseline": cpu,
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "arch": props.gcnArchName,
+                   "cus": props.multi_processor_count, "peak_clock_mhz": peak_clock_mhz()},
         "workloads": workloads,
     }
     print(json.dumps(line), flush=True)
