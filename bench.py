@@ -566,6 +566,9 @@ def main():
     ap.add_argument("--only-decode", action="store_true",
                     help="run the decode workloads only and print their results (for "
                          "counter runs; not the benchmark line)")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="run the 4x1024 backward only and print its result (for counter "
+                         "runs; not the benchmark line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy 4 times (known bytes, for "
                          "scaling HBM counters)")
@@ -612,6 +615,12 @@ def main():
                 name, res[name]["decode_us"], res[name]["decode_gbs"],
                 res[name]["us_per_step_fused"]), file=sys.stderr, flush=True)
         print(json.dumps({"workloads": res}), flush=True)
+        return
+    if args.only_backward:
+        b = bench_prefill_backward(HEADLINE, 20, 2, torch, api, None)
+        print("%s: %.3f ms, %.1f TFLOP/s" % (b["workload"], b["ms_per_call"], b["tflops"]),
+              file=sys.stderr, flush=True)
+        print(json.dumps({"workloads": {b["workload"]: b}}), flush=True)
         return
     head = bench_prefill(HEADLINE, args.steps, args.warmup, torch, api)
     print("headline %s: %.3f ms, %.1f TFLOP/s" % (HEADLINE, head["ms_per_call"], head["tflops"]),
