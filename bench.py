@@ -3,21 +3,22 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Headline (`value`): useful (unmasked) TFLOP/s of swa_prefill on 4 packed
-documents x 1024 tokens, Hq = Hkv = 32, D = 128, W = 1024, causal, bf16.  A
-step is one swa_prefill over one batch; inputs rotate over several resident
-copies so the 256 MB Infinity Cache cannot hold them.  The other prefill
-workloads and the two ring-decode workloads (append + decode per step, the
-roll every 64 steps) are measured in the same run and reported under
-"workloads".  Times come from HIP events on the stream the kernels run on,
-taken on settled GPU clocks: the default warm-up (1000 steps, about 60 ms
-of the headline kernel) and at least 60 ms of untimed work before every
-other timed region (an idle GPU runs the first launches at lower clocks).
+Headline (`value`): useful (unmasked) TFLOP/s of swa_prefill on the largest
+workload, one 16384-token document, Hq = 16, Hkv = 8 (GQA), D = 512,
+W = 4096, causal, bf16 ([SDPA] Benchmark: the Gemma-4 full-attention row
+"16K, 1 doc, 4K window").  A step is one swa_prefill over one batch; inputs
+rotate over resident copies larger than the 256 MB Infinity Cache.  The
+other prefill workloads, the backward and the two ring-decode workloads are
+measured in the same run and reported under "workloads", each with its own
+roofline block.  Times come from HIP events on the stream the kernels run
+on, taken on settled GPU clocks: every timed region, the headline's
+included, follows the given warm-up and at least 60 ms of untimed work (an
+idle GPU runs the first launches at lower clocks).
 
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the headline
-workload on this host's cores.  `roofline.traffic` is read from the counter
-summary under profiles/ only while the kernel sources still hash to the
-value recorded there.
+workload on this host's cores.  A workload's `roofline.traffic` is read from
+the counter summary under profiles/ only while its kernel sources still
+hash to the value recorded there.
 """
 import argparse
 import hashlib
@@ -36,11 +37,25 @@ import swa_inputs as si  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0       # HBM3E
-HEADLINE = "prefill_4x1024_mha_d128"
+HEADLINE = "prefill_16k_gqa_d512"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {
-    "prefill_fwd_kernel": ["prefill_kernel.h", "prefill_launch.h", "prefill_d128.hip"],
-    "decode_split_kernel": ["decode.hip"],
+# the kernel each workload's roofline is about, and the sources it is built from
+_PF = ["prefill_kernel.h", "prefill_launch.h"]
+WORKLOAD_KERNELS = {
+    "prefill_16k_gqa_d512": ("prefill_fwd_kernel", "prefill_fwd_kernel<512, bf16>",
+                             _PF + ["prefill_d512.hip"]),
+    "prefill_4x1024_mha_d128": ("prefill_fwd_kernel", "prefill_fwd_kernel<128, bf16>",
+                                _PF + ["prefill_d128.hip"]),
+    "prefill_16k_mha_d128_w4k": ("prefill_fwd_kernel", "prefill_fwd_kernel<128, bf16>",
+                                 _PF + ["prefill_d128.hip"]),
+    "prefill_vlm_4096_d256": ("prefill_fwd_kernel", "prefill_fwd_kernel<256, bf16>",
+                              _PF + ["prefill_d256.hip"]),
+    "prefill_4x1024_gqa_d320": ("prefill_fwd_kernel", "prefill_fwd_kernel<384 (320 in memory), bf16>",
+                                _PF + ["prefill_d320.hip"]),
+    "decode_b64_d256": ("decode_split_kernel", "decode_split_kernel<256, bf16> (decode alone)",
+                        ["decode.hip"]),
+    "decode_single_d256": ("decode_split_kernel", "decode_split_kernel<256, bf16> (decode alone)",
+                           ["decode.hip"]),
 }
 
 
@@ -86,25 +101,35 @@ def decode_valid_rows(pos, lo, W):
     return pos - low + 1
 
 
-def sources_hash(kernel: str) -> str:
+def sources_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
+    for f in WORKLOAD_KERNELS[workload][2]:
         with open(os.path.join(ROOT, "sliding_window_gqa_swa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def read_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    or None if absent or taken on different kernel sources."""
+def read_traffic(workload: str):
+    """HBM bytes per launch of the workload's kernel from the committed
+    rocprofv3 counter summary, or None if absent or taken on different
+    kernel sources."""
     try:
         with open(TRAFFIC_FILE) as fh:
-            rec = json.load(fh)[kernel]
+            rec = json.load(fh)[workload]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("sources_sha256") != sources_hash(kernel):
+    if rec.get("sources_sha256") != sources_hash(workload):
         return None
     return rec.get("bytes_per_launch")
+
+
+def roofline(workload: str, achieved: float, bound: str) -> dict:
+    """Roofline block of one workload's dominant kernel: achieved
+    algorithmic rate against the MI355X peak of its bound."""
+    peak, unit = (PEAK_BF16_TFLOPS, "TFLOP/s") if bound == "mfma" else (PEAK_HBM_GBS, "GB/s")
+    return {"bound": bound, "kernel": WORKLOAD_KERNELS[workload][1], "achieved": achieved,
+            "peak": peak, "unit": unit, "frac": achieved / peak,
+            "traffic": read_traffic(workload)}
 
 
 # ------------------------------------------------------------ GPU timing
@@ -177,14 +202,16 @@ def bench_prefill(name, steps, warmup, torch, api, nsets=None, settle_ms=0.0):
     # warm: one input set every call (K/V and Q stay in the Infinity Cache)
     warm_ms = time_loop(lambda i: step(0), steps, warmup, torch, settle_ms)
     fl = useful_flops(c)
+    tflops = fl / (ms * 1e-3) / 1e12
     return {
         "workload": name, "T": c.T, "docs": int(c.cu_seqlens.size - 1), "hq": c.hq,
         "hkv": c.hkv, "d": c.d, "window": c.window,
         "mask": "blockwise" if c.mode == si.BLOCKWISE else "causal",
-        "useful_flop": fl, "ms_per_call": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+        "useful_flop": fl, "ms_per_call": ms, "tflops": tflops,
         "ms_per_call_warm": warm_ms, "tflops_warm": fl / (warm_ms * 1e-3) / 1e12,
-        "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "input_sets": nsets,
+        "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "input_sets": nsets, "settle_ms": settle_ms,
+        "roofline": roofline(name, tflops, "mfma"),
     }
 
 
@@ -324,6 +351,19 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
         api.decode(q, kr, vr, meta, W, out=outs[i % layers], workspace=ws)
 
     dec_ms = time_loop(dstep, reps * layers, warmup * layers, torch, SETTLE_MS)
+    # cold: copies of the final ring state, as many as exceed 512 MB (twice
+    # the 256 MB Infinity Cache), so that every decode reads its rings from HBM
+    set_bytes = rings[0][0].numel() * rings[0][0].element_size() * 2
+    ncold = max(layers, int(np.ceil(512e6 / set_bytes)))
+    cold = [(rings[0][0].clone(), rings[0][1].clone(), rings[0][2].clone())
+            for _ in range(ncold)]
+
+    def cstep(i):
+        kr, vr, meta = cold[i % ncold]
+        api.decode(q, kr, vr, meta, W, out=outs[0], workspace=ws)
+
+    cold_ms = time_loop(cstep, max(reps * layers, ncold), ncold, torch, SETTLE_MS)
+    del cold
     # warm: the same ring set every call
     warm_ms = time_loop(lambda i: api.decode(q, rings[0][0], rings[0][1], rings[0][2], W,
                                              out=outs[0], workspace=ws), reps, warmup, torch,
@@ -366,21 +406,20 @@ def bench_decode(name, torch, api, layers=4, warmup=3, reps=20):
     e1.record()
     torch.cuda.synchronize()
     graph_us = e0.elapsed_time(e1) * 1e3 / (len(timed) * layers)
-    pos = c.prompt_lens.astype(np.int64) - 1 + c.pre_appends + nsteps
-    valid = decode_valid_rows(pos, c.left_pad.astype(np.int64), W)
-    es = 2
-    alg_bytes = int(valid.sum()) * hkv * d * es * 2 + 2 * B * hq * d * es + B * 16
-    scanned = B * hkv * R * d * es * 2
+    alg_bytes = decode_alg_bytes(c, nsteps)
+    scanned = B * hkv * R * d * 2 * 2
+    gbs = alg_bytes / (cold_ms * 1e-3) / 1e9
     return {
         "workload": name, "batch": B, "hq": hq, "hkv": hkv, "d": d, "window": W,
         "ring_rows": R, "steps": len(timed), "layers_rotated": layers,
         "us_per_step_append_decode_roll": step_us, "rolls_in_run": sum(
             1 for t in range(len(timed)) if (c.pre_appends + t) > 0 and (c.pre_appends + t) % A == 0),
-        "decode_us": dec_ms * 1e3, "decode_warm_us": warm_ms * 1e3,
+        "decode_us": cold_ms * 1e3, "decode_cold_ring_sets": ncold,
+        "decode_us_4_layers": dec_ms * 1e3, "decode_warm_us": warm_ms * 1e3,
         "us_per_step_fused": fused_us, "us_per_step_fused_graph": graph_us,
         "algorithmic_bytes": alg_bytes, "full_ring_bytes": scanned,
-        "decode_gbs": alg_bytes / (dec_ms * 1e-3) / 1e9,
-        "frac_of_hbm_peak": alg_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "decode_gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS,
+        "roofline": roofline(name, gbs, "hbm"),
     }
 
 
@@ -442,11 +481,32 @@ def cpu_baseline(budget_s=15.0):
     }
 
 
-def record_traffic(fetch_dir, write_dir, kernel="prefill_fwd_kernel", workload=HEADLINE):
-    """Write profiles/traffic.json from two rocprofv3 --pmc runs of
-    `bench.py --only-headline --copy-calibration` (FETCH_SIZE, then
-    WRITE_SIZE; KiB per dispatch).  Each counter is scaled by what it reads
-    for the 512 MiB device copy of the same run (known bytes)."""
+def decode_alg_bytes(c, nsteps):
+    """Algorithmic bytes of one decode of the workload's batch at its state
+    after `nsteps` timed steps: K and V of the valid rows, q, out, meta."""
+    pos = c.prompt_lens.astype(np.int64) - 1 + c.pre_appends + nsteps
+    valid = decode_valid_rows(pos, c.left_pad.astype(np.int64), c.window)
+    es = 2
+    return int(valid.sum()) * c.hkv * c.d * es * 2 + 2 * c.batch * c.hq * c.d * es + c.batch * 16
+
+
+def _kernel_matches(workload, name):
+    """Is the dispatched kernel `name` (mangled) the one whose traffic the
+    workload's roofline reports (bf16, plain variant)?"""
+    import re
+    if workload.startswith("prefill"):
+        m = re.search(r"prefill_fwd_kernelILi(\d+)EDF16b.*?ELb(\d)ELb(\d)ELi(\d+)E", name)
+        return m is not None and m.group(3) == "0"
+    m = re.search(r"decode_split_kernelILi(\d+)EDF16bLi(\d+)ELb(\d)E", name)
+    return m is not None and m.group(3) == "0"
+
+
+def record_traffic(workload, fetch_dir, write_dir):
+    """Add the workload's record to profiles/traffic.json from two rocprofv3
+    --pmc runs of `bench.py --only WORKLOAD --copy-calibration`
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled
+    by what it reads for the 512 MiB device copy of the same run (known
+    bytes)."""
     import csv
     import glob
 
@@ -457,7 +517,7 @@ def record_traffic(fetch_dir, write_dir, kernel="prefill_fwd_kernel", workload=H
                 if r["Counter_Name"] != counter:
                     continue
                 key = (r["Dispatch_Id"], r["Kernel_Name"])
-                tgt = vals if kernel in r["Kernel_Name"] else (
+                tgt = vals if _kernel_matches(workload, r["Kernel_Name"]) else (
                     calib if "copyBuffer" in r["Kernel_Name"] else None)
                 if tgt is not None:
                     tgt[key] = tgt.get(key, 0.0) + float(r["Counter_Value"])
@@ -469,13 +529,17 @@ def record_traffic(fetch_dir, write_dir, kernel="prefill_fwd_kernel", workload=H
         raise SystemExit("counter files lack the kernel or the copy calibration")
     copy_kib = 512 * 1024.0
     fs, ws = copy_kib / fcal, copy_kib / wcal
-    c = si.PREFILL_WORKLOADS[workload]()
-    q, k, v = c.tensors("bf16")
-    alg = q.nbytes + k.nbytes + v.nbytes + q.nbytes  # q, k, v read once; out (q-sized) written once
+    if workload in si.PREFILL_WORKLOADS:
+        c = si.PREFILL_WORKLOADS[workload]()
+        q, k, v = c.tensors("bf16")
+        alg = q.nbytes + k.nbytes + v.nbytes + q.nbytes  # q, k, v read once; out written once
+    else:
+        c = si.DECODE_WORKLOADS[workload]()
+        alg = decode_alg_bytes(c, max(c.steps, 32))
     fb = float(np.mean(fetch)) * 1024 * fs
     wb = float(np.mean(write)) * 1024 * ws
     rec = {
-        "workload": workload, "kernel": kernel,
+        "workload": workload, "kernel": WORKLOAD_KERNELS[workload][1],
         "fetch_kib_raw": float(np.mean(fetch)), "write_kib_raw": float(np.mean(write)),
         "fetch_kib_min_max": [float(np.min(fetch)), float(np.max(fetch))],
         "dispatches": [len(fetch), len(write)],
@@ -483,16 +547,18 @@ def record_traffic(fetch_dir, write_dir, kernel="prefill_fwd_kernel", workload=H
         "fetch_scale": fs, "write_scale": ws,
         "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
         "bytes_per_launch": int(fb + wb), "algorithmic_bytes_per_launch": int(alg),
-        "sources_sha256": sources_hash(kernel),
+        "traffic_over_algorithmic": (fb + wb) / alg,
+        "sources_sha256": sources_hash(workload),
     }
     try:
         with open(TRAFFIC_FILE) as fh:
             allrec = json.load(fh)
     except (OSError, ValueError):
         allrec = {}
-    allrec[kernel] = rec
+    allrec = {k2: v2 for k2, v2 in allrec.items() if k2 in WORKLOAD_KERNELS}
+    allrec[workload] = rec
     with open(TRAFFIC_FILE, "w") as fh:
-        json.dump(allrec, fh, indent=2)
+        json.dump(allrec, fh, indent=2, sort_keys=True)
         fh.write("\n")
     print(json.dumps(rec, indent=2))
 
@@ -558,23 +624,21 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # (the default warm-up, about 60 ms of the headline prefill, brings the
-    # GPU to its settled clocks before the timed steps)
-    ap.add_argument("--warmup", type=int, default=1000)
+    # (after the warm-up, every timed region, the headline's included, also
+    # waits for 60 ms of untimed work: settled clocks)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only-headline", action="store_true")
-    ap.add_argument("--only-decode", action="store_true",
-                    help="run the decode workloads only and print their results (for "
-                         "counter runs; not the benchmark line)")
-    ap.add_argument("--only-backward", action="store_true",
-                    help="run the 4x1024 backward only and print its result (for counter "
+    ap.add_argument("--only", metavar="WORKLOAD",
+                    help="run one workload (a prefill or decode workload, or a prefill "
+                         "workload name + '_backward') and print its result (for counter "
                          "runs; not the benchmark line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy 4 times (known bytes, for "
                          "scaling HBM counters)")
-    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/traffic.json from two rocprofv3 --pmc output "
-                         "directories (FETCH_SIZE, WRITE_SIZE) and exit (no GPU needed)")
+    ap.add_argument("--record-traffic", nargs=3, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
+                    help="add the workload's record to profiles/traffic.json from two "
+                         "rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) of "
+                         "`--only WORKLOAD --copy-calibration` and exit (no GPU needed)")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print a per-kernel table from a rocprofv3 --kernel-trace database "
                          "and exit (no GPU needed)")
@@ -586,8 +650,9 @@ def main():
         record_traffic(*args.record_traffic)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this implementation has no multi-GPU path "
-              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only: every GPU box here has one GPU and this "
+              "implementation has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -607,78 +672,86 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if args.only_decode:
-        res = {}
-        for name in ("decode_b64_d256", "decode_single_d256"):
-            res[name] = bench_decode(name, torch, api)
-            print("%s: decode %.2f us, %.0f GB/s; fused step %.2f us" % (
-                name, res[name]["decode_us"], res[name]["decode_gbs"],
-                res[name]["us_per_step_fused"]), file=sys.stderr, flush=True)
-        print(json.dumps({"workloads": res}), flush=True)
-        return
-    if args.only_backward:
-        b = bench_prefill_backward(HEADLINE, 20, 2, torch, api, None)
-        print("%s: %.3f ms, %.1f TFLOP/s" % (b["workload"], b["ms_per_call"], b["tflops"]),
-              file=sys.stderr, flush=True)
-        print(json.dumps({"workloads": {b["workload"]: b}}), flush=True)
-        return
-    head = bench_prefill(HEADLINE, args.steps, args.warmup, torch, api)
-    print("headline %s: %.3f ms, %.1f TFLOP/s" % (HEADLINE, head["ms_per_call"], head["tflops"]),
-          file=sys.stderr, flush=True)
-    workloads = {HEADLINE: head}
-    if not args.only_headline:
-        for name in ("prefill_16k_gqa_d512", "prefill_vlm_4096_d256", "prefill_4x1024_gqa_d320",
-                     "prefill_16k_mha_d128_w4k"):
-            workloads[name] = bench_prefill(name, max(5, args.steps // 5), 3, torch, api,
-                                            settle_ms=SETTLE_MS)
-            print("%s: %.3f ms, %.1f TFLOP/s" % (name, workloads[name]["ms_per_call"],
-                                                 workloads[name]["tflops"]), file=sys.stderr,
-                  flush=True)
-        ch = bench_prefill_chunked("prefill_16k_gqa_d512", 8, 5, 2, torch, api)
-        workloads[ch["workload"]] = ch
-        print("%s: %.3f ms, %.1f TFLOP/s" % (ch["workload"], ch["ms_per_prompt"], ch["tflops"]),
-              file=sys.stderr, flush=True)
-        # ([SDPA] Benchmark: forward + backward on H100 with the explicit-mask
-        # SDPA path: 612 ms for the 16K, window-4K, 16/8-head, D = 512 shape
-        # and 50 ms for the 16K, window-4K, 32-head, D = 128 shape)
-        for name, st, pages in (("prefill_4x1024_mha_d128", 20, None),
-                                ("prefill_vlm_4096_d256", 20, None),
-                                ("prefill_16k_gqa_d512", 3, 612.0),
-                                ("prefill_16k_mha_d128_w4k", 5, 50.0)):
-            b = bench_prefill_backward(name, st, 2, torch, api, pages)
-            workloads[b["workload"]] = b
-            print("%s: %.3f ms, %.1f TFLOP/s (recomputing lse %.3f ms; forward + backward %.3f ms)" % (
-                b["workload"], b["ms_per_call"], b["tflops"], b["ms_per_call_recomputing_lse"],
-                b["ms_forward_plus_backward"]), file=sys.stderr, flush=True)
-        for name in ("decode_b64_d256", "decode_single_d256"):
-            workloads[name] = bench_decode(name, torch, api)
-            print("%s: %.2f us/step, fused %.2f us/step (graph %.2f), decode %.2f us, %.0f GB/s" % (
-                name, workloads[name]["us_per_step_append_decode_roll"],
-                workloads[name]["us_per_step_fused"], workloads[name]["us_per_step_fused_graph"],
-                workloads[name]["decode_us"], workloads[name]["decode_gbs"]), file=sys.stderr,
-                flush=True)
 
-    traffic = read_traffic("prefill_fwd_kernel", HEADLINE)
-    roof = {
-        "bound": "mfma", "kernel": "prefill_fwd_kernel<128, bf16>",
-        "achieved": head["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-        "frac": head["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic,
-    }
+    def log(r, name):
+        if "decode_us" in r:
+            print("%s: %.2f us/step (roll + append + decode), fused %.2f us/step (graph %.2f), "
+                  "decode %.2f us cold, %.2f us warm, %.0f GB/s" % (
+                      name, r["us_per_step_append_decode_roll"], r["us_per_step_fused"],
+                      r["us_per_step_fused_graph"], r["decode_us"], r["decode_warm_us"],
+                      r["decode_gbs"]), file=sys.stderr, flush=True)
+        elif "ms_per_call_recomputing_lse" in r:
+            print("%s: %.3f ms, %.1f TFLOP/s (recomputing lse %.3f ms; forward + backward "
+                  "%.3f ms)" % (name, r["ms_per_call"], r["tflops"],
+                                r["ms_per_call_recomputing_lse"], r["ms_forward_plus_backward"]),
+                  file=sys.stderr, flush=True)
+        elif "ms_per_prompt" in r:
+            print("%s: %.3f ms, %.1f TFLOP/s" % (name, r["ms_per_prompt"], r["tflops"]),
+                  file=sys.stderr, flush=True)
+        else:
+            print("%s: %.3f ms, %.1f TFLOP/s (%.3f of bf16 peak)" % (
+                name, r["ms_per_call"], r["tflops"], r["frac_of_bf16_peak"]),
+                file=sys.stderr, flush=True)
+
+    # ([SDPA] Benchmark: forward + backward on H100 with the explicit-mask
+    # SDPA path: 612 ms for the 16K, window-4K, 16/8-head, D = 512 shape and
+    # 50 ms for the 16K, window-4K, 32-head, D = 128 shape; context only)
+    pages_fb = {"prefill_16k_gqa_d512": 612.0, "prefill_16k_mha_d128_w4k": 50.0}
+    bwd_steps = {"prefill_16k_gqa_d512": 3, "prefill_16k_mha_d128_w4k": 5}
+    if args.only:
+        name = args.only
+        if name in si.DECODE_WORKLOADS:
+            r = bench_decode(name, torch, api)
+        elif name.endswith("_backward") and name[:-9] in si.PREFILL_WORKLOADS:
+            base = name[:-9]
+            r = bench_prefill_backward(base, bwd_steps.get(base, 20), 2, torch, api,
+                                       pages_fb.get(base))
+        elif name in si.PREFILL_WORKLOADS:
+            r = bench_prefill(name, args.steps, args.warmup, torch, api, settle_ms=SETTLE_MS)
+        else:
+            raise SystemExit("unknown workload %s" % name)
+        log(r, name)
+        print(json.dumps({"workloads": {name: r}}), flush=True)
+        return
+
+    head = bench_prefill(HEADLINE, args.steps, args.warmup, torch, api, settle_ms=SETTLE_MS)
+    log(head, "headline " + HEADLINE)
+    workloads = {HEADLINE: head}
+    for name in ("prefill_4x1024_mha_d128", "prefill_vlm_4096_d256", "prefill_4x1024_gqa_d320",
+                 "prefill_16k_mha_d128_w4k"):
+        steps = max(5, args.steps) if si.PREFILL_WORKLOADS[name]().T <= 4096 else max(5, args.steps // 4)
+        workloads[name] = bench_prefill(name, steps, 3, torch, api, settle_ms=SETTLE_MS)
+        log(workloads[name], name)
+    ch = bench_prefill_chunked("prefill_16k_gqa_d512", 8, 5, 2, torch, api)
+    workloads[ch["workload"]] = ch
+    log(ch, ch["workload"])
+    for name, st in (("prefill_4x1024_mha_d128", 20), ("prefill_vlm_4096_d256", 20),
+                     ("prefill_16k_gqa_d512", 3), ("prefill_16k_mha_d128_w4k", 5)):
+        b = bench_prefill_backward(name, st, 2, torch, api, pages_fb.get(name))
+        workloads[b["workload"]] = b
+        log(b, b["workload"])
+    for name in ("decode_b64_d256", "decode_single_d256"):
+        workloads[name] = bench_decode(name, torch, api)
+        log(workloads[name], name)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline()
         print("cpu baseline: %.4f TFLOP/s on %d threads" % (cpu["value"], cpu["cores"]),
               file=sys.stderr, flush=True)
+    c = si.PREFILL_WORKLOADS[HEADLINE]()
     line = {
-        "metric": "SWA prefill useful TFLOP/s (4x1024-token packed causal prefill, MHA 32 heads, D=128, W=1024)",
+        "metric": "SWA prefill useful TFLOP/s (one 16384-token causal document, GQA 16/8 heads, "
+                  "D=512, W=4096); decode us/step + HBM GB/s under workloads",
         "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": head["ms_per_call"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) rounded to bf16",
-        "config": {"workload": HEADLINE, "docs": 4, "tokens_per_doc": 1024, "total_tokens": 4096,
-                   "hq": 32, "hkv": 32, "head_dim": 128, "window": 1024, "mask": "causal",
-                   "useful_flop_per_step": head["useful_flop"], "input_sets": head["input_sets"]},
-        "roofline": roof, "cpu_baseline": cpu,
+        "config": {"workload": HEADLINE, "docs": 1, "total_tokens": c.T, "hq": c.hq,
+                   "hkv": c.hkv, "head_dim": c.d, "window": c.window, "mask": "causal",
+                   "useful_flop_per_step": head["useful_flop"], "input_sets": head["input_sets"],
+                   "settle_ms_before_timed_steps": SETTLE_MS},
+        "roofline": head["roofline"], "cpu_baseline": cpu,
         "device": {"name": props.name, "arch": props.gcnArchName,
                    "cus": props.multi_processor_count, "peak_clock_mhz": peak_clock_mhz()},
         "workloads": workloads,

@@ -358,20 +358,32 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 
   // The last split block of this (sequence, head block) combines all splits
-  // in a fixed order.  The barrier waits for this block's stores to
-  // complete before the counter moves; the combining block reads with
-  // agent-scope loads (no stale L2 lines).  No L2-wide fence is needed.  The
-  // counter goes back to zero for the next call.
+  // in a fixed order.  Publication, in three steps:
+  //  1. the partials above are agent-scope stores, which write through this
+  //     XCD's L2 to the device coherence point;
+  //  2. every wave waits until its own stores are acknowledged (vmcnt(0):
+  //     __syncthreads() alone orders LDS at work-group scope and leaves
+  //     global stores in flight), then the barrier, so all of the block's
+  //     partials are at the coherence point before thread 0 moves the
+  //     counter (a release at agent scope, without the L2 write-back a
+  //     fence would add: only these write-through stores need publishing);
+  //  3. the block that reads the final count issues its loads after that
+  //     atomic has returned (barrier), as agent-scope loads, which are served
+  //     from the coherence point and never from a stale line of its own L2.
+  // The counter goes back to zero for the next call.
   __shared__ int is_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   uint32_t* cnt = counters + (size_t)b * gridDim.y + blockIdx.y;
   if (threadIdx.x == 0) {
     is_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
               (uint32_t)(splits - 1);
     if constexpr (STEP) {
-      // every block of the sequence has read ring_meta: the last one to get
-      // here stores the new state (the ring row was written by its block
-      // before that block's barrier above)
+      // every block of the sequence has read ring_meta (its loads returned
+      // before any of its work): the last one to get here stores the new
+      // state.  The next launch reads it (and the appended ring row, written
+      // above by one block with plain stores) after the kernel boundary,
+      // which makes every store of this launch visible.
       uint32_t* scnt = counters + (size_t)gridDim.z * gridDim.y + b;
       const uint32_t nblk = (uint32_t)splits * gridDim.y;
       if (__hip_atomic_fetch_add(scnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nblk - 1) {

@@ -166,12 +166,24 @@ def test_decode_single_sequence_position_3000():
 
 
 def test_decode_deterministic_and_position_independent_launch():
-    """Two decodes of one state are bit-identical; the workspace size does
-    not depend on positions (one launch shape for every step)."""
+    """Two decodes of one state are bit-identical; one workspace, sized from
+    the shapes alone, serves ring states at very different positions (the
+    launch never depends on positions), each matching the oracle."""
     require_gpu()
     case = _small_case(256, 2, 64, 64, seed=3, B=4, steps=1)
     run = DecodeRun(case, "bf16")
-    q, out, _ = run.step(0)
+    q, out, seqs = run.step(0)
     out2 = host(api.decode(dev(q), run.k, run.v, run.meta, case.window, workspace=run.ws))
     np.testing.assert_array_equal(out, out2)
-    assert api.decode_workspace_bytes(4, 4, 2, 256, 128) == api.decode_workspace_bytes(4, 4, 2, 256, 128)
+    assert_close(out, run.oracle(q, seqs), "bf16", "near start")
+    # same sizes, positions around 30000 instead of below 256, same workspace
+    far = si.DecodeCase("far", batch=case.batch, hq=case.hq, hkv=case.hkv, d=case.d,
+                        window=case.window, ring_rows=case.ring_rows,
+                        prompt_lens=case.prompt_lens + 30000, left_pad=case.left_pad,
+                        tail_lens=np.full(case.batch, case.window, np.int32), steps=1, seed=5)
+    run_far = DecodeRun(far, "bf16")
+    run_far.ws = run.ws
+    log("decode far positions, shared workspace")
+    q, out, seqs = run_far.step(0)
+    assert host(run_far.meta)[:, 0].min() >= 30000
+    assert_close(out, run_far.oracle(q, seqs), "bf16", "far positions")

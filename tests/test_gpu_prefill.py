@@ -108,7 +108,7 @@ def test_prefill_window_one_is_exact(d, dtype):
     np.testing.assert_array_equal(got, want)
 
 
-@pytest.mark.parametrize("d", [128, 256, 512])
+@pytest.mark.parametrize("d", [128, 256, 320, 512])
 @pytest.mark.parametrize("strength", [40.0, 400.0])
 def test_prefill_needle_marks_window_edge(d, strength):
     """bf16 sharpness check: key j carries a strong needle; query rows that
@@ -141,6 +141,58 @@ def test_prefill_needle_marks_window_edge(d, strength):
     for i in (j - 1, j, j + W - 1, j + W):
         near = np.abs(got[i, 0] - vj).max() < 0.1
         assert near == (j <= i < j + W), (i, np.abs(got[i, 0] - vj).max())
+
+
+def _needle_inputs(d, T, j, seed):
+    """q, k, v (bf16 bits) of one document where key j dominates every row
+    that may see it: rows that admit key j output about v[j], rows that do
+    not output a flat average far from it."""
+    hkv, g = 1, 2
+    rng = si.rng_for(seed)
+    qf = rng.standard_normal((T, hkv * g, d), dtype=np.float32) * 0.1
+    kf = rng.standard_normal((T, hkv, d), dtype=np.float32) * 0.1
+    vf = rng.standard_normal((T, hkv, d), dtype=np.float32)
+    direction = np.ones(d, np.float32) / np.sqrt(d)
+    qf[:, :, :] += 4.0 * direction
+    kf[j, 0, :] = 40.0 * np.sqrt(d / 128.0) * direction
+    return tuple(si.f32_to_bf16_bits(x) for x in (qf, kf, vf))
+
+
+@pytest.mark.parametrize("d", [128, 256, 320, 512])
+def test_prefill_needle_blockwise_image_edges(d):
+    """bf16 sharpness of the vision-language mask on the pipelined kernels
+    ([SPYRE] Correctness: a future key of the same image is allowed, a
+    same-image key older than the window is rejected, text never sees the
+    future).  One document of 512 tokens, W = 64, one image run over tokens
+    300..419 (longer than the window).  Needle at key 380: the earlier image
+    rows 300..379 see it although it lies in their future, text row 299
+    does not; after it, rows see it while i - 380 < 64 (image rows up to
+    419, then text rows 420..443), not at 444.  Needle at key 305: image
+    row 368 (i - j = 63) sees it, image row 369 (exactly W back) does not,
+    image rows 300..304 see it (future, same image)."""
+    require_gpu()
+    T, W = 512, 64
+    ids = np.full(T, -1, np.int32)
+    ids[300:420] = 0
+    cu = np.array([0, T], np.int32)
+    expect = {
+        380: {299: False, 300: True, 350: True, 379: True, 380: True, 419: True, 420: True,
+              443: True, 444: False, 200: False},
+        305: {299: False, 300: True, 304: True, 305: True, 368: True, 369: False, 400: False,
+              419: False},
+    }
+    for j, rows in expect.items():
+        q, k, v = _needle_inputs(d, T, j, seed=11 + j)
+        log("prefill blockwise needle d=%d key=%d" % (d, j))
+        got_bits = _run(q, k, v, cu, ids, W, BLOCKWISE, "bf16")
+        want = orc.prefill(q, k, v, cu, ids, W, BLOCKWISE)
+        assert_close(got_bits, want, "bf16", "blockwise needle %d" % j)
+        got = as_f64(got_bits)
+        vj = as_f64(v)[j, 0]
+        for i, sees in rows.items():
+            for hh in range(2):
+                near = np.abs(got[i, hh] - vj).max() < 0.1
+                assert near == sees, (j, i, hh, np.abs(got[i, hh] - vj).max())
 
 
 def test_prefill_edge_shapes():

@@ -77,12 +77,8 @@ def _ids_for(T, cu, seed):
     return ids
 
 
-def _supported(d, dtype):
-    return True
-
-
 CASES = [(d, dtype, mode) for d in (64, 128, 256, 320, 512) for dtype in ("bf16", "f32")
-         for mode in (CAUSAL, BLOCKWISE) if _supported(d, dtype)]
+         for mode in (CAUSAL, BLOCKWISE)]
 
 
 @pytest.mark.parametrize("d,dtype,mode", CASES)
