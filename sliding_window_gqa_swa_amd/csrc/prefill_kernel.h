@@ -103,8 +103,11 @@ __device__ __forceinline__ int chunk_src(int r, int pc) {
 
 // One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from g land at
 // LDS byte address lds_wave_base + 16 * l (lds_wave_base is wave-uniform).
+// An LDS-destination memory instruction reads M0 and needs one wait state
+// after the scalar write of M0 (the s_nop); without it the load can take
+// the previous M0 and write another load's LDS slots.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(lds_wave_base), "v"(g)
                : "memory");
@@ -131,9 +134,10 @@ __device__ __forceinline__ void wait_vmcnt_units(int k) {
 
 // One 16-byte-per-lane direct-to-LDS buffer load: lane l's 16 bytes at
 // byte offset voff of the buffer land at LDS byte lds_wave_base + 16 * l; a
-// lane whose offset is outside the buffer writes zeros and reads nothing.
+// lane whose offset is outside the buffer writes zeros and reads nothing
+// (M0 wait state as for dma16).
 __device__ __forceinline__ void dma16_buf(i32x4 rsrc, int voff, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_wave_base), "v"(voff), "s"(rsrc)
                : "memory");
@@ -186,16 +190,45 @@ __device__ __forceinline__ void lgkm_wait(short4v& a, short4v& b, short4v& c, sh
 // When a kernel may use more than 256 registers the compiler gives every
 // MFMA builtin an AGPR accumulator; at D = 512 the O^T accumulators alone
 // fill the 256 AGPRs, so the score products are written by hand to keep
-// theirs in VGPRs.  The compiler does not see these as matrix instructions:
-// a VALU read of `acc` must come at least kMfmaDrain wait states after the
-// last product that wrote it (the callers guarantee that), and a product
-// whose C operand is the previous product's result with the same registers
-// is forwarded by the hardware.
-__device__ __forceinline__ void mfma_bf16_vacc(floatx4& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+// theirs in VGPRs.  The compiler does not see these as matrix instructions,
+// so the hazards it would resolve for a builtin are resolved here:
+//  - a VGPR written by a vector ALU instruction may be read by a product
+//    only two wait states later (the compiler may materialise an operand,
+//    e.g. a zero Q fragment or a copy, right before the block): each block
+//    starts with them;
+//  - a VALU read of `acc` must come at least kMfmaDrain wait states after
+//    the last product that wrote it (the callers guarantee that);
+//  - the result registers must not be handed to another value while the
+//    products still write them (the callers keep the results live for a
+//    whole phase of products after the block).
+// A product whose C operand is the previous product's result with the same
+// registers is forwarded by the hardware.
+// One block: the four products of a pair of K fragments (key blocks 0, 1)
+// with the Q fragments of two query blocks (0, 1); c<key block><query block>.
+__device__ __forceinline__ void mfma4_bf16_vacc(floatx4& c00, floatx4& c01, floatx4& c10,
+                                                floatx4& c11, const bf16x8& k0, const bf16x8& k1,
+                                                const bf16x8& q0, const bf16x8& q1) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3"
+      : "+v"(c00), "+v"(c01), "+v"(c10), "+v"(c11)
+      : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
 }
-__device__ __forceinline__ void mfma_bf16_vacc0(floatx4& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+// the same with zero accumulators (the first head-dimension step)
+__device__ __forceinline__ void mfma4_bf16_vacc0(floatx4& c00, floatx4& c01, floatx4& c10,
+                                                 floatx4& c11, const bf16x8& k0, const bf16x8& k1,
+                                                 const bf16x8& q0, const bf16x8& q1) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %6, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %4, %7, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %6, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %5, %7, 0"
+      : "=&v"(c00), "=&v"(c01), "=&v"(c10), "=&v"(c11)
+      : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
 }
 // wait states that cover an 8-pass product's result latency (with margin)
 __device__ __forceinline__ void mfma_drain() {
@@ -610,11 +643,37 @@ void prefill_fwd_kernel(
   // tile (lo_i never decreases with i), computed here from cu_seqlens alone
   // so that the first K/V loads go out together with the Q loads
   int kt0;
+  // Visit order of the key tiles (pipelined loop).  A causal work-group
+  // whose keys are cut by the window visits its n tiles rotated: visit t
+  // reads tile (t + rot) mod n, with rot chosen so that the absolute tile
+  // index of visit t is congruent to t mod n.  Every other such work-group
+  // with the same n (every window-limited query tile of a document has the
+  // same n) then reads the same absolute key tile at the same visit, so the
+  // work-groups running side by side on an XCD stream one window through
+  // its L2 together instead of each its own, shifted, window.  The order
+  // of the keys does not change the result (online softmax).  Work-groups
+  // that start at their document's first key are already aligned (rot 0).
+  int rot = 0, nrot = 0x3fffffff;
   {
     const RowKeys rk = row_keys(cu_s, cukl, cu, cuk, cu_in_lds, ndocs, q0, Tk);
     const int lo0 = (W > 0) ? max(rk.ds, rk.kp - W + 1) : rk.ds;
     kt0 = __builtin_amdgcn_readfirstlane((lo0 / BN) * BN);
+    if (PL && mode != SWA_BLOCKWISE && lo0 > rk.ds) {
+      // the work-group's tile count, as the loop below derives it (the last
+      // valid row's causal bound)
+      const RowKeys rl = row_keys(cu_s, cukl, cu, cuk, cu_in_lds, ndocs,
+                                  min(q0 + G::BM, Ttot) - 1, Tk);
+      nrot = (rl.kp - kt0) / BN + 1;
+      rot = (nrot - (kt0 / BN) % nrot) % nrot;
+    }
+    rot = __builtin_amdgcn_readfirstlane(rot);
+    nrot = __builtin_amdgcn_readfirstlane(nrot);
   }
+  // tile index of visit t (0 <= t < 2 nrot)
+  auto tix = [&](int t) {
+    const int u = t + rot;
+    return u >= nrot ? u - nrot : u;
+  };
   // pipelined layout: K ring of STAGES tiles, then V ring of STAGES tiles
   const uint32_t kring = ring_base, vring = ring_base + G::STAGES * G::TILE_BYTES;
   int voff[G::UPT];
@@ -646,9 +705,9 @@ void prefill_fwd_kernel(
   if constexpr (PL) {
     // groups 0 = {K_0} and 1 = {K_1, V_0} of the pipelined loop (K_1 is
     // loaded even when the work-group has a single key tile: unused then)
-    dma_pl(kbase, kt0, kring);
-    dma_pl(kbase, kt0 + BN, kring + G::TILE_BYTES);
-    dma_pl(vbase, kt0, vring);
+    dma_pl(kbase, kt0 + tix(0) * BN, kring);
+    dma_pl(kbase, kt0 + tix(1) * BN, kring + G::TILE_BYTES);
+    dma_pl(vbase, kt0 + tix(0) * BN, vring);
   } else {
     dma_tile(kt0, 0);
   }
@@ -851,6 +910,7 @@ void prefill_fwd_kernel(
     static_assert(TB + (NKS - 1) * 32 * ROWB + 16 * ROWB + (NDT / 8 - 1) * 256 < 65536,
                   "V offsets fit");
     const int n = (kmax - kt0) / BN + 1;  // key tiles of the work-group
+    // (a rotated visit order, rot > 0, was derived from this same count)
 
     // this wave's rows: key range, and the rectangle every one of them admits
     // (monotone causal intervals: first and last valid rows of the wave)
@@ -885,6 +945,11 @@ void prefill_fwd_kernel(
     // active key tiles of this wave: [ta, tb] (empty for a wave past the end)
     const int ta = __builtin_amdgcn_readfirstlane(whi >= wlo ? (wlo - kt0) / BN : n);
     const int tb = __builtin_amdgcn_readfirstlane(whi >= wlo ? min((whi - kt0) / BN, n - 1) : -1);
+    // does this wave have rows in the tile of visit t?
+    auto active = [&](int t) {
+      const int u = tix(t);
+      return u >= ta && u <= tb;
+    };
     wlomax = __builtin_amdgcn_readfirstlane(wlomax);
     whimin = __builtin_amdgcn_readfirstlane(whimin);
 
@@ -936,7 +1001,7 @@ void prefill_fwd_kernel(
     // outside the wave's range is masked whole (its scores may come from a
     // stale stage)
     auto mask = [&](int t, bool act, floatx4 (&sc)[MB][NKB]) {
-      const int k0 = kt0 + t * BN;
+      const int k0 = kt0 + tix(t) * BN;
       const bool full = act && (k0 >= wlomax) && (k0 + BN - 1 <= whimin);
       if (!full) {
 #pragma unroll
@@ -961,14 +1026,21 @@ void prefill_fwd_kernel(
     };
     auto s_mfmas = [&](auto kkc, auto kpc, const bf16x8 (&kf)[2], floatx4 (&sn)[MB][NKB]) {
       constexpr int kk = decltype(kkc)::value, kp = decltype(kpc)::value;
+      if constexpr (kAsmS) {
+        constexpr int kb0 = 2 * kp, kb1 = 2 * kp + 1;
+        if constexpr (kk == 0)
+          mfma4_bf16_vacc0(sn[0][kb0], sn[1][kb0], sn[0][kb1], sn[1][kb1], kf[0], kf[1], qf[0][kk],
+                           qf[1][kk]);
+        else
+          mfma4_bf16_vacc(sn[0][kb0], sn[1][kb0], sn[0][kb1], sn[1][kb1], kf[0], kf[1], qf[0][kk],
+                          qf[1][kk]);
+        return;
+      }
       static_for<2>([&](auto ic) {
         constexpr int kb = 2 * kp + decltype(ic)::value;
         static_for<2>([&](auto mbc) {
           constexpr int mb = decltype(mbc)::value;
-          if constexpr (kAsmS) {
-            if constexpr (kk == 0) mfma_bf16_vacc0(sn[mb][kb], kf[decltype(ic)::value], qf[mb][kk]);
-            else mfma_bf16_vacc(sn[mb][kb], kf[decltype(ic)::value], qf[mb][kk]);
-          } else {
+          {
             sn[mb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 kf[decltype(ic)::value], qf[mb][kk], kk == 0 ? s_init[mb] : sn[mb][kb], 0, 0, 0);
           }
@@ -1022,8 +1094,8 @@ void prefill_fwd_kernel(
       // its stage is free, and branches here cost the accumulators their
       // register assignment)
       const bool kld = t + 2 < n, vld = t + 1 < n;
-      const i32x4 rs_k = tile_rsrc(kbase, kt0 + (t + 2) * BN, kld);
-      const i32x4 rs_v = tile_rsrc(vbase, kt0 + (t + 1) * BN, vld);
+      const i32x4 rs_k = tile_rsrc(kbase, kt0 + tix(t + 2) * BN, kld);
+      const i32x4 rs_v = tile_rsrc(vbase, kt0 + tix(t + 1) * BN, vld);
       const uint32_t lw_k = kring + par * TB + wave_u * G::UPT * 1024;
       const uint32_t lw_v = vring + ((par + 1) % 2) * TB + wave_u * G::UPT * 1024;
       auto dma_unit = [&](auto uc) {
@@ -1033,13 +1105,13 @@ void prefill_fwd_kernel(
       };
       if constexpr (DPP == 0) {
         static_for<2 * G::UPT>(dma_unit);
-        if (!(t + 1 >= ta && t <= tb)) return;
+        if (!active(t) && !active(t + 1)) return;
       }
       // DPP > 0: a wave with no rows in tiles t and t+1 still runs the step
       // (its loads are spread through it; a branch around them would cost
       // the accumulators their registers): every score of such a tile is
       // masked, so its weights are 0 against finite V rows
-      const bool a_cur = t >= ta && t <= tb;
+      const bool a_cur = active(t);
       mask(t, a_cur, sc);
       if constexpr (kDiagRef) {
         // rows without a reference: their tile-t scores started from 0; the
@@ -1220,6 +1292,15 @@ void prefill_fwd_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       });
+      if constexpr (kAsmS) {
+        // the hand-written score products of tile t+1 may still be writing
+        // sn during phase 2: its registers stay reserved until here, also in
+        // a last step whose scores are never read
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) asm volatile("" : : "v"(sn[mb][kb]));
+      }
     };
 
     // Q in registers before the first product (the compiler does not count
@@ -1269,7 +1350,7 @@ void prefill_fwd_kernel(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (ta == 0) {
+      if (active(0)) {
         static_for<QR>([&](auto kkc) {
           static_for<NKB / 2>([&](auto kpc) {
             bf16x8 kf[2];
@@ -1301,9 +1382,9 @@ void prefill_fwd_kernel(
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o_acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
-      dma_pl(kbase, kt0, kring);
-      dma_pl(kbase, kt0 + BN, kring + G::TILE_BYTES);
-      dma_pl(vbase, kt0, vring);
+      dma_pl(kbase, kt0 + tix(0) * BN, kring);
+      dma_pl(kbase, kt0 + tix(1) * BN, kring + G::TILE_BYTES);
+      dma_pl(vbase, kt0 + tix(0) * BN, vring);
     };
     if constexpr (kDiagRef) {
       // (two inlined copies of the key loop rather than a loop over passes:
@@ -1334,13 +1415,13 @@ void prefill_fwd_kernel(
           mtrue[mb] = -INFINITY;
           s_init[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
-        for (int tt = 0; tt < n; ++tt) {
-          dma_pl(kbase, kt0 + tt * BN, kring);
+        for (int tt = 0; tt < n; ++tt) {  // (in visit order, as mask() reads it)
+          dma_pl(kbase, kt0 + tix(tt) * BN, kring);
           wait_vmcnt<0>();
           asm volatile("" ::: "memory");
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
-          if (tt >= ta && tt <= tb) {
+          if (active(tt)) {
             static_for<QR>([&](auto kkc) {
               static_for<NKB / 2>([&](auto kpc) {
                 bf16x8 kf[2];

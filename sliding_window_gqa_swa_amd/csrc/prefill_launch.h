@@ -23,7 +23,14 @@ int launch_prefill_cfg(const PrefillArgs& a) {
   // work-groups per XCD as its CUs hold at once (the kernel's occupancy), or
   // half the items when there are more
   int slots = (int)per_xcd, colocated = 0;
-  if (PL) {
+  // A window shorter than the average document makes most work items cost
+  // the same (a full window of key tiles): then every work-group takes one
+  // item, so that the items of an XCD start and end in cohorts that stream
+  // the same key tiles through its L2 (the rotated visit order in the
+  // kernel aligns them); pairing a long and a short item would stagger the
+  // cohorts.
+  const bool window_bound = a.window > 0 && (long long)a.window * a.num_docs < a.total_k;
+  if (PL && !window_bound) {
     constexpr int kWgPerCu = (NW == 4 && D <= 128 && !std::is_same<T, float>::value) ? 2 : 1;
     const long long fill = (long long)kWgPerCu * (device_cu_count() / 8);
     slots = (int)std::min<long long>(per_xcd, std::max<long long>(fill, (per_xcd + 1) / 2));
