@@ -13,7 +13,9 @@
  *   - All tensor arguments are DEVICE pointers on the current HIP device,
  *     row-major and contiguous, 16-byte aligned.  The caller allocates and
  *     owns every buffer (inputs, outputs, rings, ring_meta, workspace);
- *     the library allocates nothing and keeps no state between calls.
+ *     the library allocates nothing and keeps no state between calls
+ *     (swa_decode_step_noalloc alone uses a static device array of the
+ *     library as its workspace).
  *   - dtype selects the element type of every floating-point tensor of the
  *     call: SWA_BF16 (bfloat16) or SWA_F32 (float32).  Arithmetic is fp32
  *     (matrix-core products accumulate in fp32; bf16 outputs are rounded to
@@ -54,6 +56,7 @@ extern "C" {
 #define SWA_EUNSUPPORTED (-2) /* d, dtype, mode or size outside the range    */
 #define SWA_ELAUNCH (-3)      /* the HIP runtime refused a kernel launch     */
 #define SWA_EWORKSPACE (-4)   /* workspace missing or smaller than required  */
+#define SWA_ESCRATCH (-5)     /* sizes need more than the static scratch     */
 
 /* element types */
 #define SWA_BF16 0
@@ -268,6 +271,32 @@ SWA_API int swa_decode_step(const void* q, const void* k_new, const void* v_new,
                             void* out, int32_t batch, int32_t ring_rows, int32_t hq,
                             int32_t hkv, int32_t d, int32_t dtype, float scale,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * swa_decode_step_noalloc -- swa_decode_step without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments (minus the workspace), same kernels and bitwise the same
+ * results as swa_decode_step.  The split counters and fp32 partials live
+ * in a static device array of SWA_NOALLOC_SCRATCH_BYTES inside the
+ * library (one per GPU, held until the process ends); the call allocates
+ * nothing and calls no allocating routine.  Sizes whose partials and
+ * counters do not fit it (counters: batch * (kv heads x head blocks + 1)
+ * words within 64 KiB; partials: about batch * hq * splits * (d + 2) * 4
+ * bytes within the rest) return SWA_ESCRATCH before anything is launched.
+ * The first call on a device resolves the array's address and clears its
+ * counter region with a small kernel on `stream`; every call leaves the
+ * counters at zero again.  All calls on one GPU share the array: calls
+ * that overlap (different streams, or different host threads without
+ * ordering) race and must not be issued.
+ */
+#define SWA_NOALLOC_SCRATCH_BYTES (8u << 20)
+SWA_API int swa_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                                    void* k_ring, void* v_ring, int32_t* ring_meta,
+                                    int32_t window, void* out, int32_t batch, int32_t ring_rows,
+                                    int32_t hq, int32_t hkv, int32_t d, int32_t dtype,
+                                    float scale, void* stream);
 
 /*
  * swa_cache_append -- write one new token per sequence into its ring.

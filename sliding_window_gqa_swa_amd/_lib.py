@@ -14,6 +14,7 @@ SWA_EINVAL = -1
 SWA_EUNSUPPORTED = -2
 SWA_ELAUNCH = -3
 SWA_EWORKSPACE = -4
+SWA_ESCRATCH = -5
 
 SWA_BF16 = 0
 SWA_F32 = 1
@@ -39,6 +40,8 @@ SIGNATURES = {
     "swa_decode": (ctypes.c_int, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "swa_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P,
                                        _S, _P]),
+    "swa_decode_step_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
+                                               _I, _F, _P]),
     "swa_cache_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "swa_cache_compact": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "swa_cache_roll": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),

@@ -216,6 +216,24 @@ def decode_step(q, k_new, v_new, k_ring, v_ring, ring_meta, window, out=None, wo
     return out
 
 
+def decode_step_noalloc(q, k_new, v_new, k_ring, v_ring, ring_meta, window, out=None, scale=0.0):
+    """decode_step with the library's static scratch instead of a workspace
+    (nothing is allocated when `out` is given); see swa_decode_step_noalloc
+    in swa.h.  Raises with SWA_ESCRATCH for sizes beyond the scratch."""
+    B, hq, d = q.shape
+    _, hkv, R, _ = k_ring.shape
+    if k_new.shape != (B, hkv, d) or v_new.shape != (B, hkv, d):
+        raise ValueError("k_new and v_new must be [B, Hkv, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    rc = _lib.lib().swa_decode_step_noalloc(
+        _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dev(k_ring, "k_ring"),
+        _dev(v_ring, "v_ring"), _dev(ring_meta, "ring_meta", torch.int32), int(window),
+        _dev(out, "out"), B, R, hq, hkv, d, _dtype_code(q), float(scale), _stream(q))
+    _lib.check("swa_decode_step_noalloc", rc)
+    return out
+
+
 def cache_append(k_new, v_new, k_ring, v_ring, ring_meta):
     """Write one token per sequence at position pos + 1; see swa_cache_append."""
     B, hkv, R, d = k_ring.shape

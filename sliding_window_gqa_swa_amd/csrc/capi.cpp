@@ -75,6 +75,9 @@ SWA_API const char* swa_strerror(int code) {
       return "the HIP runtime refused a kernel launch";
     case SWA_EWORKSPACE:
       return "workspace missing or smaller than swa_decode_workspace_bytes()";
+    case SWA_ESCRATCH:
+      return "sizes need more split-K scratch than the static array of "
+             "swa_decode_step_noalloc holds (use swa_decode_step with a workspace)";
     default:
       return "unknown error code";
   }

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_codes():
     L = _lib.lib()
-    for code in (0, -1, -2, -3, -4, -99):
+    for code in (0, -1, -2, -3, -4, -5, -99):
         assert len(L.swa_strerror(code)) > 0
 
 
@@ -257,3 +257,26 @@ def test_binding_refuses_cpu_tensors():
     cu = torch.tensor([0, 4], dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU"):
         api.prefill(q, q[:, :1].contiguous(), q[:, :1].contiguous(), cu)
+
+
+def _noalloc(**kw):
+    a = dict(q=A, kn=A, vn=A, kr=A, vr=A, meta=B, W=1024, out=A, B=1, R=1088, hq=4, hkv=2, d=256,
+             dtype=0)
+    a.update(kw)
+    return _lib.lib().swa_decode_step_noalloc(a["q"], a["kn"], a["vn"], a["kr"], a["vr"], a["meta"],
+                                              a["W"], a["out"], a["B"], a["R"], a["hq"], a["hkv"],
+                                              a["d"], a["dtype"], 0.0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=320), _lib.SWA_EUNSUPPORTED),
+    (dict(R=1024), _lib.SWA_EINVAL),
+    (dict(hq=3), _lib.SWA_EINVAL),
+    (dict(out=None), _lib.SWA_EINVAL),
+    (dict(meta=B + 4), _lib.SWA_EINVAL),
+    # partials of 256 sequences x 32 heads x 2 splits x 514 floats: 16.8 MB,
+    # more than the 8 MiB static scratch
+    (dict(B=256, hq=32, hkv=8, d=512), _lib.SWA_ESCRATCH),
+])
+def test_decode_step_noalloc_rejects(kw, code):
+    assert _noalloc(**kw) == code
