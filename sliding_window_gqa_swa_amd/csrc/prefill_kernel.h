@@ -66,9 +66,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kCuCache = 1024;
 // exp2 arguments stay <= this between reference-max moves (p <= 2^8)
 constexpr float kRescaleSlack = 8.0f;
-// fixed-reference loop: largest rise (log2 units) of a row's scores above its
-// reference before the key loop is repeated with the true maxima (p <= 2^32)
-constexpr float kFixedRefLimit = 32.0f;
 // Work order: cost buckets of the counting sort, and the largest slice of
 // work items one XCD may hold for the sort (one byte each, in the LDS ring)
 constexpr int kPlanBuckets = 256;
@@ -141,6 +138,46 @@ __device__ __forceinline__ void dma16_buf(i32x4 rsrc, int voff, uint32_t lds_wav
                :
                : "s"(lds_wave_base), "v"(voff), "s"(rsrc)
                : "memory");
+}
+
+// NU (1 to 4) 16-byte-per-lane direct-to-LDS buffer loads that share one M0
+// write: load i lands at LDS byte lds_base + 1024 i + 16 * lane.  The
+// instruction offset (1024 i) moves both the memory and the LDS address, so
+// vo[i] holds the memory offset of load i minus 1024 i (an out-of-range
+// offset stays out of range).
+template <int NU>
+__device__ __forceinline__ void dma16_buf_group(i32x4 rsrc, const int* vo, uint32_t lds_base) {
+  static_assert(NU >= 1 && NU <= 4, "one to four loads per M0 write");
+  if constexpr (NU == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds"
+        :
+        : "s"(lds_base), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(rsrc)
+        : "memory");
+  } else if constexpr (NU == 3) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %4, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %4, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %3, %4, 0 offen offset:2048 lds"
+        :
+        : "s"(lds_base), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "s"(rsrc)
+        : "memory");
+  } else if constexpr (NU == 2) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds"
+        :
+        : "s"(lds_base), "v"(vo[0]), "v"(vo[1]), "s"(rsrc)
+        : "memory");
+  } else {
+    dma16_buf(rsrc, vo[0], lds_base);
+  }
 }
 
 // Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
@@ -272,17 +309,14 @@ struct PfTraits<float> {
 };
 
 // Pipelined loop schedule per head dimension: LDS fragment lookahead (K
-// fragment pairs, V^T fragment groups requested ahead of their use) and the
-// tile loads issued per K fragment pair (DPP; 0 = all at the start of a
-// step).  A direct-to-LDS load costs the issuing wave about 40 cycles, so a
-// burst of 16 of them idles the matrix cores of a single-wave SIMD; spread
-// out, they issue while earlier products run.  D = 128 runs two waves per
-// SIMD, which hide the burst.  (Chosen by measurement on MI355X.)
+// fragment pairs, V^T fragment groups requested ahead of their use).  The
+// tile loads of a step go out in groups of four (one M0 write each), spread
+// evenly over the step's K fragment pairs, so that they issue while earlier
+// products run.  (Chosen by measurement on MI355X.)
 template <int D>
 struct PfLookahead {
   static constexpr int K = 2;
   static constexpr int V = 1;
-  static constexpr int DPP = D == 128 ? 1 : 2;
 };
 
 // Workgroup geometry.
@@ -686,21 +720,31 @@ void prefill_fwd_kernel(
       if (chunk_src<G::CPR>(r_, s_ - r_ * G::CPR) >= CPM) voff[i] = kBufferOob;
     }
   }
-  // one K or V tile (keys k0 .. k0+BN-1 of this kv head) into an LDS stage;
-  // key rows at or past Tk fall outside the buffer and arrive as zeros
-  // descriptor of one K or V tile; `want` false gives an empty buffer, whose
-  // loads fetch nothing and fill their LDS slots with zeros
+  // the same offsets for loads issued four to an M0 write (dma16_buf_group)
+  int voffg[G::UPT];
+#pragma unroll
+  for (int i = 0; i < G::UPT; ++i) voffg[i] = voff[i] - (i % 4) * 1024;
+  // descriptor of one K or V tile (keys k0 .. k0+BN-1 of this kv head): it
+  // spans the tile's rows before Tk, so rows at or past Tk fall outside it
+  // and arrive as zeros; `want` false gives an empty buffer, whose loads
+  // fetch nothing and fill their LDS slots with zeros.  (The tile's rows
+  // are BN * Hkv * DM elements apart at most, far below 2^32 bytes.)
+  const uint32_t row_bytes = (uint32_t)(kv_row_stride * sizeof(T));
   auto tile_rsrc = [&](const T* tb, int k0, bool want = true) {
-    const T* p0 = tb + (size_t)k0 * kv_row_stride;
-    const long long rem = (long long)(Tk - k0) * (long long)kv_row_stride * (long long)sizeof(T);
-    const uint32_t nrec = (rem <= 0 || !want) ? 0u : (rem > 0xffffffffLL ? 0xffffffffu : (uint32_t)rem);
+    const char* p0 = reinterpret_cast<const char*>(tb) + (uint64_t)(uint32_t)k0 * row_bytes;
+    const int rows = min(Tk - k0, BN);
+    const uint32_t nrec = (rows <= 0 || !want) ? 0u : (uint32_t)rows * row_bytes;
     return make_buffer_rsrc(p0, nrec);
   };
+  // every unit of one tile, four loads per M0 write
   auto dma_pl = [&](const T* tb, int k0, uint32_t lds_stage) {
     const i32x4 rsrc = tile_rsrc(tb, k0);
     const uint32_t lw = lds_stage + wave_u * G::UPT * 1024;
-#pragma unroll
-    for (int i = 0; i < G::UPT; ++i) dma16_buf(rsrc, voff[i], lw + i * 1024);
+    static_for<(G::UPT + 3) / 4>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      constexpr int nu = G::UPT - 4 * g < 4 ? G::UPT - 4 * g : 4;
+      dma16_buf_group<nu>(rsrc, &voffg[4 * g], lw + 4 * g * 1024);
+    });
   };
   if constexpr (PL) {
     // groups 0 = {K_0} and 1 = {K_1, V_0} of the pipelined loop (K_1 is
@@ -896,9 +940,7 @@ void prefill_fwd_kernel(
     constexpr int NJ = NKS * (NDT / 2); // V^T fragment groups per tile (4 MFMAs each)
     // LDS fragment lookahead: K pairs and V groups requested ahead of use
     constexpr int KLA = PfLookahead<D>::K, VLA = PfLookahead<D>::V;
-    // tile loads issued per K fragment pair (0: all at the start of the step)
-    constexpr int DPP = PfLookahead<D>::DPP;
-    static_assert(DPP == 0 || DPP * NP >= 2 * G::UPT, "every load is issued in the step");
+    static_assert(NP >= 2 * ((G::UPT + 3) / 4), "a K fragment pair per load group");
     static_assert(2 * KLA <= 15 && 4 * VLA <= 15, "lgkmcnt range");
     // D >= 256: score products by hand (VGPR accumulators, see mfma_bf16_vacc)
     // and row sums on the VALU, so that the AGPRs hold O^T alone
@@ -979,13 +1021,16 @@ void prefill_fwd_kernel(
     // kDiagRef: every S^T product chain starts from minus the row's
     // reference, so the accumulator already holds the exp2 argument
     floatx4 s_init[MB];
-    bool ref_ok[MB];  // kDiagRef: the row has its reference (rows past the end need none)
-    float m_ref[MB], l_part[MB];  // l_part: this lane's share of the row sum (kAsmS)
-    float dmax[MB];               // kAsmS: rise of later tile maxima above m_ref
+    // the row has its reference (rows past the end need none)
+    bool ref_ok[MB];
+    // m_ref: running reference of the other loops; mcs (kAsmS): the row's
+    // fixed reference times c, subtracted inside the exp2 argument;
+    // l_part: this lane's share of the row sum
+    float m_ref[MB], mcs[MB], l_part[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       m_ref[mb] = -INFINITY;
-      dmax[mb] = -INFINITY;
+      mcs[mb] = 0.f;
       l_part[mb] = 0.f;
       l_acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
       s_init[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -1087,9 +1132,9 @@ void prefill_fwd_kernel(
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       // every wave is done with K_t and V_(t-1): refill their stages.  This
-      // wave's 2*UPT loads (V_(t+1) units, then K_(t+2) units) go out DPP
-      // per K fragment pair, so the vector memory queue never stalls the
-      // wave behind a burst (DPP = 0: all of them here)
+      // wave's 2*UPT loads (V_(t+1) units, then K_(t+2) units) go out in
+      // groups spread over the K fragment pairs below, so the vector memory
+      // queue never stalls the wave behind a burst
       // (a load that is not wanted gets an empty buffer instead of a branch:
       // its stage is free, and branches here cost the accumulators their
       // register assignment)
@@ -1098,26 +1143,28 @@ void prefill_fwd_kernel(
       const i32x4 rs_v = tile_rsrc(vbase, kt0 + tix(t + 1) * BN, vld);
       const uint32_t lw_k = kring + par * TB + wave_u * G::UPT * 1024;
       const uint32_t lw_v = vring + ((par + 1) % 2) * TB + wave_u * G::UPT * 1024;
-      auto dma_unit = [&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        if constexpr (u < G::UPT) dma16_buf(rs_v, voff[u], lw_v + u * 1024);
-        else dma16_buf(rs_k, voff[u - G::UPT], lw_k + (u - G::UPT) * 1024);
+      // load groups of four units (one M0 write each): V_(t+1) groups, then
+      // K_(t+2) groups
+      constexpr int GV = (G::UPT + 3) / 4;
+      auto dma_group = [&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        constexpr int gg = g < GV ? g : g - GV;
+        constexpr int nu = G::UPT - 4 * gg < 4 ? G::UPT - 4 * gg : 4;
+        if constexpr (g < GV) dma16_buf_group<nu>(rs_v, &voffg[4 * gg], lw_v + 4 * gg * 1024);
+        else dma16_buf_group<nu>(rs_k, &voffg[4 * gg], lw_k + 4 * gg * 1024);
       };
-      if constexpr (DPP == 0) {
-        static_for<2 * G::UPT>(dma_unit);
-        if (!active(t) && !active(t + 1)) return;
-      }
-      // DPP > 0: a wave with no rows in tiles t and t+1 still runs the step
-      // (its loads are spread through it; a branch around them would cost
-      // the accumulators their registers): every score of such a tile is
+      // a wave with no rows in tiles t and t+1 still runs the step (its
+      // loads are spread through it; a branch around them would cost the
+      // accumulators their registers): every score of such a tile is
       // masked, so its weights are 0 against finite V rows
       const bool a_cur = active(t);
       mask(t, a_cur, sc);
-      if constexpr (kDiagRef) {
-        // rows without a reference: their tile-t scores started from 0; the
-        // maximum of their allowed scores here becomes the reference, the
-        // scores are shifted by it, and the products issued from now on start
-        // from minus it (wave-uniform branch, taken in a row's first tiles)
+      if constexpr (kDiagRef || kAsmS) {
+        // rows without a reference: the maximum of their allowed scores in
+        // this tile becomes the reference (wave-uniform branch, taken in a
+        // row's first tiles).  kDiagRef: the tile-t scores started from 0,
+        // they are shifted by it and the products issued from now on start
+        // from minus it; kAsmS: it enters every later exp2 argument.
         bool need = false;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) need |= !ref_ok[mb];
@@ -1132,9 +1179,13 @@ void prefill_fwd_kernel(
             tmax = max_over_lane_groups(tmax);
             if (!ref_ok[mb] && tmax != -INFINITY) {
               ref_ok[mb] = true;
-              s_init[mb] = floatx4{-tmax, -tmax, -tmax, -tmax};
+              if constexpr (kDiagRef) {
+                s_init[mb] = floatx4{-tmax, -tmax, -tmax, -tmax};
 #pragma unroll
-              for (int kb = 0; kb < NKB; ++kb) sc[mb][kb] -= tmax;
+                for (int kb = 0; kb < NKB; ++kb) sc[mb][kb] -= tmax;
+              } else {
+                mcs[mb] = tmax * c_scale;
+              }
             }
           }
         }
@@ -1145,20 +1196,15 @@ void prefill_fwd_kernel(
       bool any_move = false;
       auto row_stats = [&](auto mbc) {
         constexpr int mb = decltype(mbc)::value;
-        if constexpr (kDiagRef) return;  // fixed reference, no row statistics
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sc[mb][kb][r]);
-        tmax = max_over_lane_groups(tmax);
-        if constexpr (kAsmS) {
-          // fixed reference: the maximum of the row's first tile with an
-          // allowed key; later maxima only record how far they rose above it
-          if (m_ref[mb] == -INFINITY) m_ref[mb] = tmax;
-          else dmax[mb] = fmaxf(dmax[mb], tmax - m_ref[mb]);
-          mc[mb] = m_ref[mb] == -INFINITY ? 0.f : m_ref[mb] * c_scale;
+        if constexpr (kDiagRef || kAsmS) {
+          return;  // fixed reference, no row statistics
         } else {
+          float tmax = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sc[mb][kb][r]);
+          tmax = max_over_lane_groups(tmax);
           const bool move = tmax > m_ref[mb] + slack;
           const float m_new = move ? tmax : m_ref[mb];
           alpha[mb] = move ? __builtin_amdgcn_exp2f((m_ref[mb] - m_new) * c_scale) : 1.f;
@@ -1176,15 +1222,16 @@ void prefill_fwd_kernel(
           e0 = __builtin_amdgcn_exp2f(sc[mb][kb][2 * rp]);
           e1 = __builtin_amdgcn_exp2f(sc[mb][kb][2 * rp + 1]);
         } else {
-          e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp], c_scale, -mc[mb]));
-          e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp + 1], c_scale, -mc[mb]));
+          const float m = kAsmS ? mcs[mb] : mc[mb];
+          e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp], c_scale, -m));
+          e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp + 1], c_scale, -m));
         }
         const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
         pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp] = b0;
         pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp + 1] = b1;
-        // the row sum adds the same bf16 weights that multiply V
-        if constexpr (kAsmS) l_part[mb] += (float)b0 + (float)b1;
-        if constexpr (kDiagRef) {  // one packed dot product with (1, 1)
+        if constexpr (kDiagRef || kAsmS) {
+          // the row sum adds the same bf16 weights that multiply V: one
+          // packed dot product with (1, 1)
           typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
           const bf16x2v pr = {b0, b1};
           const bf16x2v one2 = {(__bf16)1.0f, (__bf16)1.0f};
@@ -1225,12 +1272,11 @@ void prefill_fwd_kernel(
       constexpr int NE = MB * NKB * 2;  // exp pairs per tile
       static_for<NP>([&](auto qc) {
         constexpr int qq = decltype(qc)::value;
-        if constexpr (DPP > 0) {
-          static_for<DPP>([&](auto ic) {
-            constexpr int u = qq * DPP + decltype(ic)::value;
-            if constexpr (u < 2 * G::UPT) dma_unit(std::integral_constant<int, u>{});
-          });
-        }
+        // the 2 GV load groups spread evenly over the K fragment pairs
+        static_for<2 * GV>([&](auto gc) {
+          constexpr int g = decltype(gc)::value;
+          if constexpr (qq == g * NP / (2 * GV)) dma_group(gc);
+        });
         if constexpr (qq + KLA < NP)
           issue_k(std::integral_constant<int, (qq + KLA) / (NKB / 2)>{},
                   std::integral_constant<int, (qq + KLA) % (NKB / 2)>{}, KST, kf[(qq + KLA) % (KLA + 1)]);
@@ -1334,14 +1380,16 @@ void prefill_fwd_kernel(
       }
       if (tid == 0) plan_s[0] = 0;  // redo flag (the plan is done with it)
     }
-    // kAsmS: weights are exp2 of (score - reference) with a reference that
-    // never moves, so O^T is never rescaled (an in-loop rescale would give
-    // the AGPR accumulators VALU definitions, which the compiler resolves by
-    // copying them through VGPRs every iteration).  A weight can exceed 1 by
-    // at most 2^kFixedRefLimit, far inside fp32 and bf16 range.  If a row of
-    // the work-group rose further, the whole key loop runs a second time with
-    // every row's true maximum as its reference (all weights <= 1 then).
+    // kAsmS: the same fixed reference per row (the maximum of its first
+    // tile with an allowed key), with unscaled Q: the weight is
+    // exp2(s * c - reference * c), one FMA and one exp2, and O^T is never
+    // rescaled (an in-loop rescale would give the AGPR accumulators VALU
+    // definitions, which the compiler resolves by copying them through VGPRs
+    // every iteration); the same check after the loop and the same second
+    // pass with the true maxima.
     if constexpr (kAsmS) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) ref_ok[mb] = !(row_i[mb] < Ttot && row_lo[mb] != 0x3fffffff);
       if (tid == 0) plan_s[0] = 0;  // redo flag (the plan is done with it)
     }
     // group 0 (K_0) landed in every wave; the key loop of the work-group
@@ -1375,8 +1423,6 @@ void prefill_fwd_kernel(
     auto restart = [&]() {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        m_ref[mb] = m_ref[mb] == -INFINITY ? m_ref[mb] : m_ref[mb] + fmaxf(dmax[mb], 0.f);
-        dmax[mb] = -INFINITY;
         l_part[mb] = 0.f;
         l_acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1386,89 +1432,100 @@ void prefill_fwd_kernel(
       dma_pl(kbase, kt0 + tix(1) * BN, kring + G::TILE_BYTES);
       dma_pl(vbase, kt0 + tix(0) * BN, vring);
     };
+    // rows outside the safe range after a pass: row sums at or above 2^64,
+    // or (kDiagRef) a non-finite output (any inf or NaN in O^T makes the sum
+    // of its entries non-finite); one flag for the work-group.  kAsmS checks
+    // the row sums alone: summing its 256 O^T accumulators here would cost
+    // the key loop its registers, and with every weight below 2^64 the
+    // accumulators stay finite for values below 2^64 in magnitude.
+    auto out_of_range = [&]() __attribute__((always_inline)) {
+      bool bad = false;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        float l = l_part[mb];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        bad |= !(l < 0x1p64f);
+        if constexpr (kDiagRef) {
+          float osum = 0.f;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            osum += (o_acc[mb][dt][0] + o_acc[mb][dt][1]) + (o_acc[mb][dt][2] + o_acc[mb][dt][3]);
+          bad |= !(__builtin_fabsf(osum) < INFINITY);
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) plan_s[0] = 1;
+      lds_barrier();
+      return plan_s[0] != 0;
+    };
+    // the true row maxima (kDiagRef: of the log2-scaled scores), one K tile
+    // at a time, in visit order (as mask() reads it); they become the rows'
+    // references for a second pass
+    auto true_maxima = [&]() __attribute__((always_inline)) {
+      float mtrue[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        mtrue[mb] = -INFINITY;
+        s_init[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int tt = 0; tt < n; ++tt) {
+        dma_pl(kbase, kt0 + tix(tt) * BN, kring);
+        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (active(tt)) {
+          static_for<QR>([&](auto kkc) {
+            static_for<NKB / 2>([&](auto kpc) {
+              bf16x8 kf[2];
+              issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
+              lgkm_wait<0>(kf[0], kf[1]);
+              s_mfmas(kkc, kpc, kf, sA);
+            });
+          });
+          if constexpr (kAsmS) mfma_drain();  // the VALU below reads sA
+          mask(tt, true, sA);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sA[mb][kb][r]);
+            mtrue[mb] = fmaxf(mtrue[mb], max_over_lane_groups(tmax));
+          }
+        }
+        lds_barrier();  // every wave is done with the stage before it is refilled
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const float m = mtrue[mb] == -INFINITY ? 0.f : mtrue[mb];
+        if constexpr (kDiagRef) s_init[mb] = floatx4{-m, -m, -m, -m};
+        else mcs[mb] = m * c_scale;
+        ref_ok[mb] = true;
+      }
+    };
     if constexpr (kDiagRef) {
       // (two inlined copies of the key loop rather than a loop over passes:
       // a loop would keep the first pass's registers live across its back
       // edge and spill)
       key_loop();
-      // safe range: row sums below 2^64 and finite outputs (any inf or NaN
-      // in O^T makes the sum of its entries non-finite)
-      bool bad = false;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        float osum = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          osum += (o_acc[mb][dt][0] + o_acc[mb][dt][1]) + (o_acc[mb][dt][2] + o_acc[mb][dt][3]);
-        float l = l_part[mb];
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
-        bad |= !(l < 0x1p64f) || !(__builtin_fabsf(osum) < INFINITY);
-      }
-      if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) plan_s[0] = 1;
-      lds_barrier();
-      if (plan_s[0] != 0) {
-        // true row maxima of the scaled scores, one K tile at a time
-        float mtrue[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          mtrue[mb] = -INFINITY;
-          s_init[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-        for (int tt = 0; tt < n; ++tt) {  // (in visit order, as mask() reads it)
-          dma_pl(kbase, kt0 + tix(tt) * BN, kring);
-          wait_vmcnt<0>();
-          asm volatile("" ::: "memory");
-          __builtin_amdgcn_s_barrier();
-          asm volatile("" ::: "memory");
-          if (active(tt)) {
-            static_for<QR>([&](auto kkc) {
-              static_for<NKB / 2>([&](auto kpc) {
-                bf16x8 kf[2];
-                issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
-                lgkm_wait<0>(kf[0], kf[1]);
-                s_mfmas(kkc, kpc, kf, sA);
-              });
-            });
-            mask(tt, true, sA);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-              float tmax = -INFINITY;
-#pragma unroll
-              for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sA[mb][kb][r]);
-              mtrue[mb] = fmaxf(mtrue[mb], max_over_lane_groups(tmax));
-            }
-          }
-          lds_barrier();  // every wave is done with the stage before it is refilled
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const float m = mtrue[mb] == -INFINITY ? 0.f : mtrue[mb];
-          s_init[mb] = floatx4{-m, -m, -m, -m};
-          ref_ok[mb] = true;
-        }
+      if (out_of_range()) {
+        true_maxima();
         restart();
         key_loop();
       }
-    } else {
+    } else if constexpr (kAsmS) {
+      // (one copy of the key loop: at D = 512 a second inlined copy spills)
 #pragma nounroll
       for (int pass = 0;; ++pass) {
         if (pass > 0) restart();
         key_loop();
-        if constexpr (!kAsmS) {
-          break;
-        } else {
-          if (pass > 0) break;
-          bool rose = false;
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) rose |= dmax[mb] * c_scale > kFixedRefLimit;
-          if (__builtin_amdgcn_ballot_w64(rose) && lane == 0) plan_s[0] = 1;
-          lds_barrier();
-          if (plan_s[0] == 0) break;
-        }
+        if (pass > 0 || !out_of_range()) break;
+        true_maxima();
       }
+    } else {
+      key_loop();
     }
 
     // ---- epilogue: normalise, transpose through LDS, store whole rows --------
@@ -1507,7 +1564,7 @@ void prefill_fwd_kernel(
         if (LSE && grp == 0 && q0 + rb * G::WR + rr < Ttot) {
           // the row's log-sum-exp: its reference (log2 units) plus log2 of
           // its sum relative to it, in natural-log units
-          const float ref2 = kDiagRef ? -s_init[mb][0] : m_ref[mb] * c_scale;
+          const float ref2 = kDiagRef ? -s_init[mb][0] : (kAsmS ? mcs[mb] : m_ref[mb] * c_scale);
           lse_out[(size_t)h * Ttot + q0 + rb * G::WR + rr] =
               l > 0.f ? (ref2 + __builtin_log2f(l)) * kLn2 : -INFINITY;
         }
