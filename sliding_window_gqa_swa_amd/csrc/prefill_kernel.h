@@ -254,6 +254,18 @@ __device__ __forceinline__ void mfma4_bf16_vacc(floatx4& c00, floatx4& c01, floa
       : "+v"(c00), "+v"(c01), "+v"(c10), "+v"(c11)
       : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
 }
+// One product on its own, for schedules that interleave other instructions
+// between the products (one instruction issues per four cycles, so a run of
+// back-to-back products keeps the wave from issuing anything else).  No
+// leading wait states: callers must not write an operand with a vector ALU
+// instruction in the two wait states before it (the build checks the
+// generated code for that).
+__device__ __forceinline__ void mfma1_bf16_vacc(floatx4& c, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(k), "v"(q));
+}
+__device__ __forceinline__ void mfma1_bf16_vacc0(floatx4& c, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(k), "v"(q));
+}
 // the same with zero accumulators (the first head-dimension step)
 __device__ __forceinline__ void mfma4_bf16_vacc0(floatx4& c00, floatx4& c01, floatx4& c10,
                                                  floatx4& c11, const bf16x8& k0, const bf16x8& k1,
@@ -316,7 +328,7 @@ struct PfTraits<float> {
 template <int D>
 struct PfLookahead {
   static constexpr int K = 2;
-  static constexpr int V = 1;
+  static constexpr int V = 2;
 };
 
 // Workgroup geometry.
@@ -1069,6 +1081,13 @@ void prefill_fwd_kernel(
       dst[0] = lds_b128<OFF + (2 * kp) * 16 * ROWB>(kaddr[kk % 4]);
       dst[1] = lds_b128<OFF + (2 * kp + 1) * 16 * ROWB>(kaddr[kk % 4]);
     };
+    // one of the two reads of issue_k (ic = 0, 1)
+    auto issue_k1 = [&](auto kkc, auto kpc, auto kstc, auto icc, bf16x8& dst) {
+      constexpr int kk = decltype(kkc)::value, kp = decltype(kpc)::value, KST = decltype(kstc)::value;
+      constexpr int ic = decltype(icc)::value;
+      constexpr int OFF = KST + (kk / 4) * 256;
+      dst = lds_b128<OFF + (2 * kp + ic) * 16 * ROWB>(kaddr[kk % 4]);
+    };
     auto s_mfmas = [&](auto kkc, auto kpc, const bf16x8 (&kf)[2], floatx4 (&sn)[MB][NKB]) {
       constexpr int kk = decltype(kkc)::value, kp = decltype(kpc)::value;
       if constexpr (kAsmS) {
@@ -1102,6 +1121,23 @@ void prefill_fwd_kernel(
       dst[1] = lds_tr16_b64<OFF + 16 * ROWB>(vaddr[dt0 % 8]);
       dst[2] = lds_tr16_b64<OFF>(vaddr[dt0 % 8 + 1]);
       dst[3] = lds_tr16_b64<OFF + 16 * ROWB>(vaddr[dt0 % 8 + 1]);
+    };
+    // read r (0..3) of issue_v
+    auto issue_v1 = [&](auto jc, auto vstc, auto rc, short4v& dst) {
+      constexpr int j = decltype(jc)::value, VST = decltype(vstc)::value, r = decltype(rc)::value;
+      constexpr int ks = j / (NDT / 2), dt0 = 2 * (j % (NDT / 2));
+      constexpr int OFF = VST + ks * 32 * ROWB + (dt0 / 8) * 256 + (r & 1) * 16 * ROWB;
+      dst = lds_tr16_b64<OFF>(vaddr[dt0 % 8 + (r >> 1)]);
+    };
+    // product (hh, mb) of V^T group j
+    auto pv1 = [&](auto jc, auto hc, auto mbc, const short4v (&v4)[4], const bf16x8 (&pf)[MB][NKS]) {
+      constexpr int j = decltype(jc)::value, hh = decltype(hc)::value, mb = decltype(mbc)::value;
+      constexpr int ks = j / (NDT / 2), dt0 = 2 * (j % (NDT / 2));
+      const short8v x8 = {v4[2 * hh][0], v4[2 * hh][1], v4[2 * hh][2], v4[2 * hh][3],
+                          v4[2 * hh + 1][0], v4[2 * hh + 1][1], v4[2 * hh + 1][2], v4[2 * hh + 1][3]};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, x8);
+      o_acc[mb][dt0 + hh] =
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[mb][ks], o_acc[mb][dt0 + hh], 0, 0, 0);
     };
     auto pv_mfmas = [&](auto jc, const short4v (&v4)[4], const bf16x8 (&pf)[MB][NKS]) {
       constexpr int j = decltype(jc)::value;
@@ -1270,7 +1306,50 @@ void prefill_fwd_kernel(
       // waits for phase 2, whose first half does not read it); otherwise
       // exp pairs spread evenly over the K pairs
       constexpr int NE = MB * NKB * 2;  // exp pairs per tile
-      static_for<NP>([&](auto qc) {
+      if constexpr (kAsmS) {
+        // One wave per SIMD issues one instruction per four cycles, so each
+        // product is followed by the other work of its K fragment pair (a
+        // read of the pair KLA ahead, a load group, an exp pair) rather than
+        // four products back to back: the matrix pipe runs while they issue.
+        static_for<NP>([&](auto qc) {
+          constexpr int qq = decltype(qc)::value;
+          constexpr int kk = qq / (NKB / 2), kp = qq % (NKB / 2);
+          constexpr int kb0 = 2 * kp, kb1 = 2 * kp + 1;
+          constexpr int cur = qq % (KLA + 1), nxt = (qq + KLA) % (KLA + 1);
+          constexpr bool more = qq + KLA < NP;
+          constexpr std::integral_constant<int, (qq + KLA) / (NKB / 2)> nkk{};
+          constexpr std::integral_constant<int, (qq + KLA) % (NKB / 2)> nkp{};
+          // pairs qq+1 .. min(qq+KLA-1, NP-1) may stay in flight
+          constexpr int kahead = (NP - 1 - qq) < (KLA - 1) ? (NP - 1 - qq) : (KLA - 1);
+          auto prod = [&](floatx4& c, const bf16x8& a, const bf16x8& b) {
+            if constexpr (kk == 0) mfma1_bf16_vacc0(c, a, b);
+            else mfma1_bf16_vacc(c, a, b);
+          };
+          lgkm_wait<2 * kahead>(kf[cur][0], kf[cur][1]);
+          prod(sn[0][kb0], kf[cur][0], qf[0][kk]);
+          if constexpr (more) issue_k1(nkk, nkp, KST, I0, kf[nxt][0]);
+          __builtin_amdgcn_sched_barrier(0);
+          prod(sn[1][kb0], kf[cur][0], qf[1][kk]);
+          if constexpr (more) issue_k1(nkk, nkp, KST, I1, kf[nxt][1]);
+          __builtin_amdgcn_sched_barrier(0);
+          prod(sn[0][kb1], kf[cur][1], qf[0][kk]);
+          static_for<2 * GV>([&](auto gc) {
+            constexpr int g = decltype(gc)::value;
+            if constexpr (qq == g * NP / (2 * GV)) dma_group(gc);
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          prod(sn[1][kb1], kf[cur][1], qf[1][kk]);
+          static_for<NE>([&](auto ec) {
+            constexpr int e = decltype(ec)::value;
+            if constexpr (qq == e * NP / NE) {
+              exp_pair_pinned(std::integral_constant<int, e / (NKB * 2)>{},
+                              std::integral_constant<int, (e / 2) % NKB>{},
+                              std::integral_constant<int, e % 2>{});
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else static_for<NP>([&](auto qc) {
         constexpr int qq = decltype(qc)::value;
         // the 2 GV load groups spread evenly over the K fragment pairs
         static_for<2 * GV>([&](auto gc) {
@@ -1323,13 +1402,25 @@ void prefill_fwd_kernel(
       // weights alongside)
       static_for<NJ>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
-        if constexpr (j + VLA < NJ)
-          issue_v(std::integral_constant<int, j + VLA>{}, VST, vf[(j + VLA) % (VLA + 1)]);
         if constexpr (D == 128 && j == 0) { exp_quarter(I1, I1); asm volatile("" : "+v"(pc[1][1])); }
-        constexpr int vahead = (NJ - 1 - j) < VLA ? (NJ - 1 - j) : VLA;
-        constexpr int vs = j % (VLA + 1);
+        // groups j+1 .. min(j+VLA-1, NJ-1) may stay in flight; the reads of
+        // group j+VLA go out one after each product of group j
+        constexpr int vahead = (NJ - 1 - j) < (VLA - 1) ? (NJ - 1 - j) : (VLA - 1);
+        constexpr int vs = j % (VLA + 1), vn = (j + VLA) % (VLA + 1);
+        constexpr bool vmore = j + VLA < NJ;
+        constexpr std::integral_constant<int, j + VLA> jn{};
         lgkm_wait<4 * vahead>(vf[vs][0], vf[vs][1], vf[vs][2], vf[vs][3]);
-        pv_mfmas(jc, vf[vs], pc);
+        pv1(jc, I0, I0, vf[vs], pc);
+        if constexpr (vmore) issue_v1(jn, VST, I0, vf[vn][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        pv1(jc, I0, I1, vf[vs], pc);
+        if constexpr (vmore) issue_v1(jn, VST, I1, vf[vn][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        pv1(jc, I1, I0, vf[vs], pc);
+        if constexpr (vmore) issue_v1(jn, VST, I2, vf[vn][2]);
+        __builtin_amdgcn_sched_barrier(0);
+        pv1(jc, I1, I1, vf[vs], pc);
+        if constexpr (vmore) issue_v1(jn, VST, I3, vf[vn][3]);
         if constexpr (!kAsmS && !kDiagRef && j % (NDT / 2) == NDT / 2 - 1) {
           static_for<2>([&](auto mbc) {
             constexpr int mb = decltype(mbc)::value;
