@@ -266,6 +266,20 @@ __device__ __forceinline__ void mfma1_bf16_vacc(floatx4& c, const bf16x8& k, con
 __device__ __forceinline__ void mfma1_bf16_vacc0(floatx4& c, const bf16x8& k, const bf16x8& q) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(k), "v"(q));
 }
+// lgkm_wait<N> on the K fragment pair (k0, k1) and the product (c, k0, q)
+// as one statement (two statements let the compiler put wait states between
+// them that the hardware does not need)
+template <int N, bool ZERO>
+__device__ __forceinline__ void lgkm_wait_mfma1(floatx4& c, bf16x8& k0, bf16x8& k1,
+                                                const bf16x8& q) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  if constexpr (ZERO)
+    asm volatile("s_waitcnt lgkmcnt(%4)\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %3, 0"
+                 : "=&v"(c), "+v"(k0), "+v"(k1) : "v"(q), "i"(N));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%4)\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %3, %0"
+                 : "+v"(c), "+v"(k0), "+v"(k1) : "v"(q), "i"(N));
+}
 // the same with zero accumulators (the first head-dimension step)
 __device__ __forceinline__ void mfma4_bf16_vacc0(floatx4& c00, floatx4& c01, floatx4& c10,
                                                  floatx4& c11, const bf16x8& k0, const bf16x8& k1,
@@ -1081,12 +1095,16 @@ void prefill_fwd_kernel(
       dst[0] = lds_b128<OFF + (2 * kp) * 16 * ROWB>(kaddr[kk % 4]);
       dst[1] = lds_b128<OFF + (2 * kp + 1) * 16 * ROWB>(kaddr[kk % 4]);
     };
-    // one of the two reads of issue_k (ic = 0, 1)
+    // one of the two reads of issue_k (ic = 0, 1), as a plain LDS load: the
+    // compiler then places the lgkmcnt wait before the first product that
+    // reads it, counting exactly the reads issued after it (the scheduling
+    // barriers around each product keep the reads where they are written)
     auto issue_k1 = [&](auto kkc, auto kpc, auto kstc, auto icc, bf16x8& dst) {
       constexpr int kk = decltype(kkc)::value, kp = decltype(kpc)::value, KST = decltype(kstc)::value;
       constexpr int ic = decltype(icc)::value;
-      constexpr int OFF = KST + (kk / 4) * 256;
-      dst = lds_b128<OFF + (2 * kp + ic) * 16 * ROWB>(kaddr[kk % 4]);
+      constexpr int OFF = KST + (kk / 4) * 256 + (2 * kp + ic) * 16 * ROWB;
+      dst = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+          (size_t)(kaddr[kk % 4] + OFF));
     };
     auto s_mfmas = [&](auto kkc, auto kpc, const bf16x8 (&kf)[2], floatx4 (&sn)[MB][NKB]) {
       constexpr int kk = decltype(kkc)::value, kp = decltype(kpc)::value;
@@ -1122,12 +1140,14 @@ void prefill_fwd_kernel(
       dst[2] = lds_tr16_b64<OFF>(vaddr[dt0 % 8 + 1]);
       dst[3] = lds_tr16_b64<OFF + 16 * ROWB>(vaddr[dt0 % 8 + 1]);
     };
-    // read r (0..3) of issue_v
+    // read r (0..3) of issue_v, as a plain transposed LDS load (see issue_k1)
     auto issue_v1 = [&](auto jc, auto vstc, auto rc, short4v& dst) {
       constexpr int j = decltype(jc)::value, VST = decltype(vstc)::value, r = decltype(rc)::value;
       constexpr int ks = j / (NDT / 2), dt0 = 2 * (j % (NDT / 2));
       constexpr int OFF = VST + ks * 32 * ROWB + (dt0 / 8) * 256 + (r & 1) * 16 * ROWB;
-      dst = lds_tr16_b64<OFF>(vaddr[dt0 % 8 + (r >> 1)]);
+      dst = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<__attribute__((address_space(3))) short4v*>(
+              (size_t)(vaddr[dt0 % 8 + (r >> 1)] + OFF)));
     };
     // product (hh, mb) of V^T group j
     auto pv1 = [&](auto jc, auto hc, auto mbc, const short4v (&v4)[4], const bf16x8 (&pf)[MB][NKS]) {
@@ -1195,12 +1215,12 @@ void prefill_fwd_kernel(
       // masked, so its weights are 0 against finite V rows
       const bool a_cur = active(t);
       mask(t, a_cur, sc);
-      if constexpr (kDiagRef || kAsmS) {
+      if constexpr (kDiagRef) {
         // rows without a reference: the maximum of their allowed scores in
         // this tile becomes the reference (wave-uniform branch, taken in a
-        // row's first tiles).  kDiagRef: the tile-t scores started from 0,
-        // they are shifted by it and the products issued from now on start
-        // from minus it; kAsmS: it enters every later exp2 argument.
+        // row's first tiles): the tile-t scores started from 0, they are
+        // shifted by it and the products issued from now on start from
+        // minus it
         bool need = false;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) need |= !ref_ok[mb];
@@ -1215,13 +1235,9 @@ void prefill_fwd_kernel(
             tmax = max_over_lane_groups(tmax);
             if (!ref_ok[mb] && tmax != -INFINITY) {
               ref_ok[mb] = true;
-              if constexpr (kDiagRef) {
-                s_init[mb] = floatx4{-tmax, -tmax, -tmax, -tmax};
+              s_init[mb] = floatx4{-tmax, -tmax, -tmax, -tmax};
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) sc[mb][kb] -= tmax;
-              } else {
-                mcs[mb] = tmax * c_scale;
-              }
+              for (int kb = 0; kb < NKB; ++kb) sc[mb][kb] -= tmax;
             }
           }
         }
@@ -1232,7 +1248,7 @@ void prefill_fwd_kernel(
       bool any_move = false;
       auto row_stats = [&](auto mbc) {
         constexpr int mb = decltype(mbc)::value;
-        if constexpr (kDiagRef || kAsmS) {
+        if constexpr (kDiagRef) {
           return;  // fixed reference, no row statistics
         } else {
           float tmax = -INFINITY;
@@ -1258,14 +1274,13 @@ void prefill_fwd_kernel(
           e0 = __builtin_amdgcn_exp2f(sc[mb][kb][2 * rp]);
           e1 = __builtin_amdgcn_exp2f(sc[mb][kb][2 * rp + 1]);
         } else {
-          const float m = kAsmS ? mcs[mb] : mc[mb];
-          e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp], c_scale, -m));
-          e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp + 1], c_scale, -m));
+          e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp], c_scale, -mc[mb]));
+          e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp + 1], c_scale, -mc[mb]));
         }
         const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
         pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp] = b0;
         pc[mb][kb / 2][(kb & 1) * 4 + 2 * rp + 1] = b1;
-        if constexpr (kDiagRef || kAsmS) {
+        if constexpr (kDiagRef) {
           // the row sum adds the same bf16 weights that multiply V: one
           // packed dot product with (1, 1)
           typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -1297,8 +1312,14 @@ void prefill_fwd_kernel(
       bf16x8 kf[KLA + 1][2];
       static_for<(KLA < NP ? KLA : NP)>([&](auto pc0) {
         constexpr int q0 = decltype(pc0)::value;
-        issue_k(std::integral_constant<int, q0 / (NKB / 2)>{}, std::integral_constant<int, q0 % (NKB / 2)>{},
-                KST, kf[q0]);
+        constexpr std::integral_constant<int, q0 / (NKB / 2)> kk0{};
+        constexpr std::integral_constant<int, q0 % (NKB / 2)> kp0{};
+        if constexpr (kAsmS) {
+          issue_k1(kk0, kp0, KST, std::integral_constant<int, 0>{}, kf[q0][0]);
+          issue_k1(kk0, kp0, KST, std::integral_constant<int, 1>{}, kf[q0][1]);
+        } else {
+          issue_k(kk0, kp0, KST, kf[q0]);
+        }
       });
       row_stats(I0);
       __builtin_amdgcn_sched_barrier(0);
@@ -1306,50 +1327,7 @@ void prefill_fwd_kernel(
       // waits for phase 2, whose first half does not read it); otherwise
       // exp pairs spread evenly over the K pairs
       constexpr int NE = MB * NKB * 2;  // exp pairs per tile
-      if constexpr (kAsmS) {
-        // One wave per SIMD issues one instruction per four cycles, so each
-        // product is followed by the other work of its K fragment pair (a
-        // read of the pair KLA ahead, a load group, an exp pair) rather than
-        // four products back to back: the matrix pipe runs while they issue.
-        static_for<NP>([&](auto qc) {
-          constexpr int qq = decltype(qc)::value;
-          constexpr int kk = qq / (NKB / 2), kp = qq % (NKB / 2);
-          constexpr int kb0 = 2 * kp, kb1 = 2 * kp + 1;
-          constexpr int cur = qq % (KLA + 1), nxt = (qq + KLA) % (KLA + 1);
-          constexpr bool more = qq + KLA < NP;
-          constexpr std::integral_constant<int, (qq + KLA) / (NKB / 2)> nkk{};
-          constexpr std::integral_constant<int, (qq + KLA) % (NKB / 2)> nkp{};
-          // pairs qq+1 .. min(qq+KLA-1, NP-1) may stay in flight
-          constexpr int kahead = (NP - 1 - qq) < (KLA - 1) ? (NP - 1 - qq) : (KLA - 1);
-          auto prod = [&](floatx4& c, const bf16x8& a, const bf16x8& b) {
-            if constexpr (kk == 0) mfma1_bf16_vacc0(c, a, b);
-            else mfma1_bf16_vacc(c, a, b);
-          };
-          lgkm_wait<2 * kahead>(kf[cur][0], kf[cur][1]);
-          prod(sn[0][kb0], kf[cur][0], qf[0][kk]);
-          if constexpr (more) issue_k1(nkk, nkp, KST, I0, kf[nxt][0]);
-          __builtin_amdgcn_sched_barrier(0);
-          prod(sn[1][kb0], kf[cur][0], qf[1][kk]);
-          if constexpr (more) issue_k1(nkk, nkp, KST, I1, kf[nxt][1]);
-          __builtin_amdgcn_sched_barrier(0);
-          prod(sn[0][kb1], kf[cur][1], qf[0][kk]);
-          static_for<2 * GV>([&](auto gc) {
-            constexpr int g = decltype(gc)::value;
-            if constexpr (qq == g * NP / (2 * GV)) dma_group(gc);
-          });
-          __builtin_amdgcn_sched_barrier(0);
-          prod(sn[1][kb1], kf[cur][1], qf[1][kk]);
-          static_for<NE>([&](auto ec) {
-            constexpr int e = decltype(ec)::value;
-            if constexpr (qq == e * NP / NE) {
-              exp_pair_pinned(std::integral_constant<int, e / (NKB * 2)>{},
-                              std::integral_constant<int, (e / 2) % NKB>{},
-                              std::integral_constant<int, e % 2>{});
-            }
-          });
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      } else static_for<NP>([&](auto qc) {
+      static_for<NP>([&](auto qc) {
         constexpr int qq = decltype(qc)::value;
         // the 2 GV load groups spread evenly over the K fragment pairs
         static_for<2 * GV>([&](auto gc) {
@@ -1367,11 +1345,12 @@ void prefill_fwd_kernel(
         if constexpr (qq == 0) row_stats(I1);
         // (each finished fragment is pinned by an empty asm: the compiler
         // would otherwise sink the work to its use after the rescale branch)
-        if constexpr (D == 128) {
-          if constexpr (qq == 1) { exp_quarter(I0, I0); asm volatile("" : "+v"(pc[0][0])); }
-          if constexpr (qq == 3) { exp_quarter(I0, I1); asm volatile("" : "+v"(pc[0][1])); }
-          if constexpr (qq == 5) { exp_quarter(I1, I0); asm volatile("" : "+v"(pc[1][0])); }
-        } else {
+        // (conditions on qq, so that other head sizes never instantiate the
+        // D = 128 calls)
+        if constexpr (D == 128 && qq == 1) { exp_quarter(I0, I0); asm volatile("" : "+v"(pc[0][0])); }
+        if constexpr (D == 128 && qq == 3) { exp_quarter(I0, I1); asm volatile("" : "+v"(pc[0][1])); }
+        if constexpr (D == 128 && qq == 5) { exp_quarter(I1, I0); asm volatile("" : "+v"(pc[1][0])); }
+        if constexpr (D != 128) {
           static_for<NE>([&](auto ec) {
             constexpr int e = decltype(ec)::value;
             if constexpr (qq == 1 + e * (NP - 1) / NE) {
@@ -1386,7 +1365,9 @@ void prefill_fwd_kernel(
       short4v vf[VLA + 1][4];
       static_for<(VLA < NJ ? VLA : NJ)>([&](auto jc0) {
         constexpr int j0 = decltype(jc0)::value;
-        issue_v(std::integral_constant<int, j0>{}, VST, vf[j0]);
+        static_for<4>([&](auto rc) {
+          issue_v1(std::integral_constant<int, j0>{}, VST, rc, vf[j0][decltype(rc)::value]);
+        });
       });
       if constexpr (!kAsmS && !kDiagRef) {
         if (__builtin_amdgcn_ballot_w64(any_move)) {  // rare after the first tiles
@@ -1402,14 +1383,17 @@ void prefill_fwd_kernel(
       // weights alongside)
       static_for<NJ>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
-        if constexpr (D == 128 && j == 0) { exp_quarter(I1, I1); asm volatile("" : "+v"(pc[1][1])); }
-        // groups j+1 .. min(j+VLA-1, NJ-1) may stay in flight; the reads of
-        // group j+VLA go out one after each product of group j
-        constexpr int vahead = (NJ - 1 - j) < (VLA - 1) ? (NJ - 1 - j) : (VLA - 1);
+        if constexpr (D == 128 && j == 0) {
+          // (indices written so that other head sizes, which discard this
+          // branch, still name elements inside the arrays)
+          constexpr std::integral_constant<int, (NKB >= 4 ? 1 : 0)> E1{};
+          exp_quarter(I1, E1);
+          asm volatile("" : "+v"(pc[1][NKS - 1]));
+        }
+        // the reads of group j+VLA go out one after each product of group j
         constexpr int vs = j % (VLA + 1), vn = (j + VLA) % (VLA + 1);
         constexpr bool vmore = j + VLA < NJ;
         constexpr std::integral_constant<int, j + VLA> jn{};
-        lgkm_wait<4 * vahead>(vf[vs][0], vf[vs][1], vf[vs][2], vf[vs][3]);
         pv1(jc, I0, I0, vf[vs], pc);
         if constexpr (vmore) issue_v1(jn, VST, I0, vf[vn][0]);
         __builtin_amdgcn_sched_barrier(0);
@@ -1429,15 +1413,218 @@ void prefill_fwd_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
       });
-      if constexpr (kAsmS) {
-        // the hand-written score products of tile t+1 may still be writing
-        // sn during phase 2: its registers stay reserved until here, also in
-        // a last step whose scores are never read
+    };
+
+    // ---- D >= 256: the weights of tile t+1 are formed in the output phase
+    // of step t.  The score phase of step t (S^T of tile t+1) then carries
+    // only products, K reads and tile loads, and the output phase (O^T of
+    // tile t) the V^T reads, the exps of tile t+1 and its mask, so that each
+    // phase issues at most about one other instruction per product.  One
+    // score buffer serves every step (its scores are consumed within the
+    // step); the weights alternate between two buffers (those of tile t
+    // are read while those of tile t+1 are written).
+    bf16x8 pwA[MB][NKS], pwB[MB][NKS];
+    // rows that have no reference take the maximum of their allowed scores
+    // in sc (wave-uniform branch, taken in a row's first tiles)
+    auto set_refs = [&](const floatx4 (&sc)[MB][NKB]) __attribute__((always_inline)) {
+      bool need = false;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb) need |= !ref_ok[mb];
+      if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) asm volatile("" : : "v"(sn[mb][kb]));
+        for (int mb = 0; mb < MB; ++mb) {
+          float tmax = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sc[mb][kb][r]);
+          tmax = max_over_lane_groups(tmax);
+          if (!ref_ok[mb] && tmax != -INFINITY) {
+            ref_ok[mb] = true;
+            mcs[mb] = tmax * c_scale;
+          }
+        }
       }
+    };
+    // weights of keys kb*16 + 4 grp + (2 rp, 2 rp + 1) of q-block mb from
+    // sc into pw, and their sum into the row sum (the same bf16 values)
+    auto exp_pair_w = [&](auto mbc, auto kbc, auto rpc, const floatx4 (&sc)[MB][NKB],
+                          bf16x8 (&pw)[MB][NKS]) __attribute__((always_inline)) {
+      constexpr int mb = decltype(mbc)::value, kb = decltype(kbc)::value, rp = decltype(rpc)::value;
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp], c_scale, -mcs[mb]));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mb][kb][2 * rp + 1], c_scale, -mcs[mb]));
+      const __bf16 b0 = (__bf16)e0, b1 = (__bf16)e1;
+      pw[mb][kb / 2][(kb & 1) * 4 + 2 * rp] = b0;
+      pw[mb][kb / 2][(kb & 1) * 4 + 2 * rp + 1] = b1;
+      typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+      const bf16x2v pr = {b0, b1};
+      const bf16x2v one2 = {(__bf16)1.0f, (__bf16)1.0f};
+      l_part[mb] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, l_part[mb], false);
+    };
+    constexpr int NEW = MB * NKB * 2;  // exp pairs per tile
+    // mask, references and every weight of visit t at once (the first tile)
+    auto weights_all = [&](int t, bool act, floatx4 (&sc)[MB][NKB], bf16x8 (&pw)[MB][NKS])
+        __attribute__((always_inline)) {
+      mask(t, act, sc);
+      set_refs(sc);
+      static_for<NEW>([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        exp_pair_w(std::integral_constant<int, e / (NKB * 2)>{},
+                   std::integral_constant<int, (e / 2) % NKB>{}, std::integral_constant<int, e % 2>{},
+                   sc, pw);
+      });
+    };
+    // one step of visit t (parity par): S^T of visit t+1 into sA; O^T of
+    // visit t with its weights (pw of parity par); the weights of visit t+1
+    // into the other buffer
+    auto step_as = [&](auto parc, int t) __attribute__((always_inline)) {
+      constexpr int par = decltype(parc)::value;
+      constexpr std::integral_constant<int, ((par + 1) % 2) * TB> KST{};  // K stage of visit t+1
+      constexpr std::integral_constant<int, par * TB> VST{};              // V stage of visit t
+      bf16x8 (&pcur)[MB][NKS] = par ? pwB : pwA;
+      bf16x8 (&pnxt)[MB][NKS] = par ? pwA : pwB;
+      constexpr std::integral_constant<int, 0> I0{};
+      constexpr std::integral_constant<int, 1> I1{};
+      constexpr std::integral_constant<int, 2> I2{};
+      constexpr std::integral_constant<int, 3> I3{};
+      // group t+1 = {K_(t+1), V_t}, the latest issued, landed in every wave
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // every wave is done with K_t and V_(t-1): refill their stages (the
+      // groups below are spread over the K fragment pairs; an unwanted load
+      // gets an empty buffer instead of a branch)
+      const bool kld = t + 2 < n, vld = t + 1 < n;
+      const i32x4 rs_k = tile_rsrc(kbase, kt0 + tix(t + 2) * BN, kld);
+      const i32x4 rs_v = tile_rsrc(vbase, kt0 + tix(t + 1) * BN, vld);
+      const uint32_t lw_k = kring + par * TB + wave_u * G::UPT * 1024;
+      const uint32_t lw_v = vring + ((par + 1) % 2) * TB + wave_u * G::UPT * 1024;
+      constexpr int GV = (G::UPT + 3) / 4;
+      auto dma_group = [&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        constexpr int gg = g < GV ? g : g - GV;
+        constexpr int nu = G::UPT - 4 * gg < 4 ? G::UPT - 4 * gg : 4;
+        if constexpr (g < GV) dma16_buf_group<nu>(rs_v, &voffg[4 * gg], lw_v + 4 * gg * 1024);
+        else dma16_buf_group<nu>(rs_k, &voffg[4 * gg], lw_k + 4 * gg * 1024);
+      };
+      // -- score phase: S^T of visit t+1; each product is followed by a K
+      // read of the pair KLA ahead or a load group
+      bf16x8 kf[KLA + 1][2];
+      static_for<(KLA < NP ? KLA : NP)>([&](auto pc0) {
+        constexpr int q0 = decltype(pc0)::value;
+        issue_k1(std::integral_constant<int, q0 / (NKB / 2)>{}, std::integral_constant<int, q0 % (NKB / 2)>{},
+                 KST, I0, kf[q0][0]);
+        issue_k1(std::integral_constant<int, q0 / (NKB / 2)>{}, std::integral_constant<int, q0 % (NKB / 2)>{},
+                 KST, I1, kf[q0][1]);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<NP>([&](auto qc) {
+        constexpr int qq = decltype(qc)::value;
+        constexpr int kk = qq / (NKB / 2), kp = qq % (NKB / 2);
+        constexpr int kb0 = 2 * kp, kb1 = 2 * kp + 1;
+        constexpr int cur = qq % (KLA + 1), nxt = (qq + KLA) % (KLA + 1);
+        constexpr bool more = qq + KLA < NP;
+        constexpr std::integral_constant<int, (qq + KLA) / (NKB / 2)> nkk{};
+        constexpr std::integral_constant<int, (qq + KLA) % (NKB / 2)> nkp{};
+        auto prod = [&](floatx4& c, const bf16x8& a, const bf16x8& b) {
+          if constexpr (kk == 0) mfma1_bf16_vacc0(c, a, b);
+          else mfma1_bf16_vacc(c, a, b);
+        };
+        prod(sA[0][kb0], kf[cur][0], qf[0][kk]);
+        if constexpr (more) issue_k1(nkk, nkp, KST, I0, kf[nxt][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        prod(sA[1][kb0], kf[cur][0], qf[1][kk]);
+        if constexpr (more) issue_k1(nkk, nkp, KST, I1, kf[nxt][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        prod(sA[0][kb1], kf[cur][1], qf[0][kk]);
+        static_for<2 * GV>([&](auto gc) {
+          constexpr int g = decltype(gc)::value;
+          if constexpr (qq == g * NP / (2 * GV)) dma_group(gc);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        prod(sA[1][kb1], kf[cur][1], qf[1][kk]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // -- output phase: O^T of visit t; one V^T read (two groups ahead)
+      // after each product; from group 2 on (the score products are done by
+      // then) the mask and references of visit t+1, then its exp pairs
+      short4v vf[VLA + 1][4];
+      static_for<(VLA < NJ ? VLA : NJ)>([&](auto jc0) {
+        constexpr int j0 = decltype(jc0)::value;
+        static_for<4>([&](auto rc) {
+          issue_v1(std::integral_constant<int, j0>{}, VST, rc, vf[j0][decltype(rc)::value]);
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      // visit t+1 is past the last tile in the last step: its (stale)
+      // scores are masked whole, so its weights add nothing
+      const bool a_nxt = t + 1 < n && active(t + 1);
+      constexpr int J0 = NJ > 2 ? 2 : NJ - 1;  // group that starts the weights
+      static_assert(NJ - J0 >= 1, "a group for the weights");
+      // the exp pairs of visit t+1 go one per group from group J0 on, after
+      // the group's third product (measured: splitting a pair's stages over
+      // several product gaps gained nothing)
+      static_for<NJ>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int vs = j % (VLA + 1), vn = (j + VLA) % (VLA + 1);
+        constexpr bool vmore = j + VLA < NJ;
+        constexpr std::integral_constant<int, j + VLA> jn{};
+        if constexpr (j == J0) {
+          mask(t + 1, a_nxt, sA);
+          set_refs(sA);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        pv1(jc, I0, I0, vf[vs], pcur);
+        if constexpr (vmore) issue_v1(jn, VST, I0, vf[vn][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        pv1(jc, I0, I1, vf[vs], pcur);
+        if constexpr (vmore) issue_v1(jn, VST, I1, vf[vn][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        pv1(jc, I1, I0, vf[vs], pcur);
+        if constexpr (vmore) issue_v1(jn, VST, I2, vf[vn][2]);
+        static_for<NEW>([&](auto ec) {
+          constexpr int e = decltype(ec)::value;
+          if constexpr (j == J0 + e * (NJ - J0) / NEW)
+            exp_pair_w(std::integral_constant<int, e / (NKB * 2)>{},
+                       std::integral_constant<int, (e / 2) % NKB>{},
+                       std::integral_constant<int, e % 2>{}, sA, pnxt);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        pv1(jc, I1, I1, vf[vs], pcur);
+        if constexpr (vmore) issue_v1(jn, VST, I3, vf[vn][3]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // stages that run past the last product slot
+
+    };
+    auto key_loop_as = [&]() __attribute__((always_inline)) {
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const bool a0 = active(0);
+      if (a0) {
+        static_for<QR>([&](auto kkc) {
+          static_for<NKB / 2>([&](auto kpc) {
+            bf16x8 kf[2];
+            issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
+            lgkm_wait<0>(kf[0], kf[1]);
+            s_mfmas(kkc, kpc, kf, sA);
+          });
+        });
+        mfma_drain();  // the VALU below reads sA
+      }
+      weights_all(0, a0, sA, pwA);
+      constexpr std::integral_constant<int, 0> EVEN{};
+      constexpr std::integral_constant<int, 1> ODD{};
+      int t = 0;
+      for (; t + 1 < n; t += 2) {
+        step_as(EVEN, t);
+        step_as(ODD, t + 1);
+      }
+      if (t < n) step_as(EVEN, t);
+      wait_vmcnt<0>();  // nothing may still be writing LDS below
     };
 
     // Q in registers before the first product (the compiler does not count
@@ -1484,7 +1671,10 @@ void prefill_fwd_kernel(
       if (tid == 0) plan_s[0] = 0;  // redo flag (the plan is done with it)
     }
     // group 0 (K_0) landed in every wave; the key loop of the work-group
+    // (D = 128; D >= 256 runs key_loop_as: the guard keeps the other head
+    // sizes from instantiating this one)
     auto key_loop = [&]() __attribute__((always_inline)) {
+      if constexpr (kDiagRef) {
       wait_vmcnt<0>();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -1509,6 +1699,7 @@ void prefill_fwd_kernel(
       }
       if (t < n) step(EVEN, t, sA, sB);
       wait_vmcnt<0>();  // nothing may still be writing LDS below
+      }
     };
     // second pass: accumulators cleared, first load groups again
     auto restart = [&]() {
@@ -1611,7 +1802,7 @@ void prefill_fwd_kernel(
 #pragma nounroll
       for (int pass = 0;; ++pass) {
         if (pass > 0) restart();
-        key_loop();
+        key_loop_as();
         if (pass > 0 || !out_of_range()) break;
         true_maxima();
       }
