@@ -52,6 +52,10 @@ WORKLOAD_KERNELS = {
                               _PF + ["prefill_d256.hip"]),
     "prefill_4x1024_gqa_d320": ("prefill_fwd_kernel", "prefill_fwd_kernel<384 (320 in memory), bf16>",
                                 _PF + ["prefill_d320.hip"]),
+    "prefill_16k_gqa4_d128_w4k": ("prefill_fwd_kernel", "prefill_fwd_kernel<128, bf16>",
+                                  _PF + ["prefill_d128.hip"]),
+    "prefill_16k_gqa2_d128_w4k": ("prefill_fwd_kernel", "prefill_fwd_kernel<128, bf16>",
+                                  _PF + ["prefill_d128.hip"]),
     "decode_b64_d256": ("decode_split_kernel", "decode_split_kernel<256, bf16> (decode alone)",
                         ["decode.hip"]),
     "decode_single_d256": ("decode_split_kernel", "decode_split_kernel<256, bf16> (decode alone)",

@@ -8,6 +8,8 @@ namespace swa {
 int launch_prefill_d256(const PrefillArgs& a) {
   const int g = a.hq / a.hkv;
   if (a.dtype == SWA_BF16) {
+    if (g % 4 == 0)
+      return launch_prefill_cfg<256, __bf16, 2, 64, 4, 4, true>(a);
     if (g % 2 == 0)
       return launch_prefill_cfg<256, __bf16, 2, 64, 4, 2, true>(a);
     return launch_prefill_cfg<256, __bf16, 2, 64, 4, 1, true>(a);

@@ -10,6 +10,8 @@ int launch_prefill_d320(const PrefillArgs& a) {
   const int g = a.hq / a.hkv;
   if (a.dtype == SWA_BF16) {
     // computed as head size 384 with zero padding on the pipelined loop
+    if (g % 4 == 0)
+      return launch_prefill_cfg<384, __bf16, 2, 32, 4, 4, true, 320>(a);
     if (g % 2 == 0)
       return launch_prefill_cfg<384, __bf16, 2, 32, 4, 2, true, 320>(a);
     return launch_prefill_cfg<384, __bf16, 2, 32, 4, 1, true, 320>(a);

@@ -469,13 +469,13 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // barrier.  sel_s: 6 ints, wsum_s: 2 * NT / 64 ints.
 template <int NT, int BM, int BN>
 __device__ void lpt_select(const int* cu_s, const int* cuk_s, int ndocs, int Ttot, int Tk, int W,
-                           int ntiles, int w0, int P,
+                           int ntiles, int hgroups, int w0, int P,
                            const int (&pos)[2], unsigned char* bk, int* hist_s, int* wsum_s,
                            int* sel_s, int (&out)[2]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int NWV = NT / 64;
   for (int i = tid; i < P; i += NT) {
-    const int w = w0 + i;
+    const int w = (w0 + i) / hgroups;  // (kv head, tile rank), as the kernel numbers items
     const int c = tile_cost_bucket<BM, BN>(cu_s, cuk_s, ndocs, ntiles - 1 - (w % ntiles), Ttot, Tk, W);
     bk[i] = (unsigned char)c;
     atomicAdd(&hist_s[c], 1);
@@ -636,7 +636,8 @@ void prefill_fwd_kernel(
   }
   if (plan) {
     const int posv[2] = {pos, pos2};
-    lpt_select<G::NT, G::BM, BN>(cu_s, cukl, ndocs, Ttot, Tk, W, ntiles, w0, P, posv, &ring[0][0], hist_s,
+    lpt_select<G::NT, G::BM, BN>(cu_s, cukl, ndocs, Ttot, Tk, W, ntiles, hq / hkv / GH, w0, P, posv,
+                                 &ring[0][0], hist_s,
                                  plan_s + 6, plan_s, items);
   }
 #pragma nounroll
@@ -655,13 +656,17 @@ void prefill_fwd_kernel(
   const int wave = tid >> 6;
   const int c16 = lane & 15;
   const int grp = lane >> 4;
-  const int hg_index = work / ntiles;
-  const int tile = ntiles - 1 - (work - hg_index * ntiles);  // heavy tiles first
-  const int q0 = tile * G::BM;
+  // Item numbering: (kv head, tile rank, head group), the head group
+  // fastest, so that the groups of GH heads that read the same K/V tiles
+  // (query groups larger than GH) run side by side on one XCD and share
+  // them in its L2; tile rank 0 is the last query tile (heavy tiles first).
   const int g = hq / hkv;
   const int hgroups = g / GH;
-  const int kvh = hg_index / hgroups;
-  const int hbase = kvh * g + (hg_index - kvh * hgroups) * GH;
+  const int kt_index = work / hgroups;
+  const int kvh = kt_index / ntiles;
+  const int tile = ntiles - 1 - (kt_index - kvh * ntiles);
+  const int q0 = tile * G::BM;
+  const int hbase = kvh * g + (work - kt_index * hgroups) * GH;
   const int jh = wave % GH;  // head of this wave within the group
   const int rb = wave / GH;  // row block of this wave
   const int h = hbase + jh;

@@ -143,12 +143,28 @@ def prefill_4x1024_gqa_d320() -> PrefillCase:
                        hq=16, hkv=8, d=320, window=1024, mode=CAUSAL, seed=6)
 
 
+def prefill_16k_gqa4_d128_w4k() -> PrefillCase:
+    """The 16K window-4K D=128 shape with 8 kv heads shared by groups of 4
+    query heads ([SDPA] Summary: grouped-query attention); with its group-of-2
+    twin below it shows whether K/V bytes read from memory depend on the
+    group size."""
+    return PrefillCase("prefill_16k_gqa4_d128_w4k", np.array([0, 16384], dtype=np.int32),
+                       hq=32, hkv=8, d=128, window=4096, mode=CAUSAL, seed=8)
+
+
+def prefill_16k_gqa2_d128_w4k() -> PrefillCase:
+    return PrefillCase("prefill_16k_gqa2_d128_w4k", np.array([0, 16384], dtype=np.int32),
+                       hq=16, hkv=8, d=128, window=4096, mode=CAUSAL, seed=9)
+
+
 PREFILL_WORKLOADS = {
     "prefill_4x1024_mha_d128": prefill_4x1024_mha_d128,
     "prefill_16k_gqa_d512": prefill_16k_gqa_d512,
     "prefill_vlm_4096_d256": prefill_vlm_4096_d256,
     "prefill_4x1024_gqa_d320": prefill_4x1024_gqa_d320,
     "prefill_16k_mha_d128_w4k": prefill_16k_mha_d128_w4k,
+    "prefill_16k_gqa4_d128_w4k": prefill_16k_gqa4_d128_w4k,
+    "prefill_16k_gqa2_d128_w4k": prefill_16k_gqa2_d128_w4k,
 }
 
 

@@ -29,3 +29,11 @@ def test_decode_valid_rows():
     pos = np.array([0, 5, 3000, 40], np.int64)
     lo = np.array([0, 2, 0, 39], np.int64)
     np.testing.assert_array_equal(bench.decode_valid_rows(pos, lo, 1024), [1, 4, 1024, 2])
+
+
+def test_every_workload_names_its_kernel():
+    """bench.py --only accepts every named workload: each has the kernel and
+    sources its roofline and traffic record refer to."""
+    for name in list(si.PREFILL_WORKLOADS) + list(si.DECODE_WORKLOADS):
+        assert name in bench.WORKLOAD_KERNELS, name
+        bench.sources_hash(name)

@@ -71,6 +71,40 @@ def test_prefill_small_ragged(d, dtype, mode):
         assert_close(got, want, dtype, "d=%d %s mode=%d W=%d" % (d, dtype, mode, W))
 
 
+@pytest.mark.parametrize("d", [64, 128, 256, 320, 512])
+@pytest.mark.parametrize("g", [4, 8])
+def test_prefill_gqa_groups_of_4_and_8(d, g):
+    """Query groups of 4 and 8 heads per kv head (4 heads share each K/V
+    tile; a group of 8 runs as two such work-groups side by side): ragged
+    documents under both masks, and one long document whose window is
+    shorter than it (the launch that runs one item per work-group and
+    visits its key tiles in rotated order)."""
+    require_gpu()
+    rng = si.rng_for(4000 + d + g)
+    hkv = 2 if g == 4 else 1
+    hq = hkv * g
+    T = 389
+    cu = np.array([0, 77, 78, 300, T], np.int32)
+    q = si.normal(rng, (T, hq, d), "bf16")
+    k = si.normal(rng, (T, hkv, d), "bf16")
+    v = si.normal(rng, (T, hkv, d), "bf16")
+    ids = _ids_for(T, cu, 31 + d)
+    for mode, W in ((CAUSAL, 0), (CAUSAL, 37), (BLOCKWISE, 200)):
+        log("prefill gqa d=%d g=%d mode=%d W=%d" % (d, g, mode, W))
+        got = _run(q, k, v, cu, ids if mode == BLOCKWISE else None, W, mode, "bf16")
+        want = orc.prefill(q, k, v, cu, ids if mode == BLOCKWISE else None, W, mode)
+        assert_close(got, want, "bf16", "gqa d=%d g=%d mode=%d W=%d" % (d, g, mode, W))
+    T2, W2 = 900, 100
+    cu2 = np.array([0, T2], np.int32)
+    q2 = si.normal(rng, (T2, hq, d), "bf16")
+    k2 = si.normal(rng, (T2, hkv, d), "bf16")
+    v2 = si.normal(rng, (T2, hkv, d), "bf16")
+    log("prefill gqa window-bound d=%d g=%d" % (d, g))
+    got = _run(q2, k2, v2, cu2, None, W2, CAUSAL, "bf16")
+    want = orc.prefill(q2, k2, v2, cu2, None, W2, CAUSAL)
+    assert_close(got, want, "bf16", "gqa window-bound d=%d g=%d" % (d, g))
+
+
 @pytest.mark.parametrize("d", [128, 256, 320, 512])
 @pytest.mark.parametrize("mode", [CAUSAL, BLOCKWISE])
 def test_prefill_odd_group(d, mode):
