@@ -33,11 +33,19 @@
 // keeps its physical row, the A oldest rows become free); the token is
 // appended at slot(p) unless the ring is still full (then nothing is
 // written and the sticky flag is set, as for swa_cache_append).  Blocks
-// whose rows include slot(p) take that row from k_new / v_new instead of
-// the ring, and exactly one of them writes it to the ring, so no block
-// reads a row while it is written.  The last block of a sequence (a second
-// device-scope counter) stores the new ring_meta after every block of the
-// sequence has read the old one.
+// whose rows include slot(p) use that row from k_new / v_new, never the
+// ring's copy, and exactly one of them writes it to the ring after its row
+// loop.  The last block of a sequence (a second device-scope counter)
+// stores the new ring_meta after every block of the sequence has read the
+// old one.
+//
+// Small grids (at most about one block per CU: a single sequence, or a few)
+// are bound by the chain of memory latencies, not by bandwidth.  There the
+// kernel (LA = true) requests every row of its split before ring_meta has
+// arrived and applies the mask to the loaded rows, so the ring_meta load
+// and the first row loads are in flight together (the masked rows' bytes,
+// at most the 64 slack rows of a ring, are read for nothing; a decode
+// step's appended row is loaded and replaced by the step's input).
 #include <type_traits>
 
 #include "swa_common.h"
@@ -54,6 +62,7 @@ constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kMaxRowsPerSplit = 544;
 constexpr int kTargetBlocks = 256;  // about one block per CU before the row cap adds more
 constexpr int kMaxSplits = 256;      // (m, l) of every split fit the combine's LDS
+constexpr int kLoadAllRows = 64;     // minimum rows per split of a small grid
 constexpr float kLog2e = 1.4426950408889634f;
 
 // 16-byte chunk of a row as fp32.
@@ -106,7 +115,7 @@ struct DecGeom {
   static constexpr int ELT = CPL * VEC;             // elements per lane
 };
 
-template <int D, typename T, int GB, bool STEP>
+template <int D, typename T, int GB, bool STEP, bool LA>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const T* __restrict__ q, T* __restrict__ k_ring, T* __restrict__ v_ring,
     int32_t* __restrict__ meta, int W, int R, int hq, int hkv, int head_blocks,
@@ -157,19 +166,30 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   if (W > 0) low = max(low, pos - W + 1);
   const int64_t high = pos;
 
-  // query chunks of every head of this block, pre-scaled into the log2 domain
-  float qv[GB][G::ELT];
+  // query chunks of every head of this block: bf16 queries stay packed (the
+  // scores are bf16 pair dot products, scaled into the log2 domain after
+  // the sum); fp32 queries are pre-scaled
+  constexpr bool kBf = !std::is_same<T, float>::value;
+  float qv[GB][kBf ? 1 : G::ELT];
+  u32x4 qw[GB][kBf ? G::CPL : 1];
+  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 0; j < GB; ++j) {
-    const int h = h0 + min(j, nh - 1);
+    for (int j = 0; j < GB; ++j) {
+      const int h = h0 + min(j, nh - 1);
 #pragma unroll
-    for (int c = 0; c < G::CPL; ++c) {
-      float f[G::VEC];
-      load_chunk<T>(q + ((size_t)b * hq + h) * D + (size_t)(li + c * G::LPR) * G::VEC, f);
+      for (int c = 0; c < G::CPL; ++c) {
+        const T* src = q + ((size_t)b * hq + h) * D + (size_t)(li + c * G::LPR) * G::VEC;
+        if constexpr (kBf) {
+          qw[j][c] = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          float f[G::VEC];
+          load_chunk<T>(src, f);
 #pragma unroll
-      for (int e = 0; e < G::VEC; ++e) qv[j][c * G::VEC + e] = f[e] * qk_scale_log2;
+          for (int e = 0; e < G::VEC; ++e) qv[j][c * G::VEC + e] = f[e] * qk_scale_log2;
+        }
+      }
     }
-  }
+  };
 
   // one buffer descriptor per ring: masked rows load from an out-of-range
   // offset, which returns zeros without touching memory
@@ -178,16 +198,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   const i32x4 krs = make_buffer_rsrc(k_ring + ring_off, ring_bytes);
   const i32x4 vrs = make_buffer_rsrc(v_ring + ring_off, ring_bytes);
   const size_t new_off = ((size_t)b * hkv + kvh) * D;  // row of k_new / v_new
-  if constexpr (STEP) {
-    // one writer of the appended row: head block 0 of the split holding it
-    if (hb == 0 && slot_p >= r0 && slot_p < r1) {
-      for (int c = threadIdx.x; c < D / G::VEC; c += kDecThreads) {
-        const size_t dst = ring_off + (size_t)slot_p * D + (size_t)c * G::VEC;
-        *reinterpret_cast<u32x4*>(k_ring + dst) =
-            *reinterpret_cast<const u32x4*>(k_new + new_off + (size_t)c * G::VEC);
-        *reinterpret_cast<u32x4*>(v_ring + dst) =
-            *reinterpret_cast<const u32x4*>(v_new + new_off + (size_t)c * G::VEC);
-      }
+  // LA decode step: this lane's chunks of the appended row, requested with
+  // the first row loads (they replace the ring's copy of the row in consume)
+  u32x4 kn_c[G::CPL], vn_c[G::CPL];
+  if constexpr (STEP && LA) {
+#pragma unroll
+    for (int c = 0; c < G::CPL; ++c) {
+      const size_t e0 = new_off + (size_t)(li + c * G::LPR) * G::VEC;
+      kn_c[c] = *reinterpret_cast<const u32x4*>(k_new + e0);
+      vn_c[c] = *reinterpret_cast<const u32x4*>(v_new + e0);
     }
   }
 
@@ -200,23 +219,36 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     for (int e = 0; e < G::ELT; ++e) acc[j][e] = 0.f;
   }
 
-  // row steps per batch of K and V loads (2 rather than 4: fewer registers
-  // per batch, more waves in flight; 50 vs 53.5 us at two splits, measured)
-  constexpr int U = 2;
+  // row steps per batch of K and V loads (2 rather than 4 on large grids:
+  // fewer registers per batch, more waves in flight; 50 vs 53.5 us at two
+  // splits, measured; 4 on small grids, whose blocks each take more rows)
+  constexpr int U = LA ? 4 : 2;
   constexpr int STEPR = G::RPI * U;  // rows per batch
   // One batch of row loads: every lane issues U rows x CPL chunks of K and
   // V.  Batches past r1 issue only out-of-range offsets (zeros, no memory
   // access), so the pipeline below needs no branch around a load.
+  // (LA: every row below r1 is loaded; ok is then only r < r1, and consume
+  // applies the window mask.)
   auto issue = [&](int base, u32x4 (&kw)[U][G::CPL], u32x4 (&vw)[U][G::CPL], bool (&ok)[U])
       __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = base + u * G::RPI + wave * G::RPW + rg;
+      const int32_t row_byte = r * (int32_t)(D * sizeof(T));
+      if constexpr (LA) {
+        ok[u] = r < r1;
+#pragma unroll
+        for (int c = 0; c < G::CPL; ++c) {
+          const int32_t off = ok[u] ? row_byte + (li + c * G::LPR) * 16 : kBufferOob;
+          kw[u][c] = buffer_load16(krs, off);
+          vw[u][c] = buffer_load16(vrs, off);
+        }
+        continue;
+      }
       int jj = r - start;
       jj += jj < 0 ? R : 0;
       const int64_t a = anchor + jj;
       ok[u] = r < r1 && a >= low && a <= high;
-      const int32_t row_byte = r * (int32_t)(D * sizeof(T));
 #pragma unroll
       for (int c = 0; c < G::CPL; ++c) {
         const int32_t off = ok[u] ? row_byte + (li + c * G::LPR) * 16 : kBufferOob;
@@ -232,22 +264,63 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     }
   };
   // scores, online softmax over the batch, then the weighted V rows
-  auto consume = [&](const u32x4 (&kw)[U][G::CPL], const u32x4 (&vw)[U][G::CPL],
-                     const bool (&ok)[U]) __attribute__((always_inline)) {
+  auto consume = [&](int base, u32x4 (&kw)[U][G::CPL], u32x4 (&vw)[U][G::CPL], bool (&ok)[U])
+      __attribute__((always_inline)) {
+    if constexpr (LA) {
+      // the window mask of the rows loaded unconditionally; the appended
+      // row of a decode step comes from the step's input
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = base + u * G::RPI + wave * G::RPW + rg;
+        int jj = r - start;
+        jj += jj < 0 ? R : 0;
+        const int64_t a = anchor + jj;
+        ok[u] = ok[u] && a >= low && a <= high;
+        if constexpr (STEP) {
+          if (r == slot_p) {
+#pragma unroll
+            for (int c = 0; c < G::CPL; ++c) {
+              kw[u][c] = kn_c[c];
+              vw[u][c] = vn_c[c];
+            }
+          }
+        }
+      }
+    }
     // scores (identical in every lane of a row group)
     float sc[U][GB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float kf[G::ELT];
+      if constexpr (kBf) {
+        typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 #pragma unroll
-      for (int c = 0; c < G::CPL; ++c) unpack_chunk<T>(kw[u][c], &kf[c * G::VEC]);
+        for (int j = 0; j < GB; ++j) {
+          float x = 0.f;
 #pragma unroll
-      for (int j = 0; j < GB; ++j) {
-        float x = 0.f;
+          for (int c = 0; c < G::CPL; ++c)
 #pragma unroll
-        for (int e = 0; e < G::ELT; ++e) x = fmaf(qv[j][e], kf[e], x);
-        x = group_sum<G::LPR>(x);
-        sc[u][j] = ok[u] ? x : -INFINITY;
+            for (int w = 0; w < 4; ++w) {
+              // (through scalars: a bit cast of a vector element reads
+              // element 0 whatever the index, in this compiler)
+              const uint32_t kx = kw[u][c][w], qx = qw[j][c][w];
+              x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, kx),
+                                                  __builtin_bit_cast(bf16x2v, qx), x, false);
+            }
+          x = group_sum<G::LPR>(x) * qk_scale_log2;
+          sc[u][j] = ok[u] ? x : -INFINITY;
+        }
+      } else {
+        float kf[G::ELT];
+#pragma unroll
+        for (int c = 0; c < G::CPL; ++c) unpack_chunk<T>(kw[u][c], &kf[c * G::VEC]);
+#pragma unroll
+        for (int j = 0; j < GB; ++j) {
+          float x = 0.f;
+#pragma unroll
+          for (int e = 0; e < G::ELT; ++e) x = fmaf(qv[j][e], kf[e], x);
+          x = group_sum<G::LPR>(x);
+          sc[u][j] = ok[u] ? x : -INFINITY;
+        }
       }
     }
 #pragma unroll
@@ -281,30 +354,51 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   };
   // two batches in flight: the next batch's loads go out before the current
   // batch is consumed, so a wave waits for memory once per split, not once
-  // per batch
+  // per batch.  LA: the query loads go out after the first two batches
+  // (loads complete in order: waiting for the query earlier would wait for
+  // it alone and leave the batches for a second round trip).
   {
     u32x4 kA[U][G::CPL], vA[U][G::CPL], kB[U][G::CPL], vB[U][G::CPL];
     bool okA[U], okB[U];
     int base = r0;
+    if constexpr (!LA) load_q();
     issue(base, kA, vA, okA);
+    issue(base + STEPR, kB, vB, okB);
+    if constexpr (LA) {
+      asm volatile("" ::: "memory");
+      load_q();
+    }
     while (base < r1) {
-      issue(base + STEPR, kB, vB, okB);
-      consume(kA, vA, okA);
+      consume(base, kA, vA, okA);
       base += STEPR;
       if (base >= r1) break;
       issue(base + STEPR, kA, vA, okA);
-      consume(kB, vB, okB);
+      consume(base, kB, vB, okB);
       base += STEPR;
+      if (base >= r1) break;
+      issue(base + STEPR, kB, vB, okB);
+    }
+  }
+  if constexpr (STEP) {
+    // one writer of the appended row: head block 0 of the split holding it
+    if (hb == 0 && slot_p >= r0 && slot_p < r1) {
+      for (int c = threadIdx.x; c < D / G::VEC; c += kDecThreads) {
+        const size_t dst = ring_off + (size_t)slot_p * D + (size_t)c * G::VEC;
+        *reinterpret_cast<u32x4*>(k_ring + dst) =
+            *reinterpret_cast<const u32x4*>(k_new + new_off + (size_t)c * G::VEC);
+        *reinterpret_cast<u32x4*>(v_ring + dst) =
+            *reinterpret_cast<const u32x4*>(v_new + new_off + (size_t)c * G::VEC);
+      }
     }
   }
 
   // merge the row groups of the wave (lanes that differ above LPR)
-#pragma unroll
-  for (int o = G::LPR; o < kWave; o <<= 1) {
+  auto merge_rows = [&](auto oc) __attribute__((always_inline)) {
+    constexpr int o = decltype(oc)::value;
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
-      const float m2 = __shfl_xor(mrun[j], o, kWave);
-      const float l2 = __shfl_xor(lrun[j], o, kWave);
+      const float m2 = lane_xor<o>(mrun[j]);
+      const float l2 = lane_xor<o>(lrun[j]);
       const float M = fmaxf(mrun[j], m2);
       const float Mr = M == -INFINITY ? 0.f : M;
       const float e1 = __builtin_amdgcn_exp2f(mrun[j] - Mr);
@@ -312,12 +406,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       lrun[j] = lrun[j] * e1 + l2 * e2;
 #pragma unroll
       for (int e = 0; e < G::ELT; ++e) {
-        const float a2 = __shfl_xor(acc[j][e], o, kWave);
+        const float a2 = lane_xor<o>(acc[j][e]);
         acc[j][e] = acc[j][e] * e1 + a2 * e2;
       }
       mrun[j] = M;
     }
-  }
+  };
+  static_assert(G::LPR >= 8, "row groups are 8, 16, 32 or 64 lanes");
+  if constexpr (G::LPR <= 8) merge_rows(std::integral_constant<int, 8>{});
+  if constexpr (G::LPR <= 16) merge_rows(std::integral_constant<int, 16>{});
+  if constexpr (G::LPR <= 32) merge_rows(std::integral_constant<int, 32>{});
   if (rg == 0) {
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
@@ -398,33 +496,130 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
   __syncthreads();
   if (!is_last) return;
-  // (m, l) of every split -> LDS in one batch of independent loads
+  // Combine, in split order.  Every partial this block reads is requested
+  // in one batch of independent agent-scope loads before any is used (16
+  // bytes of o per split and thread, the (m, l) pairs of all splits), so
+  // the combine waits for memory once instead of once per split.  Thread
+  // (part, item): item = (head j, 4 columns), part p takes the splits
+  // p, p + PARTS, ...; the parts' sums are added in order through LDS.
+  constexpr int C4 = D / 4;
+  constexpr int ITEMS = GB * C4;
+  constexpr int PARTS = ITEMS >= kDecThreads ? 1 : (kDecThreads / ITEMS > 4 ? 4 : kDecThreads / ITEMS);
+  constexpr int IPT = (ITEMS * PARTS + kDecThreads - 1) / kDecThreads;  // items per thread
+  // splits per load batch and item (large grids have few splits; the
+  // registers would cost them occupancy)
+  constexpr int NB = IPT == 1 ? (LA ? 18 : 4) : (LA ? 9 : 2);
+  constexpr int MLN = (GB * kMaxSplits + kDecThreads - 1) / kDecThreads;
   __shared__ float cm[GB][kMaxSplits], cl[GB][kMaxSplits];
-  for (int idx = threadIdx.x; idx < nh * splits; idx += kDecThreads) {
-    const int j = idx / splits, ss = idx - j * splits;
-    const float* ml = ws_ml + (((size_t)b * hq + h0 + j) * splits + ss) * 2;
-    cm[j][ss] = ld_agent(&ml[0]);
-    cl[j][ss] = ld_agent(&ml[1]);
+  // o partials of this (sequence, head block): [nh][splits][D] fp32
+  const size_t o_base = ((size_t)b * hq + h0) * splits * D;
+  const i32x4 ors = make_buffer_rsrc(ws_o + o_base, (uint32_t)((size_t)nh * splits * D * 4));
+  constexpr int kAgent = 16;  // cache policy of an agent-scope load (sc1)
+  int it_j[IPT], it_c[IPT], it_p[IPT];
+  bool it_ok[IPT];
+  u32x4 ob[IPT][NB];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int t = threadIdx.x + i * kDecThreads;
+    it_p[i] = t / ITEMS;
+    const int item = t - it_p[i] * ITEMS;
+    it_j[i] = item / C4;
+    it_c[i] = item - it_j[i] * C4;
+    it_ok[i] = it_p[i] < PARTS && it_j[i] < nh;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int ss = it_p[i] + n * PARTS;
+      const int32_t off = it_ok[i] && ss < splits ? ((it_j[i] * splits + ss) * D + it_c[i] * 4) * 4
+                                                 : kBufferOob;
+      ob[i][n] = llvm_raw_buffer_load_v4i32(ors, off, 0, kAgent);
+    }
+  }
+  float mlv[MLN][2];
+#pragma unroll
+  for (int n = 0; n < MLN; ++n) {
+    const int idx = threadIdx.x + n * kDecThreads;
+    if (idx < nh * splits) {
+      const int j = idx / splits, ss = idx - j * splits;
+      const float* ml = ws_ml + (((size_t)b * hq + h0 + j) * splits + ss) * 2;
+      mlv[n][0] = ld_agent(&ml[0]);
+      mlv[n][1] = ld_agent(&ml[1]);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < MLN; ++n) {
+    const int idx = threadIdx.x + n * kDecThreads;
+    if (idx < nh * splits) {
+      const int j = idx / splits, ss = idx - j * splits;
+      cm[j][ss] = mlv[n][0];
+      cl[j][ss] = mlv[n][1];
+    }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < nh * D; idx += kDecThreads) {
-    const int j = idx / D, dd = idx - j * D;
-    const size_t bh = (size_t)b * hq + h0 + j;
+  float4* red4 = reinterpret_cast<float4*>(&red_o[0][0][0]);  // [PARTS][ITEMS]
+  float Lsum[IPT];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int j = it_ok[i] ? it_j[i] : 0;
+    // (unrolled so that the LDS reads of several splits are in flight at once)
     float M = -INFINITY;
+#pragma unroll 8
     for (int ss = 0; ss < splits; ++ss) M = fmaxf(M, cm[j][ss]);
     const float Mref = M == -INFINITY ? 0.f : M;
-    float L = 0.f, x = 0.f;
-#pragma unroll 16
-    for (int ss = 0; ss < splits; ++ss) {
-      const float e = __builtin_amdgcn_exp2f(cm[j][ss] - Mref);
-      L += e * cl[j][ss];
-      x += e * ld_agent(&ws_o[(bh * splits + ss) * D + dd]);
+    float L = 0.f;
+#pragma unroll 8
+    for (int ss = 0; ss < splits; ++ss) L += __builtin_amdgcn_exp2f(cm[j][ss] - Mref) * cl[j][ss];
+    Lsum[i] = L;
+    float4 x = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < splits; c0 += NB * PARTS) {
+      if (c0 > 0) {  // splits beyond the first batch (more than NB * PARTS)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          const int ss = c0 + it_p[i] + n * PARTS;
+          const int32_t off = it_ok[i] && ss < splits
+                                  ? ((it_j[i] * splits + ss) * D + it_c[i] * 4) * 4
+                                  : kBufferOob;
+          ob[i][n] = llvm_raw_buffer_load_v4i32(ors, off, 0, kAgent);
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int ss = c0 + it_p[i] + n * PARTS;
+        if (ss < splits) {
+          const float e = __builtin_amdgcn_exp2f(cm[j][ss] - Mref);
+          x.x += e * __uint_as_float(ob[i][n][0]);
+          x.y += e * __uint_as_float(ob[i][n][1]);
+          x.z += e * __uint_as_float(ob[i][n][2]);
+          x.w += e * __uint_as_float(ob[i][n][3]);
+        }
+      }
     }
-    x = L > 0.f ? x / L : 0.f;
+    if (it_p[i] < PARTS) red4[it_p[i] * ITEMS + (threadIdx.x + i * kDecThreads) % ITEMS] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    if (!it_ok[i] || it_p[i] != 0) continue;
+    const int item = threadIdx.x + i * kDecThreads;
+    float4 x = red4[item];
+#pragma unroll
+    for (int pp = 1; pp < PARTS; ++pp) {
+      const float4 y = red4[pp * ITEMS + item];
+      x.x += y.x;
+      x.y += y.y;
+      x.z += y.z;
+      x.w += y.w;
+    }
+    const float L = Lsum[i];
+    const size_t o = ((size_t)b * hq + h0 + it_j[i]) * D + it_c[i] * 4;
+    const float r4[4] = {L > 0.f ? x.x / L : 0.f, L > 0.f ? x.y / L : 0.f,
+                         L > 0.f ? x.z / L : 0.f, L > 0.f ? x.w / L : 0.f};
     if constexpr (std::is_same<T, float>::value) {
-      out[bh * D + dd] = x;
+      *reinterpret_cast<float4*>(out + o) = float4{r4[0], r4[1], r4[2], r4[3]};
     } else {
-      reinterpret_cast<uint16_t*>(out)[bh * D + dd] = (uint16_t)float_to_bf16_bits(x);
+      uint2 w;
+      w.x = float_to_bf16_bits(r4[0]) | (float_to_bf16_bits(r4[1]) << 16);
+      w.y = float_to_bf16_bits(r4[2]) | (float_to_bf16_bits(r4[3]) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + o) = w;
     }
   }
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -439,19 +634,15 @@ int launch_decode_t(const void* q, const void* k_new, const void* v_new, void* k
   float* ws_ml = (float*)((char*)workspace + p.counter_bytes);
   float* ws_o = ws_ml + (size_t)batch * hq * p.splits * 2;
   dim3 grid(p.splits, hkv * p.head_blocks, batch);
-  if (k_new == nullptr) {
-    hipLaunchKernelGGL((decode_split_kernel<D, T, GB, false>), grid, dim3(kDecThreads), 0, stream,
-                       (const T*)q, (T*)k_ring, (T*)v_ring, meta, window,
-                       ring_rows, hq, hkv, p.head_blocks, p.rows_per_split,
-                       scale * kLog2e, ws_o, ws_ml, p.splits, counters, (T*)out,
-                       (const T*)nullptr, (const T*)nullptr);
-  } else {
-    hipLaunchKernelGGL((decode_split_kernel<D, T, GB, true>), grid, dim3(kDecThreads), 0, stream,
-                       (const T*)q, (T*)k_ring, (T*)v_ring, meta, window,
-                       ring_rows, hq, hkv, p.head_blocks, p.rows_per_split,
-                       scale * kLog2e, ws_o, ws_ml, p.splits, counters, (T*)out,
-                       (const T*)k_new, (const T*)v_new);
-  }
+  const bool step = k_new != nullptr;
+  auto kern = step ? (p.load_all ? decode_split_kernel<D, T, GB, true, true>
+                                 : decode_split_kernel<D, T, GB, true, false>)
+                   : (p.load_all ? decode_split_kernel<D, T, GB, false, true>
+                                 : decode_split_kernel<D, T, GB, false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), 0, stream, (const T*)q, (T*)k_ring,
+                     (T*)v_ring, meta, window, ring_rows, hq, hkv, p.head_blocks,
+                     p.rows_per_split, scale * kLog2e, ws_o, ws_ml, p.splits, counters,
+                     (T*)out, (const T*)k_new, (const T*)v_new);
   return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
 }
 
@@ -486,6 +677,13 @@ DecodePlan plan_decode(int batch, int hq, int hkv, int d, int ring_rows) {
   if (rps < rps_min) rps = rps_min;
   p.rows_per_split = rps;
   p.splits = (ring_rows + rps - 1) / rps;
+  // latency-bound grids (no more blocks than CUs) load whole splits ahead
+  // of the ring state, at least 64 rows per block (two batches of 32)
+  p.load_all = units * p.splits <= kTargetBlocks;
+  if (p.load_all && p.rows_per_split < kLoadAllRows) {
+    p.rows_per_split = kLoadAllRows;
+    p.splits = (ring_rows + kLoadAllRows - 1) / kLoadAllRows;
+  }
   // [counters: one uint32 per (sequence, kv head, head block), then one per
   //  sequence (decode step), 256-byte padded][(m, l) per (sequence, query
   //  head, split)][o per ... and d]

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/swa.h"
 
 namespace swa {
@@ -68,18 +70,50 @@ __device__ __forceinline__ u32x4 buffer_load16(i32x4 rsrc, int32_t byte_offset) 
   return llvm_raw_buffer_load_v4i32(rsrc, byte_offset, 0, 0);
 }
 
-// Butterfly sum / max over groups of `width` consecutive lanes (power of 2).
+// Sum over groups of `width` consecutive lanes (power of 2, at most 64),
+// the same value in every lane of a group, without LDS: DPP within rows of
+// 16 lanes (neighbour in the quad, the other lane pair of the quad, the
+// mirrored half-row, the mirrored row; each step adds two values that are
+// already uniform over their halves, so every lane adds the same two
+// numbers), then the gfx950 row swaps for lanes l ^ 16 and l ^ 32.
 template <int width>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int o = width / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  static_assert(width >= 1 && width <= 64 && (width & (width - 1)) == 0, "power of 2");
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value,
+                                                      0xf, 0xf, false));
+  };
+  if constexpr (width >= 2) x += dpp(x, std::integral_constant<int, 0xb1>{});   // quad_perm 1,0,3,2
+  if constexpr (width >= 4) x += dpp(x, std::integral_constant<int, 0x4e>{});   // quad_perm 2,3,0,1
+  if constexpr (width >= 8) x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (width >= 16) x += dpp(x, std::integral_constant<int, 0x140>{}); // row_mirror
+  if constexpr (width >= 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  }
+  if constexpr (width >= 64) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  }
   return x;
 }
-template <int width>
-__device__ __forceinline__ float group_max(float x) {
-#pragma unroll
-  for (int o = width / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
+
+// x of lane l ^ o (o = 8, 16 or 32), without LDS.
+template <int o>
+__device__ __forceinline__ float lane_xor(float x) {
+  static_assert(o == 8 || o == 16 || o == 32, "lane distance");
+  if constexpr (o == 8) {
+    // l ^ 8 is l + 8 mod 16 within a row of 16: row_ror:8
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  } else {
+    // the row swaps return (x of the lower row, x of the upper row) in every
+    // lane of the pair of rows
+    const auto a = o == 16
+                       ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                       : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const bool upper = (__lane_id() & o) != 0;
+    return __uint_as_float(upper ? a[0] : a[1]);
+  }
 }
 
 }  // namespace swa

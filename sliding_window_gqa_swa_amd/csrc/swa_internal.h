@@ -27,6 +27,7 @@ struct DecodePlan {
   int head_blocks;      // ceil(g / heads_per_block)
   int splits;           // ring row ranges per (sequence, kv head)
   int rows_per_split;   // multiple of 32
+  bool load_all;        // rows loaded before the ring state is known (small grids)
   size_t counter_bytes;  // leading region of the workspace: split counters
   size_t workspace_bytes;
 };
