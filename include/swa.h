@@ -20,8 +20,8 @@
  *     call: SWA_BF16 (bfloat16) or SWA_F32 (float32).  Arithmetic is fp32
  *     (matrix-core products accumulate in fp32; bf16 outputs are rounded to
  *     nearest even).
- *   - head dimension d must be 64, 128, 256 or 512 (swa_prefill and
- *     swa_prefill_chunk also take 320); hq must be a multiple
+ *   - head dimension d must be 64, 128, 256, 320 or 512 (320: the
+ *     non-power-of-two size of [SDPA] Test plan); hq must be a multiple
  *     of hkv; query head h reads key/value head h / (hq / hkv), the head
  *     map of repeat_interleave ([SDPA] Summary) without materialising it.
  *   - stream is a hipStream_t (NULL = the null stream).  Every call only

@@ -104,15 +104,23 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
+
+// A row of CH 16-byte chunks is spread over LPR lanes (the power of two at
+// or above CH, at most 64); with CH not a power of two (head size 320:
+// 40 chunks of bf16, 80 of fp32) the lanes past the last chunk load
+// nothing and add zeros to the lane-group sums.
 template <int D, typename T>
 struct DecGeom {
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16 bytes
   static constexpr int CH = D / VEC;                // chunks per row
-  static constexpr int LPR = CH < kWave ? CH : kWave;  // lanes per row
-  static constexpr int CPL = CH / LPR;              // chunks per lane per row
+  static constexpr int LPR = pow2_at_least(CH) < kWave ? pow2_at_least(CH) : kWave;  // lanes per row
+  static constexpr int CPL = (CH + LPR - 1) / LPR;  // chunks per lane per row
   static constexpr int RPW = kWave / LPR;           // rows per wave step
   static constexpr int RPI = RPW * kDecWaves;       // rows per block step
   static constexpr int ELT = CPL * VEC;             // elements per lane
+  static constexpr bool FULL = CH % LPR == 0;       // every lane's chunks exist
+  static_assert(D % VEC == 0, "whole 16-byte chunks per row");
 };
 
 template <int D, typename T, int GB, bool STEP, bool LA>
@@ -178,12 +186,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       const int h = h0 + min(j, nh - 1);
 #pragma unroll
       for (int c = 0; c < G::CPL; ++c) {
+        const bool have = G::FULL || li + c * G::LPR < G::CH;
         const T* src = q + ((size_t)b * hq + h) * D + (size_t)(li + c * G::LPR) * G::VEC;
         if constexpr (kBf) {
-          qw[j][c] = *reinterpret_cast<const u32x4*>(src);
+          qw[j][c] = have ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
         } else {
           float f[G::VEC];
-          load_chunk<T>(src, f);
+          if (have) {
+            load_chunk<T>(src, f);
+          } else {
+#pragma unroll
+            for (int e = 0; e < G::VEC; ++e) f[e] = 0.f;
+          }
 #pragma unroll
           for (int e = 0; e < G::VEC; ++e) qv[j][c * G::VEC + e] = f[e] * qk_scale_log2;
         }
@@ -205,8 +219,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
     for (int c = 0; c < G::CPL; ++c) {
       const size_t e0 = new_off + (size_t)(li + c * G::LPR) * G::VEC;
-      kn_c[c] = *reinterpret_cast<const u32x4*>(k_new + e0);
-      vn_c[c] = *reinterpret_cast<const u32x4*>(v_new + e0);
+      const bool have = G::FULL || li + c * G::LPR < G::CH;
+      kn_c[c] = have ? *reinterpret_cast<const u32x4*>(k_new + e0) : u32x4{0u, 0u, 0u, 0u};
+      vn_c[c] = have ? *reinterpret_cast<const u32x4*>(v_new + e0) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -239,7 +254,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         ok[u] = r < r1;
 #pragma unroll
         for (int c = 0; c < G::CPL; ++c) {
-          const int32_t off = ok[u] ? row_byte + (li + c * G::LPR) * 16 : kBufferOob;
+          const bool have = G::FULL || li + c * G::LPR < G::CH;
+          const int32_t off = ok[u] && have ? row_byte + (li + c * G::LPR) * 16 : kBufferOob;
           kw[u][c] = buffer_load16(krs, off);
           vw[u][c] = buffer_load16(vrs, off);
         }
@@ -251,11 +267,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       ok[u] = r < r1 && a >= low && a <= high;
 #pragma unroll
       for (int c = 0; c < G::CPL; ++c) {
-        const int32_t off = ok[u] ? row_byte + (li + c * G::LPR) * 16 : kBufferOob;
+        const bool have = G::FULL || li + c * G::LPR < G::CH;
+        const int32_t off = ok[u] && have ? row_byte + (li + c * G::LPR) * 16 : kBufferOob;
         if (STEP && r == slot_p) {  // the appended row, from the step's input
           const size_t e0 = new_off + (size_t)(li + c * G::LPR) * G::VEC;
-          kw[u][c] = *reinterpret_cast<const u32x4*>(k_new + e0);
-          vw[u][c] = *reinterpret_cast<const u32x4*>(v_new + e0);
+          kw[u][c] = have ? *reinterpret_cast<const u32x4*>(k_new + e0) : u32x4{0u, 0u, 0u, 0u};
+          vw[u][c] = have ? *reinterpret_cast<const u32x4*>(v_new + e0) : u32x4{0u, 0u, 0u, 0u};
         } else {
           kw[u][c] = buffer_load16(krs, off);
           vw[u][c] = buffer_load16(vrs, off);
@@ -420,10 +437,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
 #pragma unroll
-      for (int c = 0; c < G::CPL; ++c)
+      for (int c = 0; c < G::CPL; ++c) {
+        if (!G::FULL && li + c * G::LPR >= G::CH) continue;  // no such chunk
 #pragma unroll
         for (int e = 0; e < G::VEC; ++e)
           red_o[wave][j][(li + c * G::LPR) * G::VEC + e] = acc[j][c * G::VEC + e];
+      }
       if (li == 0) {
         red_m[wave][j] = mrun[j];
         red_l[wave][j] = lrun[j];
@@ -710,11 +729,13 @@ int launch_decode(const void* q, const void* k_new, const void* v_new, void* k_r
     SWA_DEC_D(64, __bf16)
     SWA_DEC_D(128, __bf16)
     SWA_DEC_D(256, __bf16)
+    SWA_DEC_CASE(320, __bf16, 1) SWA_DEC_CASE(320, __bf16, 2) SWA_DEC_CASE(320, __bf16, 4)
     SWA_DEC_CASE(512, __bf16, 1) SWA_DEC_CASE(512, __bf16, 2) SWA_DEC_CASE(512, __bf16, 4)
   } else {
     SWA_DEC_D(64, float)
     SWA_DEC_D(128, float)
     SWA_DEC_D(256, float)
+    SWA_DEC_CASE(320, float, 1) SWA_DEC_CASE(320, float, 2) SWA_DEC_CASE(320, float, 4)
     SWA_DEC_CASE(512, float, 1) SWA_DEC_CASE(512, float, 2) SWA_DEC_CASE(512, float, 4)
   }
 #undef SWA_DEC_D

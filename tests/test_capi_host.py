@@ -94,13 +94,21 @@ def test_prefill_chunk_rejects(kw, code):
     assert _prefill_chunk(**kw) == code
 
 
-def test_head_320_is_a_prefill_size_only():
-    """d = 320 passes the prefill checks (an empty call returns OK after
-    them) and is refused by decode."""
+def test_head_320_passes_every_size_check():
+    """d = 320 passes the head-size checks of every entry point (each call
+    below fails on a later check, or is an empty no-op), and 160 does not."""
     assert _prefill_chunk(d=320, Tq=0, q=None, out=None) == _lib.SWA_OK
     assert _prefill_chunk(d=320, cuk=None) == _lib.SWA_EINVAL  # checked past the size
-    assert _decode(d=320) == _lib.SWA_EUNSUPPORTED
-    assert _decode_step(d=320) == _lib.SWA_EUNSUPPORTED
+    assert _decode(d=320, ws=None) == _lib.SWA_EWORKSPACE
+    assert _decode_step(d=320, ws=None) == _lib.SWA_EWORKSPACE
+    assert _noalloc(d=320, out=None) == _lib.SWA_EINVAL
+    L = _lib.lib()
+    assert L.swa_decode_workspace_bytes(2, 8, 4, 320, 1088) > 0
+    assert L.swa_cache_append(A, A, A, A, B, 0, 1088, 4, 320, 0, None) == _lib.SWA_OK
+    assert L.swa_cache_roll(A, A, B, 1024, 0, 1088, 4, 320, 0, None) == _lib.SWA_OK
+    for call in (_decode, _decode_step, _noalloc):
+        assert call(d=160) == _lib.SWA_EUNSUPPORTED
+    assert L.swa_decode_workspace_bytes(2, 8, 4, 160, 1088) == 0
 
 
 def test_prefill_chunk_empty_is_a_no_op():
@@ -269,7 +277,7 @@ def _noalloc(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=320), _lib.SWA_EUNSUPPORTED),
+    (dict(d=160), _lib.SWA_EUNSUPPORTED),
     (dict(R=1024), _lib.SWA_EINVAL),
     (dict(hq=3), _lib.SWA_EINVAL),
     (dict(out=None), _lib.SWA_EINVAL),

@@ -75,7 +75,8 @@ def _small_case(d, g, W, A, seed, B=6, steps=None):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d,g,W,A", [(64, 1, 40, 8), (128, 4, 100, 16), (256, 2, 50, 64),
-                                     (512, 2, 30, 8), (256, 8, 33, 5)])
+                                     (512, 2, 30, 8), (256, 8, 33, 5), (320, 2, 60, 16),
+                                     (320, 4, 31, 7)])
 def test_ring_decode_equals_linear_decode_every_step(dtype, d, g, W, A):
     require_gpu()
     case = _small_case(d, g, W, A, seed=d + g + W)
@@ -187,3 +188,27 @@ def test_decode_deterministic_and_position_independent_launch():
     q, out, seqs = run_far.step(0)
     assert host(run_far.meta)[:, 0].min() >= 30000
     assert_close(out, run_far.oracle(q, seqs), "bf16", "far positions")
+
+
+def test_decode_batched_d320_across_a_roll():
+    """Head size 320 (640-byte rows: 40 chunks over 64 lanes) on the large
+    grid of the batched decode: 64 sequences at seeded positions up to 8192,
+    W = 1024, 1088-row rings, 70 steps across the roll, sampled sequences
+    checked on every fifth step and all of them around the roll."""
+    require_gpu()
+    rng = si.rng_for(320)
+    B = 64
+    pos = rng.integers(1, 8192 + 1, size=B).astype(np.int32)
+    lo = np.array([rng.integers(0, min(63, int(p) - 1) + 1) for p in pos], np.int32)
+    case = si.DecodeCase("b64_d320", batch=B, hq=8, hkv=4, d=320, window=1024, ring_rows=1088,
+                         prompt_lens=pos, left_pad=lo, tail_lens=np.minimum(pos, 1024).astype(np.int32),
+                         steps=70, seed=320)
+    run = DecodeRun(case, "bf16")
+    for s in range(case.steps):
+        full = s in (0, 63, 64, 65, 69)
+        seqs = None if full else [(s * 8 + i) % B for i in range(8)]
+        q, out, seqs = run.step(s, seqs)
+        if full or s % 5 == 0:
+            log("decode b64 d320 step %d" % s)
+            assert_close(out[seqs], run.oracle(q, seqs), "bf16", "b64 d320 step %d" % s)
+    assert not (host(run.meta)[:, 3] < 0).any()
