@@ -133,6 +133,18 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const int32_t* __restrict
 // Descriptor of rows [r0, T) of a [T, heads, D] tensor at head h: row r of
 // the tile at byte offset r * heads * D * sizeof(T); rows at or past T fall
 // outside the buffer and load as zeros.
+// dk^T / dv^T product with the accumulator pinned to AGPRs.  At D = 512 a
+// dk/dv wave needs more than the 256 VGPRs: the builtin then gives the
+// accumulators AGPRs but moves all of them through VGPRs on every tile (a
+// D operand other than the C operand, then copies back).  Written by hand,
+// the hazards the compiler resolves for the builtin are handled here: the
+// B operand comes from vector ALU conversions just before, so the product
+// waits two wait states (s_nop 1); the accumulators are read by vector
+// instructions only after the loop, past mfma_drain().
+__device__ __forceinline__ void bw_mfma_aacc(floatx4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 template <typename T, int D>
 __device__ __forceinline__ i32x4 bw_rows_rsrc(const T* base, int r0, int h, int heads, int T_) {
   const T* p0 = base + ((size_t)r0 * heads + h) * D;
@@ -516,6 +528,8 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? bw_blocks_per_cu<D, T>() : 1)) 
   constexpr int QH = G::QREG / DS;         // S / dP fragments of this wave's d range
   constexpr int NDT = D / 16 / DS;         // 16-wide d blocks of this wave's accumulators
   constexpr int CPW = G::CPR / DS;         // 16-byte chunks of this wave's d range
+  // accumulators pinned to AGPRs (bf16 at D = 512, see bw_mfma_aacc)
+  constexpr bool kPinAcc = !kF32 && D >= 512;
   static_assert(DS == 1 || DS == 2, "one or two waves per key block");
   static_assert(KB == 1 || KB == 2, "one or two key blocks per wave");
   static_assert(G::QREG % DS == 0 && (D / 16) % DS == 0, "d splits evenly");
@@ -628,6 +642,15 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? bw_blocks_per_cu<D, T>() : 1)) 
 
   if (n > 0) load_tile(0, 0);
   for (int t = 0; t < n; ++t) {
+    if constexpr (kPinAcc) {
+      // the accumulators live in AGPRs across the whole loop (without this
+      // the compiler keeps them in VGPRs and copies them over for every
+      // product)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(dva[kb][dt]), "+a"(dka[kb][dt]));
+    }
     wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -777,14 +800,20 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? bw_blocks_per_cu<D, T>() : 1)) 
           const short8v qx = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
-            dva[kb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, dx), pf[kb], dva[kb][dt], 0, 0, 0);
-            dka[kb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qx), sf[kb], dka[kb][dt], 0, 0, 0);
+            if constexpr (kPinAcc) {
+              bw_mfma_aacc(dva[kb][dt], __builtin_bit_cast(bf16x8, dx), pf[kb]);
+              bw_mfma_aacc(dka[kb][dt], __builtin_bit_cast(bf16x8, qx), sf[kb]);
+            } else {
+              dva[kb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, dx), pf[kb], dva[kb][dt], 0, 0, 0);
+              dka[kb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qx), sf[kb], dka[kb][dt], 0, 0, 0);
+            }
           }
         }
       }
     }
   }
 
+  if constexpr (kPinAcc) mfma_drain();  // the stores below read the accumulators
   // ---- store dk = scale dk^T, dv = dv^T: 4 consecutive d of a key per lane --
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
