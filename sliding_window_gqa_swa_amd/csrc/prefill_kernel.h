@@ -967,8 +967,15 @@ void prefill_fwd_kernel(
     constexpr int NKS = BN / 32;    // 32-key P^T fragments per tile
     constexpr int NDT = D / 16;     // 16-wide head-dim blocks
     constexpr int QR = G::QREG;     // 32-wide head-dim steps of S^T
-    constexpr int NP = QR * (NKB / 2);  // K fragment pairs per tile (4 MFMAs each)
-    constexpr int NJ = NKS * (NDT / 2); // V^T fragment groups per tile (4 MFMAs each)
+    // head-dim steps and blocks that carry data: a head size padded in
+    // registers (DM < D, 320 computed as 384) runs no products over the
+    // padding (zeros in every K, V and Q fragment there, whose products add
+    // nothing and whose outputs are not stored)
+    constexpr bool kTrim = DM < D && DM % 32 == 0;
+    constexpr int QRE = kTrim ? DM / 32 : QR;     // S^T head-dim steps
+    constexpr int NDTE = kTrim ? DM / 16 : NDT;   // O^T head-dim blocks
+    constexpr int NP = QRE * (NKB / 2);  // K fragment pairs per tile (4 MFMAs each)
+    constexpr int NJ = NKS * (NDTE / 2); // V^T fragment groups per tile (4 MFMAs each)
     // LDS fragment lookahead: K pairs and V groups requested ahead of use
     constexpr int KLA = PfLookahead<D>::K, VLA = PfLookahead<D>::V;
     static_assert(NP >= 2 * ((G::UPT + 3) / 4), "a K fragment pair per load group");
@@ -1134,11 +1141,11 @@ void prefill_fwd_kernel(
         });
       });
     };
-    // V^T fragments of head-dim blocks (dt0, dt0 + 1), dt0 = 2 (j % (NDT/2)),
-    // of 32-key step j / (NDT/2)
+    // V^T fragments of head-dim blocks (dt0, dt0 + 1), dt0 = 2 (j % (NDTE/2)),
+    // of 32-key step j / (NDTE/2)
     auto issue_v = [&](auto jc, auto vstc, short4v (&dst)[4]) {
       constexpr int j = decltype(jc)::value, VST = decltype(vstc)::value;
-      constexpr int ks = j / (NDT / 2), dt0 = 2 * (j % (NDT / 2));
+      constexpr int ks = j / (NDTE / 2), dt0 = 2 * (j % (NDTE / 2));
       constexpr int OFF = VST + ks * 32 * ROWB + (dt0 / 8) * 256;
       dst[0] = lds_tr16_b64<OFF>(vaddr[dt0 % 8]);
       dst[1] = lds_tr16_b64<OFF + 16 * ROWB>(vaddr[dt0 % 8]);
@@ -1148,7 +1155,7 @@ void prefill_fwd_kernel(
     // read r (0..3) of issue_v, as a plain transposed LDS load (see issue_k1)
     auto issue_v1 = [&](auto jc, auto vstc, auto rc, short4v& dst) {
       constexpr int j = decltype(jc)::value, VST = decltype(vstc)::value, r = decltype(rc)::value;
-      constexpr int ks = j / (NDT / 2), dt0 = 2 * (j % (NDT / 2));
+      constexpr int ks = j / (NDTE / 2), dt0 = 2 * (j % (NDTE / 2));
       constexpr int OFF = VST + ks * 32 * ROWB + (dt0 / 8) * 256 + (r & 1) * 16 * ROWB;
       dst = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           reinterpret_cast<__attribute__((address_space(3))) short4v*>(
@@ -1157,7 +1164,7 @@ void prefill_fwd_kernel(
     // product (hh, mb) of V^T group j
     auto pv1 = [&](auto jc, auto hc, auto mbc, const short4v (&v4)[4], const bf16x8 (&pf)[MB][NKS]) {
       constexpr int j = decltype(jc)::value, hh = decltype(hc)::value, mb = decltype(mbc)::value;
-      constexpr int ks = j / (NDT / 2), dt0 = 2 * (j % (NDT / 2));
+      constexpr int ks = j / (NDTE / 2), dt0 = 2 * (j % (NDTE / 2));
       const short8v x8 = {v4[2 * hh][0], v4[2 * hh][1], v4[2 * hh][2], v4[2 * hh][3],
                           v4[2 * hh + 1][0], v4[2 * hh + 1][1], v4[2 * hh + 1][2], v4[2 * hh + 1][3]};
       const bf16x8 a = __builtin_bit_cast(bf16x8, x8);
@@ -1166,7 +1173,7 @@ void prefill_fwd_kernel(
     };
     auto pv_mfmas = [&](auto jc, const short4v (&v4)[4], const bf16x8 (&pf)[MB][NKS]) {
       constexpr int j = decltype(jc)::value;
-      constexpr int ks = j / (NDT / 2), dt0 = 2 * (j % (NDT / 2));
+      constexpr int ks = j / (NDTE / 2), dt0 = 2 * (j % (NDTE / 2));
       static_for<2>([&](auto hc) {
         constexpr int hh = decltype(hc)::value;
         const short8v x8 = {v4[2 * hh][0], v4[2 * hh][1], v4[2 * hh][2], v4[2 * hh][3],
@@ -1410,10 +1417,10 @@ void prefill_fwd_kernel(
         __builtin_amdgcn_sched_barrier(0);
         pv1(jc, I1, I1, vf[vs], pc);
         if constexpr (vmore) issue_v1(jn, VST, I3, vf[vn][3]);
-        if constexpr (!kAsmS && !kDiagRef && j % (NDT / 2) == NDT / 2 - 1) {
+        if constexpr (!kAsmS && !kDiagRef && j % (NDTE / 2) == NDTE / 2 - 1) {
           static_for<2>([&](auto mbc) {
             constexpr int mb = decltype(mbc)::value;
-            l_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[mb][j / (NDT / 2)], l_acc[mb], 0, 0, 0);
+            l_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pc[mb][j / (NDTE / 2)], l_acc[mb], 0, 0, 0);
           });
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1600,8 +1607,6 @@ void prefill_fwd_kernel(
         if constexpr (vmore) issue_v1(jn, VST, I3, vf[vn][3]);
         __builtin_amdgcn_sched_barrier(0);
       });
-      // stages that run past the last product slot
-
     };
     auto key_loop_as = [&]() __attribute__((always_inline)) {
       wait_vmcnt<0>();
@@ -1610,7 +1615,7 @@ void prefill_fwd_kernel(
       asm volatile("" ::: "memory");
       const bool a0 = active(0);
       if (a0) {
-        static_for<QR>([&](auto kkc) {
+        static_for<QRE>([&](auto kkc) {
           static_for<NKB / 2>([&](auto kpc) {
             bf16x8 kf[2];
             issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
@@ -1685,7 +1690,7 @@ void prefill_fwd_kernel(
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       if (active(0)) {
-        static_for<QR>([&](auto kkc) {
+        static_for<QRE>([&](auto kkc) {
           static_for<NKB / 2>([&](auto kpc) {
             bf16x8 kf[2];
             issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
@@ -1723,8 +1728,9 @@ void prefill_fwd_kernel(
     // or (kDiagRef) a non-finite output (any inf or NaN in O^T makes the sum
     // of its entries non-finite); one flag for the work-group.  kAsmS checks
     // the row sums alone: summing its 256 O^T accumulators here would cost
-    // the key loop its registers, and with every weight below 2^64 the
-    // accumulators stay finite for values below 2^64 in magnitude.
+    // the key loop its registers, and an accumulator is at most the row sum
+    // times the largest |v| of the row's keys: below 2^64 |v|, finite in
+    // fp32 for |v| < 2^63.
     auto out_of_range = [&]() __attribute__((always_inline)) {
       bool bad = false;
 #pragma unroll
@@ -1762,7 +1768,7 @@ void prefill_fwd_kernel(
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (active(tt)) {
-          static_for<QR>([&](auto kkc) {
+          static_for<QRE>([&](auto kkc) {
             static_for<NKB / 2>([&](auto kpc) {
               bf16x8 kf[2];
               issue_k(kkc, kpc, std::integral_constant<int, 0>{}, kf);
