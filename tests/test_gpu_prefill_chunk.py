@@ -33,6 +33,10 @@ def _ragged_chunks(rng, d):
     return cu_q, cu_k
 
 
+# (kv heads, query heads per kv head) per head size: groups of 2, 4 and 8
+# (4 or 8 heads share each K/V tile in one work-group)
+GROUPS = {64: (1, 8), 128: (1, 4), 256: (2, 2), 320: (1, 4), 512: (1, 4)}
+
 CASES = [(d, dt, m) for d in (64, 128, 256, 320, 512) for dt in ("bf16", "f32")
          for m in (CAUSAL, BLOCKWISE)]
 
@@ -43,7 +47,7 @@ def test_chunk_small_ragged(d, dtype, mode):
     rng = si.rng_for(30 * d + (dtype == "f32") * 7 + mode)
     cu_q, cu_k = _ragged_chunks(rng, d)
     Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
-    hkv, g = (2, 2) if d != 128 else (1, 4)
+    hkv, g = GROUPS[d]
     q = si.normal(rng, (Tq, hkv * g, d), dtype)
     k = si.normal(rng, (Tk, hkv, d), dtype)
     v = si.normal(rng, (Tk, hkv, d), dtype)

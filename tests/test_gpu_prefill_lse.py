@@ -24,6 +24,10 @@ pytestmark = pytest.mark.gpu
 
 CAUSAL, BLOCKWISE = si.CAUSAL, si.BLOCKWISE
 
+# (kv heads, query heads per kv head) per head size: groups of 2, 4 and 8
+# (4 or 8 heads share each K/V tile in one work-group)
+GROUPS = {64: (1, 8), 128: (1, 4), 256: (2, 2), 320: (1, 4), 512: (1, 4)}
+
 CASES = [(d, dtype, mode) for d in (64, 128, 256, 320, 512) for dtype in ("bf16", "f32")
          for mode in (CAUSAL, BLOCKWISE)]
 
@@ -34,7 +38,7 @@ def test_prefill_lse(d, dtype, mode):
     rng = si.rng_for(55 * d + (dtype == "f32") * 5 + mode)
     T = 613 if d <= 256 else 389
     cu = np.array([0, 1, 130, 130, 401, T], np.int32) if d <= 256 else np.array([0, 77, 78, 300, T], np.int32)
-    hkv, g = (2, 2) if d != 128 else (1, 4)
+    hkv, g = GROUPS[d]
     hq = hkv * g
     q, k, v = (si.normal(rng, s, dtype) for s in [(T, hq, d), (T, hkv, d), (T, hkv, d)])
     ids = _ids_for(T, cu, 7 * d + mode) if mode == BLOCKWISE else None
