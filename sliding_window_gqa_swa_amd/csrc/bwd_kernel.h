@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256, (BN_ > 0 ? 2 : bw_blocks_per_cu<D, T>())) void
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ o, const T* __restrict__ dout, const int32_t* __restrict__ lo_a,
     const int32_t* __restrict__ hi_a, const float* __restrict__ lse_in, int Ttot, int hq,
-    int hkv, float c_scale, float scale, int ntiles, int nwork, int per_xcd, T* __restrict__ dq,
+    int hkv, int W, float c_scale, float scale, int ntiles, int nwork, int per_xcd, T* __restrict__ dq,
     float* __restrict__ lse_out, float* __restrict__ delta_out) {
   using G = BwGeom<D, T, BN_>;
   using TR = typename G::TR;
@@ -199,6 +199,23 @@ __global__ __launch_bounds__(256, (BN_ > 0 ? 2 : bw_blocks_per_cu<D, T>())) void
   // (malformed offsets could give kmax < kt0: one tile is still visited,
   // so that every issued load is waited for)
   const int nk = max((kmax - kt0) / BN + 1, 1);
+  // Visit order: at D <= 128, where the window cuts the work-group's keys
+  // (its first row's interval starts W-1 keys back, not at a document
+  // start), visit t reads key tile (t + rot) mod nk, with rot chosen so that
+  // the absolute index of that tile is congruent to t mod nk.  The
+  // work-groups of neighbouring query tiles running side by side on an XCD
+  // (all with the same nk) then read the same K/V tile at the same visit
+  // and share it in that XCD's L2, instead of each streaming its own
+  // shifted window through it.  dq is a sum over keys, so the order
+  // changes only its rounding.  (At D = 512 the same order cut this
+  // kernel's HBM reads from 7.4 to 2.6 GB on the 16K-token shape but made
+  // it about 1% slower: the natural order is kept there.)
+  const bool cut = D <= 128 && W > 0 && q0 - kmin == W - 1;
+  const int rot = cut ? (nk - (kt0 / BN) % nk) % nk : 0;
+  auto ktile = [&](int t) {
+    const int u = t + rot;
+    return kt0 + (u >= nk ? u - nk : u) * BN;
+  };
 
   int row_i[MB], row_lo[MB];
   unsigned row_rng[MB];
@@ -328,11 +345,11 @@ __global__ __launch_bounds__(256, (BN_ > 0 ? 2 : bw_blocks_per_cu<D, T>())) void
     m_run[mb] = -INFINITY;
     l_part[mb] = 0.f;
   }
-  load_tile(kt0, 0, false);
+  load_tile(ktile(0), 0, false);
   for (int it = 0; it < nk; ++it) {
-    const int k0 = kt0 + it * BN;
+    const int k0 = ktile(it);
     sync_tile();
-    if (it + 1 < nk) load_tile(k0 + BN, (it + 1) & 1, false);
+    if (it + 1 < nk) load_tile(ktile(it + 1), (it + 1) & 1, false);
     if (!(wact && k0 <= whi && k0 + BN - 1 >= wlo)) continue;  // no key of the wave's rows
     const T* Kb = reinterpret_cast<const T*>(&ring[it & 1][0]);
     floatx4 s[MB][BN / 16];
@@ -384,11 +401,11 @@ __global__ __launch_bounds__(256, (BN_ > 0 ? 2 : bw_blocks_per_cu<D, T>())) void
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) acc[mb][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  load_tile(kt0, 0, true);
+  load_tile(ktile(0), 0, true);
   for (int it = 0; it < nk; ++it) {
-    const int k0 = kt0 + it * BN;
+    const int k0 = ktile(it);
     sync_tile();
-    if (it + 1 < nk) load_tile(k0 + BN, (it + 1) & 1, true);
+    if (it + 1 < nk) load_tile(ktile(it + 1), (it + 1) & 1, true);
     if (!(wact && k0 <= whi && k0 + BN - 1 >= wlo)) continue;
     const T* Kb = reinterpret_cast<const T*>(&ring[it & 1][0]);
     const T* Vb = reinterpret_cast<const T*>(&ring[it & 1][TB]);
@@ -517,7 +534,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? bw_blocks_per_cu<D, T>() : 1)) 
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ dlt,
     const int32_t* __restrict__ lo_a, const int32_t* __restrict__ hi_a, int Ttot, int hq,
-    int hkv, float c_scale, float scale, int nktiles, int nwork, int per_xcd,
+    int hkv, int W, float c_scale, float scale, int nktiles, int nwork, int per_xcd,
     T* __restrict__ dk, T* __restrict__ dv) {
   using G = BwGeom<D, T, BQ_, NW>;
   using TR = typename G::TR;
@@ -583,6 +600,23 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? bw_blocks_per_cu<D, T>() : 1)) 
   i_max = __builtin_amdgcn_readfirstlane(i_max);
   const int ntq = i_max >= i_min ? (i_max - i_min) / BQ + 1 : 0;
   const int n = g * ntq;
+  // Visit t: head t / ntq of the group, query tile (t mod ntq + rot) mod ntq
+  // of the range.  At D <= 128, where the window cuts the rows (the last
+  // row admitting the work-group's last key is W-1 rows on, not a document
+  // end), rot is chosen as in the dq kernel (absolute tile index congruent
+  // to the visit), so that the work-groups of neighbouring key tiles read
+  // the same Q / dout tile at the same visit (16K tokens, window 4K, D =
+  // 128: about 4% off the whole backward with the dq kernel's rotation).
+  // At larger D it stays 0: the natural order already keeps the band of
+  // query tiles the work-groups of an XCD read in its L2, and aligning them
+  // raised this kernel's HBM reads from 2.6 to 7.0 GB on the 16K-token
+  // D = 512 shape (measured).
+  const bool cut = D <= 128 && W > 0 && ntq > 0 && i_max - j1 == W - 1;
+  const int rot = cut ? (ntq - (i_min / BQ) % ntq) % ntq : 0;
+  auto qtile_row = [&](int t) {
+    const int u = (t - (t / ntq) * ntq) + rot;
+    return i_min + (u >= ntq ? u - ntq : u) * BQ;
+  };
 
   // K and V fragments of this lane's keys (B operands of S = Q K^T, dP = dout V^T)
   using QF = typename std::conditional<kF32, floatx4, bf16x8>::type;
@@ -610,7 +644,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? bw_blocks_per_cu<D, T>() : 1)) 
   const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(&ring[0][0]);
   auto load_tile = [&](int t, int stage) {
     const int h = kvh * g + t / ntq;
-    const int i0 = i_min + (t - (t / ntq) * ntq) * BQ;
+    const int i0 = qtile_row(t);
     const uint32_t sb = ring_base + stage * STAGE;
     const uint32_t ql = sb + wave_u * G::UPT * 1024;
     const i32x4 rq = bw_rows_rsrc<T, D>(q, i0, h, hq, Ttot);
@@ -663,7 +697,7 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? bw_blocks_per_cu<D, T>() : 1)) 
     const float* dlt_s = reinterpret_cast<const float*>(st + 2 * TB + 1024);
     const int* lo_s = reinterpret_cast<const int*>(st + 2 * TB + 2048);
     const int* hi_s = reinterpret_cast<const int*>(st + 2 * TB + 3072);
-    const int i0 = i_min + (t - (t / ntq) * ntq) * BQ;
+    const int i0 = qtile_row(t);
     const int nrow = min(BQ, Ttot - i0);
     // rows of the tile admit a key of this wave? (monotone bounds; uniform
     // over the waves that share the keys)

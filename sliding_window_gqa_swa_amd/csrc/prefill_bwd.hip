@@ -52,7 +52,7 @@ int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
     if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
     hipLaunchKernelGGL((bwd_dq_kernel<D, T, MB, DQBN>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.out,
-                       (const T*)a.dout, w.lo, w.hi, a.lse, T_, a.hq, a.hkv, c, a.scale, ntiles,
+                       (const T*)a.dout, w.lo, w.hi, a.lse, T_, a.hq, a.hkv, a.window, c, a.scale, ntiles,
                        (int)nwork, (int)per_xcd, (T*)a.dq, w.lse, w.delta);
   }
   {
@@ -65,7 +65,7 @@ int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, C::DS, C::KB, C::BQ, C::NW>), dim3((unsigned)(8 * per_xcd)),
                        dim3(64 * C::NW), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
-                       w.lse, w.delta, w.lo, w.hi, T_, a.hq, a.hkv, c, a.scale, nkt, (int)nwork,
+                       w.lse, w.delta, w.lo, w.hi, T_, a.hq, a.hkv, a.window, c, a.scale, nkt, (int)nwork,
                        (int)per_xcd, (T*)a.dk, (T*)a.dv);
   }
   return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
