@@ -20,8 +20,9 @@
  *     call: SWA_BF16 (bfloat16) or SWA_F32 (float32).  Arithmetic is fp32
  *     (matrix-core products accumulate in fp32; bf16 outputs are rounded to
  *     nearest even).
- *   - head dimension d must be 64, 128, 256, 320 or 512 (320: the
- *     non-power-of-two size of [SDPA] Test plan); hq must be a multiple
+ *   - head dimension d must be a multiple of 64 from 64 to 512 (64, 128,
+ *     192, 256, 320, 384, 448, 512; [SDPA] Test plan exercises the
+ *     non-power-of-two size 320), else SWA_EUNSUPPORTED; hq must be a multiple
  *     of hkv; query head h reads key/value head h / (hq / hkv), the head
  *     map of repeat_interleave ([SDPA] Summary) without materialising it.
  *   - stream is a hipStream_t (NULL = the null stream).  Every call only
@@ -163,7 +164,7 @@ SWA_API int swa_prefill_chunk(const void* q, const void* k, const void* v,
  * (float32 [hq, total_tokens], 4-byte aligned), or NULL, in which case the
  * backward recomputes it with one more pass over the keys.  Every output element is written exactly once,
  * without atomics: the result is deterministic.
- *   d: 64, 128, 256, 320 or 512.
+ *   d: a multiple of 64 from 64 to 512, as everywhere.
  *   workspace: device memory of at least
  *   swa_prefill_backward_workspace_bytes(total_tokens, hq) bytes, 16-byte
  *   aligned, owned by the caller, contents on entry ignored (per-row

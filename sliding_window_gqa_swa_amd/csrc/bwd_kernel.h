@@ -71,64 +71,9 @@ constexpr int bw_blocks_per_cu() {
   return (!std::is_same<T, float>::value && D <= 128) ? 2 : 1;
 }
 
-// Per-row key intervals: lo[i] = max(doc start, i - W + 1) (doc start when
-// W <= 0); hi[i] = i, or the last token of i's image run when i is an image
-// token in blockwise mode (a run: consecutive tokens of one document with
-// the same non-negative id).  One wave per 64 rows; a run that continues
-// past the wave's rows is followed 64 tokens per step.
-__global__ __launch_bounds__(256) void bwd_rows_kernel(const int32_t* __restrict__ cu, int ndocs,
-                                                       const int32_t* __restrict__ ids, int W,
-                                                       int mode, int T, int32_t* __restrict__ lo_out,
-                                                       int32_t* __restrict__ hi_out) {
-  const int lane = threadIdx.x & 63;
-  const int base = ((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * 64;
-  if (base >= T) return;  // uniform per wave
-  const int i = base + lane;
-  const bool valid = i < T;
-  int ds = i, de = i + 1;
-  if (valid) {
-    int a = 0, b = ndocs + 1;  // first d with cu[d] > i
-    while (a < b) {
-      const int m = (a + b) >> 1;
-      if (cu[m] > i) b = m; else a = m + 1;
-    }
-    const int d = a - 1;
-    if (d >= 0 && d < ndocs) {
-      ds = cu[d];
-      de = cu[d + 1];
-    }
-    ds = min(max(ds, 0), i);  // clamps against malformed offsets
-    de = max(min(de, T), i + 1);
-  }
-  const int lo = W > 0 ? max(ds, i - W + 1) : ds;
-  int hi = i;
-  if (mode == SWA_BLOCKWISE) {
-    const int id = valid ? ids[i] : -1;
-    const bool last = !valid || i + 1 >= de || ids[i + 1] != id;
-    const unsigned long long bal = __ballot(last);
-    const unsigned long long mine = bal & (~0ull << lane);
-    int end = mine ? base + __builtin_ctzll(mine) : -1;
-    // lanes with no run end at or after them share lane 63's open run
-    if (__ballot(valid && id >= 0 && end < 0)) {
-      const int rid = __builtin_amdgcn_readlane(id, 63);
-      const int rde = __builtin_amdgcn_readlane(de, 63);
-      int t0 = base + 64, found = -1;
-      while (found < 0) {  // ends: t >= rde stops the run
-        const int t = t0 + lane;
-        const bool stop = t >= rde || ids[t] != rid;
-        const unsigned long long m = __ballot(stop);
-        if (m) found = t0 + __builtin_ctzll(m) - 1;
-        t0 += 64;
-      }
-      if (end < 0) end = found;
-    }
-    if (valid && id >= 0) hi = end;
-  }
-  if (valid) {
-    lo_out[i] = lo;
-    hi_out[i] = hi;
-  }
-}
+// Per-row key intervals (bwd_rows_kernel, prefill_bwd.hip): lo[i] and
+// hi[i] of every row, read by both kernels below.
+
 
 // Descriptor of rows [r0, T) of a [T, heads, D] tensor at head h: row r of
 // the tile at byte offset r * heads * D * sizeof(T); rows at or past T fall

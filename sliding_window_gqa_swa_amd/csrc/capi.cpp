@@ -16,9 +16,8 @@ namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// head dimensions of every entry point (320: the non-power-of-two size of
-// the pages' test plan)
-bool supported_d(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 320 || d == 512; }
+// head dimensions of every entry point (swa::head_dim_supported)
+bool supported_d(int32_t d) { return swa::head_dim_supported(d); }
 bool supported_prefill_d(int32_t d) { return supported_d(d); }
 
 size_t elem_size(int32_t dtype) { return dtype == SWA_BF16 ? 2 : 4; }

@@ -725,19 +725,28 @@ int launch_decode(const void* q, const void* k_new, const void* v_new, void* k_r
                                         p, stream);
 #define SWA_DEC_D(DD, TT) \
   SWA_DEC_CASE(DD, TT, 1) SWA_DEC_CASE(DD, TT, 2) SWA_DEC_CASE(DD, TT, 4) SWA_DEC_CASE(DD, TT, 8)
+  // (head sizes above 256 take at most 4 heads per block: heads_per_block_for)
+#define SWA_DEC_D4(DD, TT) SWA_DEC_CASE(DD, TT, 1) SWA_DEC_CASE(DD, TT, 2) SWA_DEC_CASE(DD, TT, 4)
   if (dtype == SWA_BF16) {
     SWA_DEC_D(64, __bf16)
     SWA_DEC_D(128, __bf16)
+    SWA_DEC_D(192, __bf16)
     SWA_DEC_D(256, __bf16)
-    SWA_DEC_CASE(320, __bf16, 1) SWA_DEC_CASE(320, __bf16, 2) SWA_DEC_CASE(320, __bf16, 4)
-    SWA_DEC_CASE(512, __bf16, 1) SWA_DEC_CASE(512, __bf16, 2) SWA_DEC_CASE(512, __bf16, 4)
+    SWA_DEC_D4(320, __bf16)
+    SWA_DEC_D4(384, __bf16)
+    SWA_DEC_D4(448, __bf16)
+    SWA_DEC_D4(512, __bf16)
   } else {
     SWA_DEC_D(64, float)
     SWA_DEC_D(128, float)
+    SWA_DEC_D(192, float)
     SWA_DEC_D(256, float)
-    SWA_DEC_CASE(320, float, 1) SWA_DEC_CASE(320, float, 2) SWA_DEC_CASE(320, float, 4)
-    SWA_DEC_CASE(512, float, 1) SWA_DEC_CASE(512, float, 2) SWA_DEC_CASE(512, float, 4)
+    SWA_DEC_D4(320, float)
+    SWA_DEC_D4(384, float)
+    SWA_DEC_D4(448, float)
+    SWA_DEC_D4(512, float)
   }
+#undef SWA_DEC_D4
 #undef SWA_DEC_D
 #undef SWA_DEC_CASE
   return SWA_EUNSUPPORTED;

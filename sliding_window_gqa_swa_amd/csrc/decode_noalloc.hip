@@ -85,7 +85,7 @@ SWA_API int swa_decode_step_noalloc(const void* q, const void* k_new, const void
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return SWA_EINVAL;
   if (batch < 0 || window < 1 || ring_rows <= window) return SWA_EINVAL;
   if (ring_rows > SWA_MAX_RING_ROWS) return SWA_EUNSUPPORTED;
-  if (!(d == 64 || d == 128 || d == 256 || d == 320 || d == 512)) return SWA_EUNSUPPORTED;
+  if (!swa::head_dim_supported(d)) return SWA_EUNSUPPORTED;
   if (dtype != SWA_BF16 && dtype != SWA_F32) return SWA_EUNSUPPORTED;
   if (batch == 0) return SWA_OK;
   if (!ok16(q) || !ok16(k_new) || !ok16(v_new) || !ok16(k_ring) || !ok16(v_ring) ||

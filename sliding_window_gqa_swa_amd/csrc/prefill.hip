@@ -9,10 +9,16 @@ int launch_prefill(const PrefillArgs& a) {
       return launch_prefill_d64(a);
     case 128:
       return launch_prefill_d128(a);
+    case 192:
+      return launch_prefill_d192(a);
     case 256:
       return launch_prefill_d256(a);
     case 320:
       return launch_prefill_d320(a);
+    case 384:
+      return launch_prefill_d384(a);
+    case 448:
+      return launch_prefill_d448(a);
     case 512:
       return launch_prefill_d512(a);
     default:

@@ -1,8 +1,5 @@
 // prefill_bwd.hip -- host launchers of the prefill backward (bwd_kernel.h).
-#include "bwd_kernel.h"
-#include "swa_internal.h"
-
-#include <algorithm>
+#include "prefill_bwd_launch.h"
 
 namespace swa {
 
@@ -10,68 +7,67 @@ namespace {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// 16-row blocks per dq wave: one at every head size (at D = 128 the 16-row
-// wave lets two work-groups share each CU: 147 us against 187 us for
-// 32-row waves with one work-group per CU, measured; larger D have no
-// registers for 32 rows)
-template <int D, typename T>
-constexpr int dq_mb() {
-  return 1;
-}
-
-// dk/dv kernel shape per head size: DS waves per key block (each one part
-// of d), KB 16-key blocks per wave, BQ query rows per tile; chosen so that
-// one wave's fragments and accumulators fit its registers and the stages
-// plus the partial-sum exchange fit the LDS
-template <int D, typename T>
-struct DkdvCfg {
-  static constexpr bool F = std::is_same<T, float>::value;
-  static constexpr int DS = F ? (D >= 256 ? 2 : 1) : (D >= 512 || D == 256 ? 2 : 1);
-  // (two key blocks per wave halve the LDS reads per product but cost the
-  // second wave per SIMD: 241 vs 197 us at D = 128, measured)
-  static constexpr int KB = 1;
-  static constexpr int BQ = (!F && D <= 256) ? 32 : 0;  // 0: the default tile
-  static constexpr int NW = (!F && D == 256) ? 8 : 4;   // waves per work-group
-};
-
-template <int D, typename T>
-int launch_bwd_cfg(const PrefillBwdArgs& a, const BwdWorkspace& w) {
-  constexpr int MB = dq_mb<D, T>();
-  constexpr int BM = 64 * MB;
-  // dq key tile: 32 keys at bf16 D = 256 (a 64 KB ring: two work-groups
-  // per CU), else the default
-  constexpr int DQBN = (!std::is_same<T, float>::value && D <= 256) ? 32 : 0;
-  const int T_ = a.total;
-  hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((T_ + 255) / 256)), dim3(256), 0, a.stream,
-                     a.cu, a.num_docs, a.ids, a.window, a.mode, T_, w.lo, w.hi);
-  const float c = a.scale * kPrefillLog2e;
-  {
-    const int ntiles = (T_ + BM - 1) / BM;
-    const long long nwork = (long long)ntiles * a.hq;
-    const long long per_xcd = (nwork + 7) / 8;
-    if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, T, MB, DQBN>), dim3((unsigned)(8 * per_xcd)), dim3(256), 0,
-                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.out,
-                       (const T*)a.dout, w.lo, w.hi, a.lse, T_, a.hq, a.hkv, a.window, c, a.scale, ntiles,
-                       (int)nwork, (int)per_xcd, (T*)a.dq, w.lse, w.delta);
-  }
-  {
-    using C = DkdvCfg<D, T>;
-    constexpr int BK = 16 * C::KB * C::NW / C::DS;  // keys per work-group
-    const int nkt = (T_ + BK - 1) / BK;
-    const long long nwork = (long long)nkt * a.hkv;
-    const long long per_xcd = (nwork + 7) / 8;
-    if (8 * per_xcd > 0x7fffffffLL) return SWA_EUNSUPPORTED;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, T, C::DS, C::KB, C::BQ, C::NW>), dim3((unsigned)(8 * per_xcd)),
-                       dim3(64 * C::NW), 0,
-                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
-                       w.lse, w.delta, w.lo, w.hi, T_, a.hq, a.hkv, a.window, c, a.scale, nkt, (int)nwork,
-                       (int)per_xcd, (T*)a.dk, (T*)a.dv);
-  }
-  return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
-}
-
 }  // namespace
+
+// Per-row key intervals: lo[i] = max(doc start, i - W + 1) (doc start when
+// W <= 0); hi[i] = i, or the last token of i's image run when i is an image
+// token in blockwise mode (a run: consecutive tokens of one document with
+// the same non-negative id).  One wave per 64 rows; a run that continues
+// past the wave's rows is followed 64 tokens per step.
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const int32_t* __restrict__ cu, int ndocs,
+                                                       const int32_t* __restrict__ ids, int W,
+                                                       int mode, int T, int32_t* __restrict__ lo_out,
+                                                       int32_t* __restrict__ hi_out) {
+  const int lane = threadIdx.x & 63;
+  const int base = ((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * 64;
+  if (base >= T) return;  // uniform per wave
+  const int i = base + lane;
+  const bool valid = i < T;
+  int ds = i, de = i + 1;
+  if (valid) {
+    int a = 0, b = ndocs + 1;  // first d with cu[d] > i
+    while (a < b) {
+      const int m = (a + b) >> 1;
+      if (cu[m] > i) b = m; else a = m + 1;
+    }
+    const int d = a - 1;
+    if (d >= 0 && d < ndocs) {
+      ds = cu[d];
+      de = cu[d + 1];
+    }
+    ds = min(max(ds, 0), i);  // clamps against malformed offsets
+    de = max(min(de, T), i + 1);
+  }
+  const int lo = W > 0 ? max(ds, i - W + 1) : ds;
+  int hi = i;
+  if (mode == SWA_BLOCKWISE) {
+    const int id = valid ? ids[i] : -1;
+    const bool last = !valid || i + 1 >= de || ids[i + 1] != id;
+    const unsigned long long bal = __ballot(last);
+    const unsigned long long mine = bal & (~0ull << lane);
+    int end = mine ? base + __builtin_ctzll(mine) : -1;
+    // lanes with no run end at or after them share lane 63's open run
+    if (__ballot(valid && id >= 0 && end < 0)) {
+      const int rid = __builtin_amdgcn_readlane(id, 63);
+      const int rde = __builtin_amdgcn_readlane(de, 63);
+      int t0 = base + 64, found = -1;
+      while (found < 0) {  // ends: t >= rde stops the run
+        const int t = t0 + lane;
+        const bool stop = t >= rde || ids[t] != rid;
+        const unsigned long long m = __ballot(stop);
+        if (m) found = t0 + __builtin_ctzll(m) - 1;
+        t0 += 64;
+      }
+      if (end < 0) end = found;
+    }
+    if (valid && id >= 0) hi = end;
+  }
+  if (valid) {
+    lo_out[i] = lo;
+    hi_out[i] = hi;
+  }
+}
+
 
 size_t bwd_workspace_bytes(int total, int hq) {
   const size_t t = (size_t)(total > 0 ? total : 0);
@@ -96,23 +92,31 @@ BwdWorkspace bwd_workspace(void* base, int total, int hq) {
 
 bool bwd_supported(int d, int dtype) {
   (void)dtype;  // (fp32 at D = 512: the dq kernel spills 27 registers, correct but slow)
-  return d == 64 || d == 128 || d == 256 || d == 320 || d == 512;
+  return head_dim_supported(d);
 }
 
 int launch_prefill_bwd(const PrefillBwdArgs& a) {
   const BwdWorkspace w = bwd_workspace(a.workspace, a.total, a.hq);
-  const bool bf = a.dtype == SWA_BF16;
+  const int T_ = a.total;
+  hipLaunchKernelGGL(bwd_rows_kernel, dim3((unsigned)((T_ + 255) / 256)), dim3(256), 0, a.stream,
+                     a.cu, a.num_docs, a.ids, a.window, a.mode, T_, w.lo, w.hi);
   switch (a.d) {
     case 64:
-      return bf ? launch_bwd_cfg<64, __bf16>(a, w) : launch_bwd_cfg<64, float>(a, w);
+      return launch_bwd_d64(a, w);
     case 128:
-      return bf ? launch_bwd_cfg<128, __bf16>(a, w) : launch_bwd_cfg<128, float>(a, w);
+      return launch_bwd_d128(a, w);
+    case 192:
+      return launch_bwd_d192(a, w);
     case 256:
-      return bf ? launch_bwd_cfg<256, __bf16>(a, w) : launch_bwd_cfg<256, float>(a, w);
+      return launch_bwd_d256(a, w);
     case 320:
-      return bf ? launch_bwd_cfg<320, __bf16>(a, w) : launch_bwd_cfg<320, float>(a, w);
+      return launch_bwd_d320(a, w);
+    case 384:
+      return launch_bwd_d384(a, w);
+    case 448:
+      return launch_bwd_d448(a, w);
     case 512:
-      return bf ? launch_bwd_cfg<512, __bf16>(a, w) : launch_bwd_cfg<512, float>(a, w);
+      return launch_bwd_d512(a, w);
     default:
       return SWA_EUNSUPPORTED;
   }

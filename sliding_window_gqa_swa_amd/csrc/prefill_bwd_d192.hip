@@ -1,0 +1,10 @@
+// prefill_bwd_d192.hip -- prefill backward instantiations for head dimension 192.
+#include "prefill_bwd_launch.h"
+
+namespace swa {
+
+int launch_bwd_d192(const PrefillBwdArgs& a, const BwdWorkspace& w) {
+  return a.dtype == SWA_BF16 ? launch_bwd_cfg<192, __bf16>(a, w) : launch_bwd_cfg<192, float>(a, w);
+}
+
+}  // namespace swa

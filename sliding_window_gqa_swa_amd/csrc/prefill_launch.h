@@ -52,8 +52,11 @@ int launch_prefill_cfg(const PrefillArgs& a) {
 // One translation unit per head dimension keeps compile times parallel.
 int launch_prefill_d64(const PrefillArgs& a);
 int launch_prefill_d128(const PrefillArgs& a);
+int launch_prefill_d192(const PrefillArgs& a);
 int launch_prefill_d256(const PrefillArgs& a);
 int launch_prefill_d320(const PrefillArgs& a);
+int launch_prefill_d384(const PrefillArgs& a);
+int launch_prefill_d448(const PrefillArgs& a);
 int launch_prefill_d512(const PrefillArgs& a);
 
 }  // namespace swa

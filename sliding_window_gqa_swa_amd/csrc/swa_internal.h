@@ -7,6 +7,13 @@
 
 namespace swa {
 
+// Head sizes of every entry point: the multiples of 64 up to 512.  (Rows of
+// 64 elements are whole 16-byte chunks in a count the LDS tile layout takes
+// at every element size; a size with no schedule of its own runs on the
+// pipelined prefill loop of the next multiple of 128, with no products over
+// the padding.)
+inline bool head_dim_supported(int d) { return d >= 64 && d <= 512 && d % 64 == 0; }
+
 // Ring cache (byte copies; row_bytes = d * element size, a multiple of 16).
 int launch_ring_append(const void* k_new, const void* v_new, void* k_ring,
                        void* v_ring, int32_t* meta, int batch, int ring_rows,

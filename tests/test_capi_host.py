@@ -55,7 +55,8 @@ def _prefill(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(d=100), _lib.SWA_EUNSUPPORTED),
     (dict(d=96), _lib.SWA_EUNSUPPORTED),
-    (dict(d=384), _lib.SWA_EUNSUPPORTED),
+    (dict(d=576), _lib.SWA_EUNSUPPORTED),
+    (dict(d=0), _lib.SWA_EUNSUPPORTED),
     (dict(dtype=7), _lib.SWA_EUNSUPPORTED),
     (dict(mode=2), _lib.SWA_EUNSUPPORTED),
     (dict(hq=3, hkv=2), _lib.SWA_EINVAL),
@@ -94,21 +95,33 @@ def test_prefill_chunk_rejects(kw, code):
     assert _prefill_chunk(**kw) == code
 
 
-def test_head_320_passes_every_size_check():
-    """d = 320 passes the head-size checks of every entry point (each call
-    below fails on a later check, or is an empty no-op), and 160 does not."""
-    assert _prefill_chunk(d=320, Tq=0, q=None, out=None) == _lib.SWA_OK
-    assert _prefill_chunk(d=320, cuk=None) == _lib.SWA_EINVAL  # checked past the size
-    assert _decode(d=320, ws=None) == _lib.SWA_EWORKSPACE
-    assert _decode_step(d=320, ws=None) == _lib.SWA_EWORKSPACE
-    assert _noalloc(d=320, out=None) == _lib.SWA_EINVAL
+@pytest.mark.parametrize("d", (64, 128, 192, 256, 320, 384, 448, 512))
+def test_every_multiple_of_64_passes_every_size_check(d):
+    """Every multiple of 64 from 64 to 512 passes the head-size checks of
+    every entry point (each call below fails on a later check, or is an
+    empty no-op)."""
+    assert _prefill_chunk(d=d, Tq=0, q=None, out=None) == _lib.SWA_OK
+    assert _prefill_chunk(d=d, cuk=None) == _lib.SWA_EINVAL  # checked past the size
+    assert _decode(d=d, ws=None) == _lib.SWA_EWORKSPACE
+    assert _decode_step(d=d, ws=None) == _lib.SWA_EWORKSPACE
+    assert _noalloc(d=d, out=None) == _lib.SWA_EINVAL
     L = _lib.lib()
-    assert L.swa_decode_workspace_bytes(2, 8, 4, 320, 1088) > 0
-    assert L.swa_cache_append(A, A, A, A, B, 0, 1088, 4, 320, 0, None) == _lib.SWA_OK
-    assert L.swa_cache_roll(A, A, B, 1024, 0, 1088, 4, 320, 0, None) == _lib.SWA_OK
+    assert L.swa_decode_workspace_bytes(2, 8, 4, d, 1088) > 0
+    assert L.swa_cache_append(A, A, A, A, B, 0, 1088, 4, d, 0, None) == _lib.SWA_OK
+    assert L.swa_cache_roll(A, A, B, 1024, 0, 1088, 4, d, 0, None) == _lib.SWA_OK
+
+
+@pytest.mark.parametrize("d", (32, 96, 100, 160, 200, 480, 576, 640, 1024))
+def test_other_head_sizes_are_rejected_everywhere(d):
+    """Sizes that are not a multiple of 64, or above 512, are refused by
+    every entry point with SWA_EUNSUPPORTED."""
+    L = _lib.lib()
     for call in (_decode, _decode_step, _noalloc):
-        assert call(d=160) == _lib.SWA_EUNSUPPORTED
-    assert L.swa_decode_workspace_bytes(2, 8, 4, 160, 1088) == 0
+        assert call(d=d) == _lib.SWA_EUNSUPPORTED
+    assert _prefill_chunk(d=d) == _lib.SWA_EUNSUPPORTED
+    assert L.swa_decode_workspace_bytes(2, 8, 4, d, 1088) == 0
+    assert L.swa_cache_append(A, A, A, A, B, 2, 1088, 4, d, 0, None) == _lib.SWA_EUNSUPPORTED
+    assert L.swa_cache_roll(A, A, B, 1024, 2, 1088, 4, d, 0, None) == _lib.SWA_EUNSUPPORTED
 
 
 def test_prefill_chunk_empty_is_a_no_op():
@@ -132,7 +145,8 @@ def _backward(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d=96), _lib.SWA_EUNSUPPORTED),
-    (dict(d=384), _lib.SWA_EUNSUPPORTED),
+    (dict(d=576), _lib.SWA_EUNSUPPORTED),
+    (dict(d=0), _lib.SWA_EUNSUPPORTED),
     (dict(dtype=7), _lib.SWA_EUNSUPPORTED),
     (dict(mode=2), _lib.SWA_EUNSUPPORTED),
     (dict(hq=3, hkv=2), _lib.SWA_EINVAL),
@@ -158,10 +172,12 @@ def test_prefill_backward_sizes():
     workspace holds two fp32 rows of statistics per head and two int32
     intervals per token."""
     assert _backward(T=0, q=None, dq=None, ws=None) == _lib.SWA_OK
-    for d in (64, 128, 256, 320, 512):
+    for d in (64, 128, 192, 256, 320, 384, 448, 512):
         assert _backward(d=d, wsb=0) == _lib.SWA_EWORKSPACE
-    for d in (64, 128, 256, 320, 512):
+    for d in (64, 128, 192, 256, 320, 384, 448, 512):
         assert _backward(d=d, dtype=1, wsb=0) == _lib.SWA_EWORKSPACE
+    for d in (96, 160, 576):
+        assert _backward(d=d) == _lib.SWA_EUNSUPPORTED
     L = _lib.lib()
     for T, hq in ((1, 1), (4096, 32), (16384, 16)):
         n = L.swa_prefill_backward_workspace_bytes(T, hq)

@@ -76,7 +76,8 @@ def _small_case(d, g, W, A, seed, B=6, steps=None):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d,g,W,A", [(64, 1, 40, 8), (128, 4, 100, 16), (256, 2, 50, 64),
                                      (512, 2, 30, 8), (256, 8, 33, 5), (320, 2, 60, 16),
-                                     (320, 4, 31, 7)])
+                                     (320, 4, 31, 7), (192, 8, 40, 8), (384, 4, 50, 16),
+                                     (448, 2, 30, 8)])
 def test_ring_decode_equals_linear_decode_every_step(dtype, d, g, W, A):
     require_gpu()
     case = _small_case(d, g, W, A, seed=d + g + W)

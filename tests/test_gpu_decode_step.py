@@ -57,7 +57,8 @@ class StepRun(DecodeRun):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d,g,W,A", [(64, 1, 40, 8), (128, 4, 100, 16), (256, 2, 50, 64),
                                      (512, 2, 30, 8), (256, 8, 33, 5), (320, 2, 60, 16),
-                                     (320, 4, 31, 7)])
+                                     (320, 4, 31, 7), (192, 8, 40, 8), (384, 4, 50, 16),
+                                     (448, 2, 30, 8)])
 def test_decode_step_matches_model_and_linear_decode(dtype, d, g, W, A):
     require_gpu()
     case = _small_case(d, g, W, A, seed=500 + d + g + W)

@@ -46,7 +46,7 @@ def _run(q, k, v, cu, ids, W, mode, dtype):
 
 
 CASES = []
-for d in (64, 128, 256, 320, 512):
+for d in (64, 128, 192, 256, 320, 384, 448, 512):
     for dtype in ("bf16", "f32"):
         for mode in (CAUSAL, BLOCKWISE):
             CASES.append((d, dtype, mode))
@@ -71,7 +71,7 @@ def test_prefill_small_ragged(d, dtype, mode):
         assert_close(got, want, dtype, "d=%d %s mode=%d W=%d" % (d, dtype, mode, W))
 
 
-@pytest.mark.parametrize("d", [64, 128, 256, 320, 512])
+@pytest.mark.parametrize("d", [64, 128, 192, 256, 320, 384, 448, 512])
 @pytest.mark.parametrize("g", [4, 8])
 def test_prefill_gqa_groups_of_4_and_8(d, g):
     """Query groups of 4 and 8 heads per kv head (4 heads share each K/V
@@ -105,7 +105,7 @@ def test_prefill_gqa_groups_of_4_and_8(d, g):
     assert_close(got, want, "bf16", "gqa window-bound d=%d g=%d" % (d, g))
 
 
-@pytest.mark.parametrize("d", [128, 256, 320, 512])
+@pytest.mark.parametrize("d", [128, 192, 256, 320, 384, 448, 512])
 @pytest.mark.parametrize("mode", [CAUSAL, BLOCKWISE])
 def test_prefill_odd_group(d, mode):
     """Three query heads per kv head: work-groups that hold one query head
@@ -125,7 +125,7 @@ def test_prefill_odd_group(d, mode):
         assert_close(got, want, "bf16", "odd group d=%d mode=%d W=%d" % (d, mode, W))
 
 
-@pytest.mark.parametrize("d", [64, 128, 256, 320, 512])
+@pytest.mark.parametrize("d", [64, 128, 192, 256, 320, 384, 448, 512])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_prefill_window_one_is_exact(d, dtype):
     """W = 1: every row attends only to itself, so out = v[i] bit for bit."""
@@ -142,7 +142,7 @@ def test_prefill_window_one_is_exact(d, dtype):
     np.testing.assert_array_equal(got, want)
 
 
-@pytest.mark.parametrize("d", [128, 256, 320, 512])
+@pytest.mark.parametrize("d", [128, 192, 256, 320, 384, 448, 512])
 @pytest.mark.parametrize("strength", [40.0, 400.0])
 def test_prefill_needle_marks_window_edge(d, strength):
     """bf16 sharpness check: key j carries a strong needle; query rows that
@@ -192,7 +192,7 @@ def _needle_inputs(d, T, j, seed):
     return tuple(si.f32_to_bf16_bits(x) for x in (qf, kf, vf))
 
 
-@pytest.mark.parametrize("d", [128, 256, 320, 512])
+@pytest.mark.parametrize("d", [128, 192, 256, 320, 384, 448, 512])
 def test_prefill_needle_blockwise_image_edges(d):
     """bf16 sharpness of the vision-language mask on the pipelined kernels
     ([SPYRE] Correctness: a future key of the same image is allowed, a

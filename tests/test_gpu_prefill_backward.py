@@ -77,7 +77,7 @@ def _ids_for(T, cu, seed):
     return ids
 
 
-CASES = [(d, dtype, mode) for d in (64, 128, 256, 320, 512) for dtype in ("bf16", "f32")
+CASES = [(d, dtype, mode) for d in (64, 128, 192, 256, 320, 384, 448, 512) for dtype in ("bf16", "f32")
          for mode in (CAUSAL, BLOCKWISE)]
 
 

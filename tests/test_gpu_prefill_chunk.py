@@ -35,9 +35,10 @@ def _ragged_chunks(rng, d):
 
 # (kv heads, query heads per kv head) per head size: groups of 2, 4 and 8
 # (4 or 8 heads share each K/V tile in one work-group)
-GROUPS = {64: (1, 8), 128: (1, 4), 256: (2, 2), 320: (1, 4), 512: (1, 4)}
+GROUPS = {64: (1, 8), 128: (1, 4), 192: (2, 2), 256: (2, 2), 320: (1, 4), 384: (2, 2), 448: (1, 4),
+          512: (1, 4)}
 
-CASES = [(d, dt, m) for d in (64, 128, 256, 320, 512) for dt in ("bf16", "f32")
+CASES = [(d, dt, m) for d in (64, 128, 192, 256, 320, 384, 448, 512) for dt in ("bf16", "f32")
          for m in (CAUSAL, BLOCKWISE)]
 
 

@@ -26,9 +26,10 @@ CAUSAL, BLOCKWISE = si.CAUSAL, si.BLOCKWISE
 
 # (kv heads, query heads per kv head) per head size: groups of 2, 4 and 8
 # (4 or 8 heads share each K/V tile in one work-group)
-GROUPS = {64: (1, 8), 128: (1, 4), 256: (2, 2), 320: (1, 4), 512: (1, 4)}
+GROUPS = {64: (1, 8), 128: (1, 4), 192: (2, 2), 256: (2, 2), 320: (1, 4), 384: (2, 2), 448: (1, 4),
+          512: (1, 4)}
 
-CASES = [(d, dtype, mode) for d in (64, 128, 256, 320, 512) for dtype in ("bf16", "f32")
+CASES = [(d, dtype, mode) for d in (64, 128, 192, 256, 320, 384, 448, 512) for dtype in ("bf16", "f32")
          for mode in (CAUSAL, BLOCKWISE)]
 
 
@@ -56,8 +57,9 @@ def test_prefill_lse(d, dtype, mode):
         assert err <= tol, "lse d=%d %s mode=%d W=%d: max-abs %.3g (tol %.3g)" % (d, dtype, mode, W, err, tol)
 
 
-@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "bf16"), (128, "f32"), (256, "bf16"),
-                                     (320, "bf16"), (512, "bf16")])
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "bf16"), (128, "f32"), (192, "bf16"),
+                                     (256, "bf16"), (320, "bf16"), (384, "bf16"), (448, "bf16"),
+                                     (512, "bf16")])
 @pytest.mark.parametrize("mode", [CAUSAL, BLOCKWISE])
 def test_backward_with_forward_lse(d, dtype, mode):
     """The backward that takes the forward's lse (and skips its own pass

@@ -45,7 +45,7 @@ class GpuRing:
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d,W,A", [(64, 12, 4), (256, 24, 8), (512, 9, 3), (128, 64, 64),
-                                   (320, 20, 6)])
+                                   (320, 20, 6), (192, 16, 4), (384, 12, 6), (448, 10, 6)])
 def test_ring_ops_bit_exact_against_model(dtype, d, W, A):
     require_gpu()
     rng = si.rng_for(d + W + A)
