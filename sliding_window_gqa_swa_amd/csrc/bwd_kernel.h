@@ -74,22 +74,22 @@ constexpr int bw_blocks_per_cu() {
 // Per-row key intervals (bwd_rows_kernel, prefill_bwd.hip): lo[i] and
 // hi[i] of every row, read by both kernels below.
 
-
-// Descriptor of rows [r0, T) of a [T, heads, D] tensor at head h: row r of
-// the tile at byte offset r * heads * D * sizeof(T); rows at or past T fall
-// outside the buffer and load as zeros.
-// dk^T / dv^T product with the accumulator pinned to AGPRs.  At D = 512 a
-// dk/dv wave needs more than the 256 VGPRs: the builtin then gives the
-// accumulators AGPRs but moves all of them through VGPRs on every tile (a
-// D operand other than the C operand, then copies back).  Written by hand,
-// the hazards the compiler resolves for the builtin are handled here: the
-// B operand comes from vector ALU conversions just before, so the product
-// waits two wait states (s_nop 1); the accumulators are read by vector
-// instructions only after the loop, past mfma_drain().
+// dk^T / dv^T product with the accumulator pinned to AGPRs.  When a dk/dv
+// wave needs more than the 256 VGPRs (bf16 from D = 192 with one wave per
+// SIMD), the builtin gives the accumulators AGPRs but moves all of them
+// through VGPRs on every tile (a D operand other than the C operand, then
+// copies back).  Written by hand, the hazards the compiler resolves for the
+// builtin are handled here: the B operand comes from vector ALU conversions
+// just before, so the product waits two wait states (s_nop 1); the
+// accumulators are read by vector instructions only after the loop, past
+// mfma_drain().
 __device__ __forceinline__ void bw_mfma_aacc(floatx4& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// Descriptor of rows [r0, T) of a [T, heads, D] tensor at head h: row r of
+// the tile at byte offset r * heads * D * sizeof(T); rows at or past T fall
+// outside the buffer and load as zeros.
 template <typename T, int D>
 __device__ __forceinline__ i32x4 bw_rows_rsrc(const T* base, int r0, int h, int heads, int T_) {
   const T* p0 = base + ((size_t)r0 * heads + h) * D;
@@ -490,8 +490,10 @@ __global__ __launch_bounds__(NW * 64, (NW == 4 ? bw_blocks_per_cu<D, T>() : 1)) 
   constexpr int QH = G::QREG / DS;         // S / dP fragments of this wave's d range
   constexpr int NDT = D / 16 / DS;         // 16-wide d blocks of this wave's accumulators
   constexpr int CPW = G::CPR / DS;         // 16-byte chunks of this wave's d range
-  // accumulators pinned to AGPRs (bf16 at D = 512, see bw_mfma_aacc)
-  constexpr bool kPinAcc = !kF32 && D >= 512;
+  // accumulators pinned to AGPRs (bf16 from D = 192 in 4-wave work-groups,
+  // see bw_mfma_aacc: left to the compiler, there they live in AGPRs and are
+  // copied through VGPRs around every product of every tile)
+  constexpr bool kPinAcc = !kF32 && D >= 192 && NW == 4;
   static_assert(DS == 1 || DS == 2, "one or two waves per key block");
   static_assert(KB == 1 || KB == 2, "one or two key blocks per wave");
   static_assert(G::QREG % DS == 0 && (D / 16) % DS == 0, "d splits evenly");
