@@ -213,3 +213,25 @@ def test_decode_batched_d320_across_a_roll():
             log("decode b64 d320 step %d" % s)
             assert_close(out[seqs], run.oracle(q, seqs), "bf16", "b64 d320 step %d" % s)
     assert not (host(run.meta)[:, 3] < 0).any()
+
+
+def test_decode_at_the_largest_ring():
+    """The largest ring the calls accept (SWA_MAX_RING_ROWS = 65536 rows:
+    W = 65472 plus the 64 slack rows), two sequences whose prompts are
+    longer than the window, decoded across the roll that the 64th step
+    brings, against the linear-cache oracle at the steps around it."""
+    require_gpu()
+    W, A = 65536 - 64, 64
+    L = np.array([70001, 66000], np.int32)
+    case = si.DecodeCase("max_ring", batch=2, hq=4, hkv=2, d=64, window=W, ring_rows=W + A,
+                         prompt_lens=L, left_pad=np.array([0, 5], np.int32),
+                         tail_lens=np.minimum(L, W).astype(np.int32), steps=66, seed=65536)
+    run = DecodeRun(case, "bf16")
+    for s in range(case.steps):
+        log("decode largest ring step %d" % s)
+        q, out, seqs = run.step(s)
+        if s in (0, 1, 62, 63, 64, 65):
+            assert_close(out, run.oracle(q, seqs), "bf16", "largest ring step %d" % s)
+    m = host(run.meta)
+    assert not (m[:, 3] < 0).any(), "a sequence overflowed its ring"
+    assert (m[:, 1] == L.astype(np.int64) - W + A).all(), "one roll moved each anchor by 64"
