@@ -3,8 +3,9 @@ of the library, against swa_decode_step with a caller workspace.  Both run
 the same kernels, so outputs, ring bytes and ring_meta must agree bit for
 bit.  Calls follow one another on the one shared scratch: a batch of 12
 sequences over 18 steps (across a roll), then a smaller batch of 3, then a
-float32 batch of 5, so each call finds the scratch as the previous, larger
-or differently laid out, call left it."""
+float32 batch of 5, then head size 448 with groups of 4, so each call finds
+the scratch as the previous, larger or differently laid out, call left
+it."""
 import numpy as np
 import pytest
 import torch
@@ -44,13 +45,14 @@ def _two_rings(case, dtype):
 
 def test_noalloc_step_matches_workspace_step():
     require_gpu()
-    for B, steps, dtype in ((12, 18, "bf16"), (3, 2, "bf16"), (5, 3, "f32")):
-        case = _case(B, 0 if dtype == "bf16" else 1)
+    for B, steps, dtype, d, hq, hkv in ((12, 18, "bf16", 256, 8, 4), (3, 2, "bf16", 256, 8, 4),
+                                        (5, 3, "f32", 256, 8, 4), (4, 3, "bf16", 448, 8, 2)):
+        case = _case(B, 0 if dtype == "bf16" else 1, d=d, hq=hq, hkv=hkv)
         (ka, va, ma), (kb, vb, mb) = _two_rings(case, dtype)
         ws = api.decode_workspace(torch.empty((B, case.hq, case.d), dtype=ka.dtype, device="cuda"), ka)
         for s in range(steps):
             q, kn, vn = case.step_inputs(s, dtype)
-            log("noalloc B=%d %s step %d" % (B, dtype, s))
+            log("noalloc B=%d %s d=%d step %d" % (B, dtype, d, s))
             ref = api.decode_step(dev(q), dev(kn), dev(vn), ka, va, ma, case.window, workspace=ws)
             got = api.decode_step_noalloc(dev(q), dev(kn), dev(vn), kb, vb, mb, case.window)
             torch.cuda.synchronize()
