@@ -20,10 +20,12 @@
 //   out-of-range offset, so they return zeros and move no bytes), forms the
 //   query dot products with a lane-group butterfly and folds the rows into a
 //   running (max, sum, weighted V) state, online-softmax style.  The states
-//   of the row groups and waves are merged in a fixed order; partials
-//   (m, l, o) go to the workspace; the last split block of each sequence and
-//   head block (a device-scope counter in the workspace) combines the splits
-//   in a fixed order (deterministic), so one launch does the whole decode.
+//   of the row groups and waves are merged in a fixed order.  A ring of at
+//   most 2048 rows on a grid of about one block per CU or more is one split:
+//   the block writes the output itself.  Otherwise partials (m, l, o) go to
+//   the workspace; the last split block of each sequence and head block (a
+//   device-scope counter in the workspace) combines the splits in a fixed
+//   order (deterministic), so one launch does the whole decode.
 //
 // Decode step (STEP = true): the same kernel also performs the per-token
 // cache work of the sequence first, so one launch serves a whole decode
@@ -54,15 +56,20 @@
 namespace swa {
 namespace {
 
-constexpr int kDecThreads = 256;
+// 8 waves per block: with one block per CU (a 64-sequence batch takes one
+// block per ring) the CU keeps 16 rows per wave step in flight; 48.2 us for
+// the 64-sequence D = 256 decode against 51.4 us with two 4-wave blocks of
+// 544 rows and a combine per ring (measured)
+constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / kWave;
-// bounds the work of one block (two blocks of 544 rows per 1088-row ring:
-// 50 us for the 64-sequence D = 256 decode against 55 us with three of 384,
-// measured)
-constexpr int kMaxRowsPerSplit = 544;
+// bounds the work of one block: a ring of up to 2048 rows is one split on
+// grids of at least one block per CU (no partials, no combine: the block
+// writes the output itself)
+constexpr int kMaxRowsPerSplit = 2048;
 constexpr int kTargetBlocks = 256;  // about one block per CU before the row cap adds more
 constexpr int kMaxSplits = 256;      // (m, l) of every split fit the combine's LDS
 constexpr int kLoadAllRows = 64;     // minimum rows per split of a small grid
+constexpr int kLoadAllMaxRows = 256; // larger splits stream: the row mask saves their bytes
 constexpr float kLog2e = 1.4426950408889634f;
 
 // 16-byte chunk of a row as fp32.
@@ -464,6 +471,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
       x += red_o[w][j][dd] * e;
       l += red_l[w][j] * e;
     }
+    if (splits == 1) {  // the block holds the whole ring: the output itself
+      const float o = l > 0.f ? x / l : 0.f;
+      const size_t oo = ((size_t)b * hq + h0 + j) * D + dd;
+      if constexpr (std::is_same<T, float>::value) out[oo] = o;
+      else reinterpret_cast<uint16_t*>(out)[oo] = (uint16_t)float_to_bf16_bits(o);
+      continue;
+    }
     // agent-scope stores write through to the device coherence point, so
     // the combining block (possibly on another XCD) reads them back
     st_agent(&ws_o[(((size_t)b * hq + h0 + j) * splits + s) * D + dd], x);
@@ -488,6 +502,30 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   //     atomic has returned (barrier), as agent-scope loads, which are served
   //     from the coherence point and never from a stale line of its own L2.
   // The counter goes back to zero for the next call.
+  // Decode step: every block of the sequence has read ring_meta (its loads
+  // returned before any of its work, and every thread of the block passed
+  // the barrier above): the last one to get here (a second counter, one per
+  // sequence) stores the new state.  The next launch reads it (and the
+  // appended ring row, written above by one block with plain stores) after
+  // the kernel boundary, which makes every store of this launch visible.
+  auto publish_state = [&]() __attribute__((always_inline)) {
+    uint32_t* scnt = counters + (size_t)gridDim.z * gridDim.y + b;
+    const uint32_t nblk = (uint32_t)splits * gridDim.y;
+    if (__hip_atomic_fetch_add(scnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nblk - 1) {
+      int32_t* mw = meta + 4 * (size_t)b;
+      mw[0] = (int32_t)pos;
+      mw[1] = (int32_t)anchor;
+      mw[2] = start;
+      mw[3] = slot_p >= 0 ? lo_raw : (int32_t)((uint32_t)lo_raw | 0x80000000u);
+      __hip_atomic_store(scnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  if (splits == 1) {  // output written above; no partials, no combine
+    if constexpr (STEP) {
+      if (threadIdx.x == 0) publish_state();
+    }
+    return;
+  }
   __shared__ int is_last;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -495,23 +533,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   if (threadIdx.x == 0) {
     is_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
               (uint32_t)(splits - 1);
-    if constexpr (STEP) {
-      // every block of the sequence has read ring_meta (its loads returned
-      // before any of its work): the last one to get here stores the new
-      // state.  The next launch reads it (and the appended ring row, written
-      // above by one block with plain stores) after the kernel boundary,
-      // which makes every store of this launch visible.
-      uint32_t* scnt = counters + (size_t)gridDim.z * gridDim.y + b;
-      const uint32_t nblk = (uint32_t)splits * gridDim.y;
-      if (__hip_atomic_fetch_add(scnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nblk - 1) {
-        int32_t* mw = meta + 4 * (size_t)b;
-        mw[0] = (int32_t)pos;
-        mw[1] = (int32_t)anchor;
-        mw[2] = start;
-        mw[3] = slot_p >= 0 ? lo_raw : (int32_t)((uint32_t)lo_raw | 0x80000000u);
-        __hip_atomic_store(scnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
+    if constexpr (STEP) publish_state();
   }
   __syncthreads();
   if (!is_last) return;
@@ -696,9 +718,12 @@ DecodePlan plan_decode(int batch, int hq, int hkv, int d, int ring_rows) {
   if (rps < rps_min) rps = rps_min;
   p.rows_per_split = rps;
   p.splits = (ring_rows + rps - 1) / rps;
-  // latency-bound grids (no more blocks than CUs) load whole splits ahead
-  // of the ring state, at least 64 rows per block (two batches of 32)
-  p.load_all = units * p.splits <= kTargetBlocks;
+  // latency-bound grids (no more blocks than CUs, short splits) load whole
+  // splits ahead of the ring state, at least 64 rows per block; a grid whose
+  // blocks each stream a long split (a large batch, one split per ring)
+  // waits for the ring state once and loads only the window's rows (51.3
+  // against 48.2 us for the 64-sequence D = 256 decode, measured)
+  p.load_all = units * p.splits <= kTargetBlocks && p.rows_per_split <= kLoadAllMaxRows;
   if (p.load_all && p.rows_per_split < kLoadAllRows) {
     p.rows_per_split = kLoadAllRows;
     p.splits = (ring_rows + kLoadAllRows - 1) / kLoadAllRows;
