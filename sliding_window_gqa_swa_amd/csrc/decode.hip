@@ -56,12 +56,13 @@
 namespace swa {
 namespace {
 
-// 8 waves per block: with one block per CU (a 64-sequence batch takes one
-// block per ring) the CU keeps 16 rows per wave step in flight; 48.2 us for
-// the 64-sequence D = 256 decode against 51.4 us with two 4-wave blocks of
-// 544 rows and a combine per ring (measured)
-constexpr int kDecThreads = 512;
-constexpr int kDecWaves = kDecThreads / kWave;
+// Threads per block: 8 waves on streaming grids, where one block per CU
+// (a 64-sequence batch takes one block per ring) keeps 16 rows per wave step
+// in flight (48.6 us for the 64-sequence D = 256 decode against 51.4 us
+// with two 4-wave blocks of 544 rows and a combine per ring); 4 waves on
+// small grids, whose 64-row splits give each wave 16 rows (8.5 against 8.7
+// us average launch for one sequence in a kernel trace).
+constexpr int dec_threads(bool load_all) { return load_all ? 256 : 512; }
 // bounds the work of one block: a ring of up to 2048 rows is one split on
 // grids of at least one block per CU (no partials, no combine: the block
 // writes the output itself)
@@ -117,29 +118,31 @@ constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 
 // or above CH, at most 64); with CH not a power of two (head size 320:
 // 40 chunks of bf16, 80 of fp32) the lanes past the last chunk load
 // nothing and add zeros to the lane-group sums.
-template <int D, typename T>
+template <int D, typename T, int NWV>
 struct DecGeom {
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16 bytes
   static constexpr int CH = D / VEC;                // chunks per row
   static constexpr int LPR = pow2_at_least(CH) < kWave ? pow2_at_least(CH) : kWave;  // lanes per row
   static constexpr int CPL = (CH + LPR - 1) / LPR;  // chunks per lane per row
   static constexpr int RPW = kWave / LPR;           // rows per wave step
-  static constexpr int RPI = RPW * kDecWaves;       // rows per block step
+  static constexpr int RPI = RPW * NWV;       // rows per block step
   static constexpr int ELT = CPL * VEC;             // elements per lane
   static constexpr bool FULL = CH % LPR == 0;       // every lane's chunks exist
   static_assert(D % VEC == 0, "whole 16-byte chunks per row");
 };
 
 template <int D, typename T, int GB, bool STEP, bool LA>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
+__global__ __launch_bounds__(dec_threads(LA)) void decode_split_kernel(
     const T* __restrict__ q, T* __restrict__ k_ring, T* __restrict__ v_ring,
     int32_t* __restrict__ meta, int W, int R, int hq, int hkv, int head_blocks,
     int rows_per_split, float qk_scale_log2, float* ws_o, float* ws_ml, int splits,
     uint32_t* counters, T* __restrict__ out, const T* __restrict__ k_new,
     const T* __restrict__ v_new) {
-  using G = DecGeom<D, T>;
-  __shared__ float red_o[kDecWaves][GB][D];
-  __shared__ float red_m[kDecWaves][GB], red_l[kDecWaves][GB];
+  constexpr int NT = dec_threads(LA);  // threads per block
+  constexpr int NWV = NT / kWave;      // waves per block
+  using G = DecGeom<D, T, NWV>;
+  __shared__ float red_o[NWV][GB][D];
+  __shared__ float red_m[NWV][GB], red_l[NWV][GB];
 
   const int s = blockIdx.x;
   const int kvh = blockIdx.y / head_blocks;
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   if constexpr (STEP) {
     // one writer of the appended row: head block 0 of the split holding it
     if (hb == 0 && slot_p >= r0 && slot_p < r1) {
-      for (int c = threadIdx.x; c < D / G::VEC; c += kDecThreads) {
+      for (int c = threadIdx.x; c < D / G::VEC; c += NT) {
         const size_t dst = ring_off + (size_t)slot_p * D + (size_t)c * G::VEC;
         *reinterpret_cast<u32x4*>(k_ring + dst) =
             *reinterpret_cast<const u32x4*>(k_new + new_off + (size_t)c * G::VEC);
@@ -458,15 +461,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
   __syncthreads();
   // merge the waves in a fixed order and write the split partial
-  for (int idx = threadIdx.x; idx < nh * D; idx += kDecThreads) {
+  for (int idx = threadIdx.x; idx < nh * D; idx += NT) {
     const int j = idx / D, dd = idx - j * D;
     float M = red_m[0][j];
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, red_m[w][j]);
+    for (int w = 1; w < NWV; ++w) M = fmaxf(M, red_m[w][j]);
     const float Mr = M == -INFINITY ? 0.f : M;
     float x = 0.f, l = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
+    for (int w = 0; w < NWV; ++w) {
       const float e = __builtin_amdgcn_exp2f(red_m[w][j] - Mr);
       x += red_o[w][j][dd] * e;
       l += red_l[w][j] * e;
@@ -545,12 +548,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   // p, p + PARTS, ...; the parts' sums are added in order through LDS.
   constexpr int C4 = D / 4;
   constexpr int ITEMS = GB * C4;
-  constexpr int PARTS = ITEMS >= kDecThreads ? 1 : (kDecThreads / ITEMS > 4 ? 4 : kDecThreads / ITEMS);
-  constexpr int IPT = (ITEMS * PARTS + kDecThreads - 1) / kDecThreads;  // items per thread
+  constexpr int PARTS = ITEMS >= NT ? 1 : (NT / ITEMS > 4 ? 4 : NT / ITEMS);
+  constexpr int IPT = (ITEMS * PARTS + NT - 1) / NT;  // items per thread
   // splits per load batch and item (large grids have few splits; the
   // registers would cost them occupancy)
   constexpr int NB = IPT == 1 ? (LA ? 18 : 4) : (LA ? 9 : 2);
-  constexpr int MLN = (GB * kMaxSplits + kDecThreads - 1) / kDecThreads;
+  constexpr int MLN = (GB * kMaxSplits + NT - 1) / NT;
   __shared__ float cm[GB][kMaxSplits], cl[GB][kMaxSplits];
   // o partials of this (sequence, head block): [nh][splits][D] fp32
   const size_t o_base = ((size_t)b * hq + h0) * splits * D;
@@ -561,7 +564,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   u32x4 ob[IPT][NB];
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
-    const int t = threadIdx.x + i * kDecThreads;
+    const int t = threadIdx.x + i * NT;
     it_p[i] = t / ITEMS;
     const int item = t - it_p[i] * ITEMS;
     it_j[i] = item / C4;
@@ -578,7 +581,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   float mlv[MLN][2];
 #pragma unroll
   for (int n = 0; n < MLN; ++n) {
-    const int idx = threadIdx.x + n * kDecThreads;
+    const int idx = threadIdx.x + n * NT;
     if (idx < nh * splits) {
       const int j = idx / splits, ss = idx - j * splits;
       const float* ml = ws_ml + (((size_t)b * hq + h0 + j) * splits + ss) * 2;
@@ -588,7 +591,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 #pragma unroll
   for (int n = 0; n < MLN; ++n) {
-    const int idx = threadIdx.x + n * kDecThreads;
+    const int idx = threadIdx.x + n * NT;
     if (idx < nh * splits) {
       const int j = idx / splits, ss = idx - j * splits;
       cm[j][ss] = mlv[n][0];
@@ -634,13 +637,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
         }
       }
     }
-    if (it_p[i] < PARTS) red4[it_p[i] * ITEMS + (threadIdx.x + i * kDecThreads) % ITEMS] = x;
+    if (it_p[i] < PARTS) red4[it_p[i] * ITEMS + (threadIdx.x + i * NT) % ITEMS] = x;
   }
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
     if (!it_ok[i] || it_p[i] != 0) continue;
-    const int item = threadIdx.x + i * kDecThreads;
+    const int item = threadIdx.x + i * NT;
     float4 x = red4[item];
 #pragma unroll
     for (int pp = 1; pp < PARTS; ++pp) {
@@ -680,14 +683,15 @@ int launch_decode_t(const void* q, const void* k_new, const void* v_new, void* k
                                  : decode_split_kernel<D, T, GB, true, false>)
                    : (p.load_all ? decode_split_kernel<D, T, GB, false, true>
                                  : decode_split_kernel<D, T, GB, false, false>);
-  hipLaunchKernelGGL(kern, grid, dim3(kDecThreads), 0, stream, (const T*)q, (T*)k_ring,
+  hipLaunchKernelGGL(kern, grid, dim3(dec_threads(p.load_all)), 0, stream, (const T*)q, (T*)k_ring,
                      (T*)v_ring, meta, window, ring_rows, hq, hkv, p.head_blocks,
                      p.rows_per_split, scale * kLog2e, ws_o, ws_ml, p.splits, counters,
                      (T*)out, (const T*)k_new, (const T*)v_new);
   return hipGetLastError() == hipSuccess ? SWA_OK : SWA_ELAUNCH;
 }
 
-// heads per block: bounded so the cross-wave reduction buffer stays <= 32 KB
+// heads per block: bounded so the cross-wave reduction buffer stays <= 64 KB
+// (32 KB with 4 waves)
 int heads_per_block_for(int d, int g) {
   int cap = 2048 / d;
   if (cap > 8) cap = 8;
