@@ -44,6 +44,7 @@ def assert_grad_close(got, want, dtype, what):
     else:
         tmax = 1e-5 * m + 1e-6
         assert mx <= tmax, "%s: max-abs %.3g (tol %.3g), ref max %.3g" % (what, mx, tmax, m)
+    return mx / m if m > 0 else mx, mean / m if m > 0 else mean
 
 
 def _round_out(out64, dtype):
@@ -238,11 +239,14 @@ def test_backward_full_size_sampled(name, rows, keys):
     dq, dk, dv = _run(q, k, v, out, do, case.cu_seqlens, case.ids, case.window, case.mode)
     wq, wk, wv = orc.prefill_backward(q, k, v, do, case.cu_seqlens, case.ids, case.window, case.mode,
                                       rows=rows_a, keys=np.array(keys or [], np.int32))
-    assert_grad_close(dq[rows_a], wq, "bf16", "%s dq rows" % name)
+    rel = assert_grad_close(dq[rows_a], wq, "bf16", "%s dq rows" % name)
+    log("  %s dq, %d rows: max-abs %.3g, mean-abs %.3g of the largest |dq|" % ((name, len(rows_a)) + rel))
     if keys is not None:
         ka = np.array(keys, np.int32)
-        assert_grad_close(dk[ka], wk, "bf16", "%s dk keys" % name)
-        assert_grad_close(dv[ka], wv, "bf16", "%s dv keys" % name)
+        for nm, g, w in (("dk", dk, wk), ("dv", dv, wv)):
+            rel = assert_grad_close(g[ka], w, "bf16", "%s %s keys" % (name, nm))
+            log("  %s %s, %d keys: max-abs %.3g, mean-abs %.3g of the largest |%s|"
+                % ((name, nm, len(ka)) + rel + (nm,)))
     _sum_properties(case, dk, dv, do)
 
 
