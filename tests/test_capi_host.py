@@ -258,6 +258,26 @@ def test_decode_workspace_depends_only_on_sizes():
     assert L.swa_decode_workspace_bytes(1, 8, 4, 100, 1088) == 0
 
 
+def _decode_ws(batch, hq, hkv, d, splits, head_blocks=1):
+    """Workspace of a decode plan with the given splits per ring: the
+    counters (one per sequence, kv head and head block, plus one per
+    sequence, rounded up to 256 bytes), then (m, l, o[d]) in fp32 per
+    sequence, query head and split."""
+    counters = (batch * (hkv * head_blocks + 1) * 4 + 255) // 256 * 256
+    return counters + batch * hq * splits * (d + 2) * 4
+
+
+def test_decode_plan_splits():
+    """The split plan, read back through the workspace size: 64 sequences
+    of 4 kv heads (256 blocks) take one split per 1088-row ring; a single
+    sequence takes 64-row splits (17 per ring); a 65536-row ring takes at
+    most 2048 rows per split (32)."""
+    L = _lib.lib()
+    assert L.swa_decode_workspace_bytes(64, 8, 4, 256, 1088) == _decode_ws(64, 8, 4, 256, 1)
+    assert L.swa_decode_workspace_bytes(1, 4, 2, 256, 1088) == _decode_ws(1, 4, 2, 256, 17)
+    assert L.swa_decode_workspace_bytes(2, 8, 4, 256, 65536) == _decode_ws(2, 8, 4, 256, 32)
+
+
 def test_ring_ops_reject():
     L = _lib.lib()
     # append: bad d / null meta

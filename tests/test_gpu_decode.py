@@ -158,6 +158,20 @@ def test_decode_batched_b64_70_steps():
     np.testing.assert_array_equal(m[:, 1], case.prompt_lens - case.window + 64)
 
 
+def test_decode_one_split_per_ring_is_deterministic():
+    """The 64-sequence workload's launch (one split per ring: every block
+    writes its outputs itself, no partials): two decodes of one state are
+    bit-identical and match the oracle."""
+    require_gpu()
+    case = si.decode_b64_d256()
+    run = DecodeRun(case, "bf16")
+    log("decode b64 determinism")
+    q, out, seqs = run.step(0)
+    out2 = host(api.decode(dev(q), run.k, run.v, run.meta, case.window, workspace=run.ws))
+    np.testing.assert_array_equal(out, out2)
+    assert_close(out, run.oracle(q, seqs), "bf16", "b64 one split")
+
+
 def test_decode_single_sequence_position_3000():
     require_gpu()
     c = si.decode_single_d256()
