@@ -253,3 +253,33 @@ def test_decode_at_the_largest_ring():
     m = host(run.meta)
     assert not (m[:, 3] < 0).any(), "a sequence overflowed its ring"
     assert (m[:, 1] == L.astype(np.int64) - W + A).all(), "one roll moved each anchor by 64"
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_decode_random_shapes_across_a_roll(case):
+    """Seeded random sweep of decode shapes: batch (1 to 128, so that both
+    the small-grid path and the one-split-per-ring path of large grids
+    run), kv heads, group (1, 2, 3, 4, 8), head size, window, slack rows
+    and element type per case; every sequence checked against the
+    linear-cache oracle at every step across the first roll."""
+    require_gpu()
+    rng = si.rng_for(8800 + case)
+    d = (64, 128, 192, 256, 320, 384, 448, 512)[case % 8]
+    B = int(rng.choice([1, 3, 17, 64, 128]))
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 4, 8]))
+    W = int(rng.integers(1, 300))
+    A = int(rng.choice([1, 5, 64]))
+    dtype = "f32" if rng.random() < 0.25 else "bf16"
+    L = rng.integers(1, 3 * W + 2, size=B).astype(np.int32)
+    lo = np.array([rng.integers(0, min(int(x), 7)) for x in L], np.int32)
+    c = si.DecodeCase("random", batch=B, hq=g * hkv, hkv=hkv, d=d, window=W, ring_rows=W + A,
+                      prompt_lens=L, left_pad=lo, tail_lens=np.minimum(L, W).astype(np.int32),
+                      steps=A + 2, seed=8800 + case)
+    what = "case %d: B=%d hq=%d hkv=%d d=%d W=%d A=%d %s" % (case, B, g * hkv, hkv, d, W, A, dtype)
+    run = DecodeRun(c, dtype)
+    for s in range(c.steps):
+        log("decode random %s step %d" % (what, s))
+        q, out, seqs = run.step(s)
+        assert_close(out, run.oracle(q, seqs), dtype, "%s step %d" % (what, s))
+    assert not (host(run.meta)[:, 3] < 0).any(), what
