@@ -16,7 +16,7 @@ What the pages fix, restated:
   - [BONSAI] Steps 2 and 3: cache writes wrap around with a modulo and the
     window mask follows the wrap.
 
-Readings taken where the pages are silent (listed in the design doc):
+Readings taken where the pages are silent:
   - per sequence b the state is ring_meta[b] = (pos, anchor, start, lo):
     pos = position of the newest row, anchor = position held by logical
     ring row 0 (the buffer origin), start = physical row of the anchor,

@@ -16,7 +16,7 @@
  *   [SDPA]   "Add SDPA attention implementation" (ServiceNow/Fast-LLM pull
  *            request 512)
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *   - window W keeps key j for query i iff 0 <= i - j < W (W keys, self
  *     included); W <= 0 means no window (a global layer);
  *   - the window is one-sided: keys after the query (allowed only inside an
