@@ -654,8 +654,9 @@ def main():
         record_traffic(*args.record_traffic)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: every GPU box here has one GPU and this "
-              "implementation has no multi-GPU path (--gpus %d requested)" % args.gpus,
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(--gpus %d requested); prefill and decode would shard by kv head or by "
+              "sequence, with no exchange between GPUs" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
