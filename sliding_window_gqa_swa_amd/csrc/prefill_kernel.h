@@ -1824,7 +1824,11 @@ void prefill_fwd_kernel(
     // ---- epilogue: normalise, transpose through LDS, store whole rows --------
     // O^T fragments give each lane 4 head-dim values of one row, i.e. 8-byte
     // pieces of 16 rows per store; staging the wave's rows in LDS lets 16
-    // lanes write each 2*D-byte output row contiguously.  D = 128: no
+    // lanes write each 2*D-byte output row contiguously.  The rows are
+    // written once and never read here: streaming (non-temporal) stores
+    // keep them from displacing the K/V tiles that other work-groups read
+    // through L2 (48.7 -> 46.8 us on the 4096-token blockwise D=256
+    // workload, measured).  D = 128: no
     // barrier: once this wave is past the last iteration, every wave is past
     // iteration n-2, and iteration n-1 reads neither K stage (n-1) % 2 nor V
     // stage n % 2, and no load is still headed there; waves 0-1 stage in the
@@ -1879,7 +1883,7 @@ void prefill_fwd_kernel(
           const int pc = (ch & ~15) | ((ch + rr) & 15);
           const u32x4 x = *reinterpret_cast<const u32x4*>(ost + rr * ROWB + pc * 16);
           const int i = q0 + rb * G::WR + rr;
-          if (i < Ttot) *reinterpret_cast<u32x4*>(out + ((size_t)i * hq + h) * D + ch * 8) = x;
+          if (i < Ttot) __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(out + ((size_t)i * hq + h) * D + ch * 8));
         }
       } else {
         // the wave's rows' stored chunks (CPM of each) in order, 64 per pass
@@ -1892,7 +1896,7 @@ void prefill_fwd_kernel(
           if (idx < CPW && i < Ttot) {
             const int pc = (ch & ~15) | ((ch + rr) & 15);
             const u32x4 x = *reinterpret_cast<const u32x4*>(ost + rr * ROWB + pc * 16);
-            *reinterpret_cast<u32x4*>(out + ((size_t)i * hq + h) * DM + ch * 8) = x;
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(out + ((size_t)i * hq + h) * DM + ch * 8));
           }
         }
       }
