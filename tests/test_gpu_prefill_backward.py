@@ -36,6 +36,14 @@ def assert_grad_close(got, want, dtype, what):
     m = float(np.abs(want).max(initial=0.0))
     err = np.abs(g - want)
     mx, mean = float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0
+    if m == 0.0 and err.size:
+        # an exactly zero reference (every row admits only keys whose weight
+        # is 1, e.g. window 1): only the rounding residue of dP - delta
+        # remains, the window-1 floor 1e-5 sqrt(D / 128) (see
+        # test_backward_window_one)
+        floor = 1e-5 * np.sqrt(g.shape[-1] / 128.0)
+        assert mx <= floor, "%s: max-abs %.3g where the reference is 0 (floor %.3g)" % (what, mx, floor)
+        return mx, mean
     if dtype == "bf16":
         tmax, tmean = 2e-2 * m + 1e-5, 2e-3 * m + 1e-6
         assert mx <= tmax and mean <= tmean, \
@@ -314,8 +322,4 @@ def test_backward_random_shapes(case):
     got = _run(q, k, v, out, do, cu, ids, W, mode)
     want = orc.prefill_backward(q, k, v, do, cu, ids, W, mode)
     for name, a, b in zip(("dq", "dk", "dv"), got, want):
-        if W == 1 and mode == CAUSAL and name != "dv":
-            # exactly zero in the reference: the W=1 floor of the test above
-            assert np.abs(as_f64(a)).max() <= 1e-5 * np.sqrt(d / 128), (name, what)
-        else:
-            assert_grad_close(a, b, dtype, "%s %s" % (name, what))
+        assert_grad_close(a, b, dtype, "%s %s" % (name, what))
