@@ -179,3 +179,34 @@ def test_decode_step_graph_replays_match_eager():
     np.testing.assert_array_equal(host(g.meta), host(eager.meta))
     np.testing.assert_array_equal(host(g.k), host(eager.k))
     np.testing.assert_array_equal(host(g.v), host(eager.v))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_decode_step_random_shapes(case):
+    """Seeded random sweep of the fused step: batch (1 to 128, so that both
+    the small-grid launch and the one-split-per-ring launch run), kv heads,
+    group, head size, window, slack rows and element type per case; ring
+    bytes and ring_meta bit for bit against the ring model and every
+    sequence's attention against the linear-cache oracle at every step
+    across the first roll."""
+    require_gpu()
+    rng = si.rng_for(8600 + case)
+    d = (64, 128, 192, 256, 320, 384, 448, 512)[case % 8]
+    B = int(rng.choice([1, 5, 64, 128]))
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 4, 8]))
+    W = int(rng.integers(1, 200))
+    A = int(rng.choice([1, 4, 64]))
+    dtype = "f32" if rng.random() < 0.25 else "bf16"
+    L = rng.integers(1, 3 * W + 2, size=B).astype(np.int32)
+    lo = np.array([rng.integers(0, min(int(x), 7)) for x in L], np.int32)
+    c = si.DecodeCase("random step", batch=B, hq=g * hkv, hkv=hkv, d=d, window=W,
+                      ring_rows=W + A, prompt_lens=L, left_pad=lo,
+                      tail_lens=np.minimum(L, W).astype(np.int32), steps=A + 2, seed=8600 + case)
+    what = "case %d: B=%d hq=%d hkv=%d d=%d W=%d A=%d %s" % (case, B, g * hkv, hkv, d, W, A, dtype)
+    run = StepRun(c, dtype)
+    for s in range(c.steps):
+        log("decode step random %s step %d" % (what, s))
+        q, out, seqs = run.step(s)
+        run.check_ring("%s step %d" % (what, s))
+        assert_close(out, run.oracle(q, seqs), dtype, "%s step %d" % (what, s))
